@@ -1,0 +1,168 @@
+"""Decode attention over a paged KV cache — plain float64 definition.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``): imported by ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``.
+
+What is computed
+----------------
+For every sequence ``s`` and query head ``h`` the output is scaled dot-product
+attention of one query row against the sequence's cached keys and values,
+``softmax(scale * q K^T) V`` ([KVPA] §2.1, the attention formula; the decode
+case has one query row and ``S`` cached rows).  The cached rows are not stored
+contiguously: token ``t`` of a sequence sits in physical block
+``block_table[t // block_size]`` at row ``t % block_size`` ([KVPA] §4.2, the
+100-token / block-size-16 paging example and its block table; §5.3, where the
+new token's row is ``t % block_size`` of the last block).
+
+The physical pool has layout ``[num_blocks, 2, num_kv_heads, block_size,
+head_dim]`` with index 0 = K and 1 = V ([KVPA] §4.3 and §5.1, the KV-cache
+shape drawn for the kernel and the engine).
+
+Readings where the pages are silent or inconsistent
+---------------------------------------------------
+* Only tokens ``t < context_len`` take part.  The page's block-level
+  pseudocode multiplies whole blocks, but its own example says the last block
+  is only partly filled ([KVPA] §4.2), so rows past the context are not keys.
+* [KVPA] §4.3 normalises a softmax inside every block and sums the block
+  outputs; that is not attention.  The global softmax of §2.1 is taken,
+  which is also what the online-softmax loop of §7.2 reaches.
+* Grouped-query attention ([KV2P] §5.3; [NANO] §1.2): query heads are split
+  into ``num_kv_heads`` contiguous groups of ``G = Hq / Hkv``; query head
+  ``h`` reads KV head ``h // G``.
+* A sequence with context length 0 has output 0 (the pages' loop would end
+  with 0/0).
+
+Split-context partials
+----------------------
+The pages merge block results with decay factors ([KVPA] §7.2 running max /
+running sum; [NANO] §2.4 merging across blocks with decay coefficients).  The
+same algebra across fixed-size token partitions gives, per partition ``p``,
+``m_p = max z``, ``l_p = sum exp(z - m_p)``, ``o_p = sum exp(z - m_p) v / l_p``
+and, across partitions, ``M = max m_p``, ``w_p = l_p exp(m_p - M)``,
+``out = sum w_p o_p / sum w_p``.  ``split_ref`` and ``merge_ref`` write that
+out; their agreement with ``decode_ref`` is a test.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def gather_sequence(kv_cache, block_table_row, context_len):
+    """Return the logical K and V rows of one sequence, each ``[n, Hkv, D]``.
+
+    Token ``t`` is read from physical block ``block_table_row[t // bs]``, row
+    ``t % bs`` ([KVPA] §4.2 example: with block size 16, tokens 96..99 sit in
+    the seventh table entry, rows 0..3).  Only ``t < context_len`` is read, so
+    table entries past ``ceil(n / bs)`` and rows past ``n`` in the last block
+    are never touched.
+    """
+    block_size = kv_cache.shape[3]
+    t = np.arange(int(context_len))
+    physical = np.asarray(block_table_row)[t // block_size]
+    row = t % block_size
+    # advanced indices separated by a slice: the token axis comes first
+    k = kv_cache[physical, 0, :, row, :]
+    v = kv_cache[physical, 1, :, row, :]
+    return k, v
+
+
+def _attend(qvec, keys, values, scale):
+    """softmax(scale * keys @ q) @ values for one query row, in float64."""
+    z = scale * (keys @ qvec)
+    w = np.exp(z - z.max())
+    return (w @ values) / w.sum()
+
+
+def decode_ref(q, kv_cache, block_tables, context_lens, scale):
+    """Reference decode attention.
+
+    q:             [S, Hq, D]  (any float dtype; upcast exactly to float64)
+    kv_cache:      [NB, 2, Hkv, bs, D]
+    block_tables:  [S, max_blocks] integer, physical block ids
+    context_lens:  [S] integer
+    scale:         softmax scale (the pages use 1/sqrt(head_dim))
+    returns        [S, Hq, D] float64
+    """
+    q = np.asarray(q)
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = kv_cache.shape[2]
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(num_seqs):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        k, v = gather_sequence(kv_cache, block_tables[s], n)
+        k = k.astype(np.float64)
+        v = v.astype(np.float64)
+        for h in range(num_q_heads):
+            g = h // group
+            out[s, h] = _attend(q[s, h].astype(np.float64), k[:, g, :], v[:, g, :], scale)
+    return out
+
+
+def split_ref(q, kv_cache, block_tables, context_lens, scale, partition_size):
+    """Per-partition partial results of decode attention.
+
+    Tokens of sequence ``s`` are cut into partitions of ``partition_size``
+    logical tokens.  For partition ``p`` and head ``h``:
+    ``m = max z``, ``l = sum exp(z - m)``, ``o = sum exp(z - m) v / l`` with
+    ``z = scale * q.k`` over the partition's tokens.  Partitions with no token
+    get ``m = -inf``, ``l = 0``, ``o = 0``.
+
+    returns (m [S, Hq, NP], l [S, Hq, NP], o [S, Hq, NP, D]), float64, with
+    ``NP = ceil(max(context_lens) / partition_size)``.
+    """
+    q = np.asarray(q)
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = kv_cache.shape[2]
+    group = num_q_heads // num_kv_heads
+    max_len = int(np.max(context_lens)) if len(context_lens) else 0
+    num_parts = max(1, -(-max_len // partition_size))
+    m = np.full((num_seqs, num_q_heads, num_parts), -np.inf)
+    l = np.zeros((num_seqs, num_q_heads, num_parts))
+    o = np.zeros((num_seqs, num_q_heads, num_parts, head_dim))
+    for s in range(num_seqs):
+        n = int(context_lens[s])
+        if n == 0:
+            continue
+        k, v = gather_sequence(kv_cache, block_tables[s], n)
+        k = k.astype(np.float64)
+        v = v.astype(np.float64)
+        for p in range(num_parts):
+            lo, hi = p * partition_size, min(n, (p + 1) * partition_size)
+            if lo >= hi:
+                continue
+            for h in range(num_q_heads):
+                g = h // group
+                z = scale * (k[lo:hi, g, :] @ q[s, h].astype(np.float64))
+                m[s, h, p] = z.max()
+                w = np.exp(z - m[s, h, p])
+                l[s, h, p] = w.sum()
+                o[s, h, p] = (w @ v[lo:hi, g, :]) / l[s, h, p]
+    return m, l, o
+
+
+def merge_ref(m, l, o):
+    """Log-sum-exp merge of partition partials into the attention output.
+
+    ``M = max_p m_p``; ``w_p = l_p exp(m_p - M)``; ``out = sum w_p o_p / sum w_p``.
+    Empty partitions (``l_p = 0``) weigh nothing; if every partition is empty
+    the output is 0.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    out = np.zeros(o.shape[:2] + o.shape[3:])
+    for s in range(m.shape[0]):
+        for h in range(m.shape[1]):
+            live = l[s, h] > 0
+            if not live.any():
+                continue
+            big = m[s, h, live].max()
+            w = l[s, h, live] * np.exp(m[s, h, live] - big)
+            out[s, h] = (w @ o[s, h, live]) / w.sum()
+    return out

@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the paged-KV hot path on one MI355X.
+
+One *step* is one pass of the whole path for one batch of sequences:
+  1. host block manager: reserve every sequence's next slot (copy-on-write
+     pairs included) and emit the padded block tables and context lengths;
+  2. copy slots, pairs, tables and lengths to the device (pinned, async, on
+     the compute stream);
+  3. pa_cache_write: copy-on-write block copies, then the new K/V rows;
+  4. pa_decode: attention of every query head over its paged context
+     (single pass, or split context plus the log-sum-exp merge).
+
+Inputs (pool contents, new K/V rows, queries) are synthetic, seeded and
+resident in HBM before timing starts.  The pool is fragmented first (every
+block taken once and given back in a seeded random order), so each
+sequence's blocks are scattered across it.
+
+Printed: one JSON line.  ``value`` is the whole-step KV-read throughput
+(algorithmic K+V bytes the decode reads / wall time per step); ``roofline``
+is the decode call alone (HIP events on its stream) against the 8 TB/s HBM
+peak; ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of
+the same step on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD specification
+METRIC = "decode attention KV-read GB/s and % of HBM peak; seq·ctx tokens/sec per layer"
+
+WORKLOADS = {
+    # name: (num_seqs, Hq, Hkv, D, bs, dtype, lengths-spec, std, pool)
+    "llama7b_mha": dict(S=32, Hq=32, Hkv=32, D=128, bs=16, dtype="f16", ctx=4096, std=1.0,
+                        pool=9000,
+                        desc="LLaMA-2-7B-shaped layer: 32 seqs x ctx 4096, 32 heads (MHA) x 128, "
+                             "fp16 KV, block 16, 9000-block pool"),
+    "gqa7b": dict(S=64, Hq=32, Hkv=8, D=128, bs=16, dtype="f16", ctx=(128, 8192), std=1.0,
+                  pool=None,
+                  desc="GQA 7B-shaped layer: 64 seqs, ctx ~ U[128, 8192], 32 q / 8 KV heads x "
+                       "128, fp16, block 16"),
+    "llama70b": dict(S=16, Hq=64, Hkv=8, D=128, bs=16, dtype="f16", ctx=32768, std=0.5,
+                     pool=None,
+                     desc="LLaMA-2-70B-shaped layer: 16 seqs x ctx 32768, 64 q / 8 KV heads x "
+                          "128, fp16, block 16, values N(0, 0.5^2)"),
+    "shared_prefix": dict(S=64, Hq=32, Hkv=8, D=128, bs=16, dtype="f16", ctx=None, std=1.0,
+                          pool=None,
+                          desc="shared-prefix decode: 64 seqs = one 512-token ref-counted prefix "
+                               "+ private suffix U[1, 2048], 32 q / 8 KV heads x 128, fp16; one "
+                               "fork + copy-on-write per step"),
+    "tiny": dict(S=4, Hq=8, Hkv=8, D=64, bs=16, dtype="f32", ctx=[100, 37, 16, 1], std=1.0,
+                 pool=64, desc="tiny: 4 seqs, MHA 8 x 64, fp32, block 16, lengths 100/37/16/1"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Holds the block manager, device buffers and the per-step logic."""
+
+    def __init__(self, name, bs, seed, steps_total, kernel, partition, device):
+        import torch
+        import paged_kv_cache_153_amd as pa
+        import synth
+        self.torch, self.pa = torch, pa
+        w = dict(WORKLOADS[name])
+        if name == "shared_prefix":
+            w["bs"] = bs
+        self.w, self.name, self.kernel, self.partition = w, name, kernel, partition
+        S, Hq, Hkv, D, bs = w["S"], w["Hq"], w["Hkv"], w["D"], w["bs"]
+        self.S, self.Hq, self.Hkv, self.D, self.bs = S, Hq, Hkv, D, bs
+        tdt = synth.DTYPES[w["dtype"]]
+        self.elem = torch.tensor([], dtype=tdt).element_size()
+        g_cpu = torch.Generator().manual_seed(seed)
+
+        # ---- context lengths at the first decoded step ----
+        if name == "shared_prefix":
+            self.prefix = 512
+            suffix = torch.randint(1, 2049, (S - 1,), generator=g_cpu).tolist()
+            lens0 = [self.prefix + n for n in suffix]           # sequences 0..S-2
+        elif isinstance(w["ctx"], tuple):
+            lens0 = synth.gqa_lengths(S, w["ctx"][0], w["ctx"][1], seed)
+        elif isinstance(w["ctx"], list):
+            lens0 = list(w["ctx"])
+        else:
+            lens0 = [w["ctx"]] * S
+        grow = steps_total
+        need = sum(-(-(n + grow) // bs) for n in lens0) + (S * 2 if name == "shared_prefix" else 0)
+        nb = w["pool"] or math.ceil(1.1 * need)
+        nb = max(nb, need)
+        self.num_blocks = nb
+        self.mb = max(-(-(n + grow) // bs) for n in lens0) + 1
+
+        # ---- host block manager over a fragmented pool ----
+        bm = pa.BlockManager(nb, bs)
+        tmp = 1 << 40
+        for i in range(nb):
+            bm.allocate(tmp + i, 1)
+        for i in torch.randperm(nb, generator=g_cpu).tolist():
+            bm.free(tmp + i)
+        self.bm = bm
+        if name == "shared_prefix":
+            self.prefix_seq = 1 << 41
+            bm.allocate(self.prefix_seq, self.prefix)
+            pblocks, _ = bm.block_table(self.prefix_seq)
+            for s in range(S - 1):
+                bm.share(s, pblocks, self.prefix)
+            # private suffix tokens, one batched append per token position
+            remaining = [n - self.prefix for n in lens0]
+            while any(r > 0 for r in remaining):
+                live = [s for s in range(S - 1) if remaining[s] > 0]
+                bm.append_slots(live)
+                for s in live:
+                    remaining[s] -= 1
+            # every sequence was decoded once already: last token is appended per step
+            self.fork_child = S - 1
+            self.rng = torch.Generator().manual_seed(seed + 1)
+        else:
+            for s, n in enumerate(lens0):
+                bm.allocate(s, n - 1)        # the step appends token n
+        self.seqs = torch.arange(S, dtype=torch.int64)
+        if name == "shared_prefix":
+            self.seqs = torch.cat([torch.tensor([S - 1]), torch.arange(S - 1)]).to(torch.int64)
+
+        # ---- device data (resident before timing) ----
+        dev = device
+        g = torch.Generator(device=dev).manual_seed(seed + 2)
+        log(f"[bench] {name}: pool {nb} blocks x {2 * Hkv * bs * D * self.elem} B = "
+            f"{nb * 2 * Hkv * bs * D * self.elem / 2**30:.2f} GiB, generating on {dev}")
+        self.pool = synth.normal((nb, 2, Hkv, bs, D), tdt, g, dev, w["std"],
+                                 chunk_rows=max(1, (1 << 26) // (2 * Hkv * bs * D)))
+        self.q = synth.normal((S, Hq, D), tdt, g, dev, w["std"])
+        self.new_k = synth.normal((S, Hkv, D), tdt, g, dev, w["std"])
+        self.new_v = synth.normal((S, Hkv, D), tdt, g, dev, w["std"])
+        self.scale = 1.0 / math.sqrt(D)
+        self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+        ws = pa.decode_workspace_size(S, Hq, Hkv, D, bs, self.mb, self.mb * bs, partition,
+                                      pa.F32 if w["dtype"] == "f32" else pa.F16, kernel)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.d_slots = torch.empty(S, dtype=torch.int64, device=dev)
+        self.d_pairs = torch.empty((S, 2), dtype=torch.int32, device=dev)
+        self.d_tables = torch.empty((S, self.mb), dtype=torch.int32, device=dev)
+        self.d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+        self.bufs = []
+        for _ in range(2):
+            self.bufs.append(dict(
+                slots=torch.empty(S, dtype=torch.int64).pin_memory(),
+                pairs=torch.empty((S, 2), dtype=torch.int32).pin_memory(),
+                tables=torch.empty((S, self.mb), dtype=torch.int32).pin_memory(),
+                lens=torch.empty(S, dtype=torch.int32).pin_memory(),
+                event=torch.cuda.Event()))
+        self.k = 0
+        self.kv_bytes = []       # algorithmic decode bytes per step
+        self.ctx_tokens = []
+        self.ncow = []
+
+    def run(self, timed_events=None):
+        torch, pa = self.torch, self.pa
+        buf = self.bufs[self.k % 2]
+        buf["event"].synchronize()          # its previous copies have left pinned memory
+        if self.name == "shared_prefix":
+            child = self.fork_child
+            try:
+                self.bm.free(child)
+            except pa.PAError:
+                pass
+            while True:
+                parent = int(torch.randint(0, self.S - 1, (1,), generator=self.rng))
+                _, n = self.bm.block_table(parent)
+                if n % self.bs:
+                    break
+            self.bm.fork(parent, child)
+        ncow = self.bm.append_slots_into(self.seqs, buf["slots"], buf["pairs"])
+        self.bm.block_tables_into(self.seqs, buf["tables"], buf["lens"])
+        maxlen = int(buf["lens"].max())
+        self.d_slots.copy_(buf["slots"], non_blocking=True)
+        self.d_tables.copy_(buf["tables"], non_blocking=True)
+        self.d_lens.copy_(buf["lens"], non_blocking=True)
+        if ncow:
+            self.d_pairs[:ncow].copy_(buf["pairs"][:ncow], non_blocking=True)
+        buf["event"].record()
+        pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
+                       cow_pairs=self.d_pairs[:ncow] if ncow else None)
+        if timed_events is not None:
+            timed_events[0].record()
+        pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
+                  max_context_len=maxlen, partition_size=self.partition, kernel=self.kernel,
+                  out=self.out, workspace=self.ws)
+        if timed_events is not None:
+            timed_events[1].record()
+        tokens = int(buf["lens"].sum())
+        self.ctx_tokens.append(tokens)
+        self.kv_bytes.append(tokens * 2 * self.Hkv * self.D * self.elem)
+        self.ncow.append(ncow)
+        self.k += 1
+        return buf
+
+    def host_inputs(self, positions):
+        """Host copies of the last step's inputs for some table rows: only those
+        rows' blocks (renumbered 0..), so the oracle reads the very same bits."""
+        import numpy as np
+        buf = self.bufs[(self.k - 1) % 2]
+        tables, lens = buf["tables"], buf["lens"]
+        blocks, rows, lns, off = [], [], [], 0
+        for pos in positions:
+            n = int(lens[pos])
+            nblk = -(-n // self.bs)
+            ids = tables[pos, :nblk].long().to(self.pool.device)
+            blocks.append(self.pool[ids].cpu().numpy())
+            rows.append(np.arange(off, off + nblk))
+            off += nblk
+            lns.append(n)
+        pool = np.concatenate(blocks)
+        bt = np.full((len(rows), max(1, max(len(r) for r in rows))), -1, dtype=np.int64)
+        for i, r in enumerate(rows):
+            bt[i, :len(r)] = r
+        pos_t = self.torch.tensor(list(positions), device=self.q.device)
+        q = self.q[pos_t].cpu().numpy()
+        return q, pool, bt, np.array(lns), pos_t
+
+
+def cpu_baseline(st, budget_s=12.0):
+    """Time the fp64 oracle on a bounded sample of the step (1 thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    order = list(range(st.S))
+    done, t_used, nbytes, toks = 0, 0.0, 0, 0
+    with threadpool_limits(1):
+        while done < len(order) and t_used < budget_s:
+            q, pool, bt, lens, _ = st.host_inputs([order[done]])
+            t0 = time.perf_counter()
+            oracle.decode_ref(q, pool, bt, lens, st.scale)
+            t_used += time.perf_counter() - t0
+            nbytes += int(lens.sum()) * 2 * st.Hkv * st.D * st.elem
+            toks += int(lens.sum())
+            done += 1
+    return dict(value=round(nbytes / t_used / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"fp64 NumPy oracle, 1 thread, on {done} of {st.S} sequences of the last "
+                       f"timed step ({toks} context tokens, {nbytes} KV bytes) in {t_used:.2f} s; "
+                       f"{toks / t_used:.4g} seq*ctx tokens/s")
+
+
+def parity_sample(st, samples=3):
+    """Max-abs error of the last step's output vs the oracle on a few sequences."""
+    import numpy as np
+    import oracle
+    picks = sorted({0, st.S - 1, st.S // 2})[:samples]
+    q, pool, bt, lens, pos = st.host_inputs(picks)
+    want = oracle.decode_ref(q, pool, bt, lens, st.scale)
+    got = st.out[pos].cpu().numpy().astype(np.float64)
+    return float(np.abs(got - want).max())
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_mha", choices=sorted(WORKLOADS))
+    ap.add_argument("--block-size", type=int, default=16, help="shared_prefix: 8, 16 or 32")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition", type=int, default=0, help="0 auto, -1 single pass, or tokens")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", flush=True)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_153_amd as pa
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pa.lib()
+    dev = torch.device("cuda:0")
+    st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
+              args.partition, dev)
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+    st.kv_bytes.clear()
+    st.ctx_tokens.clear()
+    st.ncow.clear()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.run(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    total_bytes = sum(st.kv_bytes)
+    total_tokens = sum(st.ctx_tokens)
+    step_s = wall / args.steps
+    value = total_bytes / wall / 1e9
+    achieved = total_bytes / args.steps / dec_avg_s / 1e9
+    log(f"[bench] step {step_s * 1e6:.1f} us, decode {dec_avg_s * 1e6:.1f} us, "
+        f"{achieved:.1f} GB/s decode, {value:.1f} GB/s whole step")
+
+    parity = None if args.no_parity else parity_sample(st)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(st)
+    w = st.w
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded N(0, std^2) K/V/Q; fragmented pool; no weights)",
+        "config": {
+            "workload": w["desc"] + (f" (block {st.bs})" if args.workload == "shared_prefix" else ""),
+            "num_seqs": st.S, "num_q_heads": st.Hq, "num_kv_heads": st.Hkv, "head_dim": st.D,
+            "block_size": st.bs, "pool_blocks": st.num_blocks,
+            "mean_context": round(total_tokens / args.steps / st.S, 1),
+            "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
+            "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
+        },
+        "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
+        "seq_ctx_tokens_per_s": round(total_tokens / wall, 1),
+        "decode_us": round(dec_avg_s * 1e6, 2),
+        "decode_seq_ctx_tokens_per_s": round(total_tokens / args.steps / dec_avg_s, 1),
+        "cow_pairs_per_step": round(sum(st.ncow) / args.steps, 3),
+        "parity_max_abs_err": parity,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

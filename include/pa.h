@@ -1,0 +1,215 @@
+/*
+ * pa.h — paged-KV decode attention for AMD MI355X (gfx950), C ABI.
+ *
+ * Three pieces, as the source pages describe a PagedAttention engine:
+ *   1. pa_cache_write — append new K/V rows into the paged cache through a
+ *      slot mapping, after any copy-on-write block copies;
+ *   2. pa_decode      — single-query decode attention over the paged cache,
+ *      addressed through per-sequence block tables;
+ *   3. pa_bm_*        — a host-side block manager: free pool, per-sequence
+ *      block tables, reference-counted sharing, fork and copy-on-write.
+ *
+ * Sources (page title, then the section on that page):
+ *   [KVPA]  "KV Cache与PagedAttention深度解析：vLLM内存管理革命" (iopencloud.com)
+ *   [KV2P]  "KV Cache从原理到实战：大模型推理内存管理演进与优化" (xnwp.cn)
+ *   [NANO]  the zwxr.cn nano-vllm walkthrough (untitled in the extract)
+ *
+ * Conventions for every call:
+ *   - Return value is a pa_status (0 = PA_OK).  No C++ exception crosses the
+ *     ABI.  pa_strerror() names a status; pa_last_error() gives the detail of
+ *     the last failure on the calling thread.
+ *   - Device pointers are raw HIP device addresses owned by the caller; the
+ *     library never allocates, frees or retains device memory.  Host pointers
+ *     are only read or written during the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it and the call returns without waiting; a
+ *     device-side fault surfaces at the caller's next synchronisation.
+ *   - Sizes and shapes are host integers.  Contents of device arrays (block
+ *     ids, slots, lengths) are the caller's contract; the kernels clamp every
+ *     index they read so a bad entry cannot address memory outside the
+ *     buffers, but the result is then unspecified.  With the environment
+ *     variable PA_CHECK=1 the library copies those arrays to the host,
+ *     validates them and returns PA_ERR_INVALID_ARG instead (slow; for
+ *     debugging).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* bad pointer, size, shape or alignment       */
+  PA_ERR_UNSUPPORTED = -2,  /* shape/dtype combination with no kernel       */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or too small; see *needed  */
+  PA_ERR_OOM = -4,          /* block manager: not enough free blocks        */
+  PA_ERR_NOT_FOUND = -5,    /* block manager: unknown sequence id           */
+  PA_ERR_HIP = -6           /* a HIP runtime call failed                    */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0, /* IEEE binary32 */
+  PA_F16 = 1  /* IEEE binary16 */
+} pa_dtype;
+
+/* Kernel family for pa_decode.  PA_KERNEL_AUTO picks per shape. */
+typedef enum pa_kernel {
+  PA_KERNEL_AUTO = 0,
+  PA_KERNEL_VALU = 1, /* vector-ALU dot products, DPP lane reductions     */
+  PA_KERNEL_MFMA = 2  /* matrix-core q.K^T and P.V tiles (f16, GQA only)  */
+} pa_kernel;
+
+/* -------------------------------------------------------------------------
+ * 1. Cache write ([KVPA] §2.2 and §5.3; [KV2P] §2.1; [NANO] §2.3)
+ *
+ * Decoding computes K and V for the new token only and appends them to the
+ * cache; with paging the row lands in block slot/block_size at row
+ * slot%block_size.  Before the scatter, each (src, dst) pair in cow_pairs
+ * copies the whole physical block src onto dst (K and V, every head, every
+ * row): the copy-on-write a sequence needs before writing into a block it
+ * shares ([NANO] §2.3, §5.5).  Both steps are enqueued on `stream`, copies
+ * first.  The result is a byte copy (bit-exact).
+ *
+ *   key, value   device, [num_tokens, num_kv_heads, head_dim], dtype,
+ *                contiguous, 16-byte aligned
+ *   kv_cache     device, [num_blocks, 2, num_kv_heads, block_size, head_dim],
+ *                dtype, contiguous, 16-byte aligned; index 1 of dim 1 is V
+ *   slot_mapping device, [num_tokens] int64; slot < 0 skips the row; slots
+ *                must lie in [0, num_blocks*block_size) and be distinct
+ *   cow_pairs    device, [num_cow, 2] int32 (src, dst) block ids, or NULL
+ *                when num_cow == 0; destinations distinct and not sources
+ *   num_tokens, num_cow >= 0 (0 = nothing to do)
+ *   head_dim * element size must be a multiple of 16 bytes.
+ * ------------------------------------------------------------------------- */
+int pa_cache_write(const void* key, const void* value, void* kv_cache,
+                   const int64_t* slot_mapping, int64_t num_tokens,
+                   const int32_t* cow_pairs, int64_t num_cow,
+                   int64_t num_blocks, int num_kv_heads, int head_dim,
+                   int block_size, int dtype, void* stream);
+
+/* -------------------------------------------------------------------------
+ * 2. Decode attention ([KVPA] §2.1 formula, §4.3 block-table addressing,
+ *    §7.2 online softmax; [NANO] §2.4 kernel structure; [KV2P] §5.3 GQA)
+ *
+ * For each sequence s and query head h, with G = num_q_heads/num_kv_heads,
+ * g = h / G and n = context_lens[s]:
+ *   out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K_t) * V_t ,  t < n,
+ * where token t is row t%block_size of physical block
+ * block_tables[s, t/block_size]; K_t = kv_cache[b,0,g,row,:],
+ * V_t = kv_cache[b,1,g,row,:].  Rows past n are never read; n == 0 gives 0.
+ * Accumulation is float32; the output is float32.
+ *
+ *   out            device, [num_seqs, num_q_heads, head_dim] float32
+ *   query          device, [num_seqs, num_q_heads, head_dim] dtype, 16B aligned
+ *   kv_cache       device, as for pa_cache_write
+ *   block_tables   device, [num_seqs, max_blocks_per_seq] int32 (row stride =
+ *                  max_blocks_per_seq); entries past ceil(n/block_size) unused
+ *   context_lens   device, [num_seqs] int32, 0 <= n <= max_context_len and
+ *                  n <= max_blocks_per_seq * block_size
+ *   max_context_len host bound on context_lens (sizes the partition grid)
+ *   scale          softmax scale, normally 1/sqrt(head_dim)
+ *   partition_size 0 = choose; -1 = single pass (one workgroup per (s, KV
+ *                  head)); > 0 = split each context into partitions of this
+ *                  many tokens (a multiple of 16 and of block_size), combined
+ *                  by a log-sum-exp merge kernel
+ *   kernel         a pa_kernel value
+ *   workspace      device scratch for split partials (caller-owned), may be
+ *                  NULL when *workspace_needed is 0
+ *   workspace_needed  out (may be NULL): bytes this call needs.  Calling with
+ *                  out == NULL only computes it and returns PA_OK.
+ * Supported: dtype f32 or f16; head_dim 64 or 128; block_size 8, 16 or 32;
+ * G in {1, 2, 4, 8}.  MFMA needs f16 and G >= 2.  Anything else returns
+ * PA_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+int pa_decode(float* out, const void* query, const void* kv_cache,
+              const int32_t* block_tables, const int32_t* context_lens,
+              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              int block_size, int max_blocks_per_seq, int max_context_len,
+              int64_t num_blocks, float scale, int partition_size, int kernel,
+              void* workspace, size_t workspace_bytes, size_t* workspace_needed,
+              int dtype, void* stream);
+
+/* -------------------------------------------------------------------------
+ * 3. Host block manager ([KVPA] §5.1-§5.3, §8.2; [KV2P] §6.2; [NANO] §2.3,
+ *    §4.2)
+ *
+ * An opaque handle over host memory only; not thread-safe (one caller at a
+ * time per handle).  Sequence ids are arbitrary int64 keys.  The free pool is
+ * a stack that starts as [0, 1, ..., num_blocks-1] and hands out from the
+ * top.  Every block carries a reference count = the number of tables that
+ * hold it; it returns to the pool when the count reaches 0.  Every failing
+ * call leaves the state unchanged.
+ * ------------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm;
+
+/* NULL on bad arguments (num_blocks <= 0, block_size <= 0) or no memory. */
+pa_bm* pa_bm_create(int64_t num_blocks, int block_size);
+void pa_bm_destroy(pa_bm* bm);
+
+/* New sequence holding ceil(num_tokens/block_size) fresh blocks, count 1.
+ * PA_ERR_INVALID_ARG if seq exists or num_tokens < 0; PA_ERR_OOM if too few
+ * blocks are free. */
+int pa_bm_allocate(pa_bm* bm, int64_t seq, int64_t num_tokens);
+
+/* Append n blocks already held by other sequences to seq's table (creating
+ * seq if needed) and add a reference to each: prefix reuse.  The blocks carry
+ * num_tokens tokens (ceil(num_tokens/block_size) == n) and seq, if it exists,
+ * must end on a block boundary. */
+int pa_bm_share(pa_bm* bm, int64_t seq, const int32_t* blocks, int n,
+                int64_t num_tokens);
+
+/* child := copy of parent's table and token count, one more reference per
+ * block.  PA_ERR_NOT_FOUND for an unknown parent; INVALID_ARG if child
+ * exists. */
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+
+/* Reserve the place of seq's next token.  *slot = block*block_size + row.
+ * A fresh block is taken when the sequence ends on a block boundary; if the
+ * last block is shared, a fresh block replaces it in seq's table and
+ * *cow_src and *cow_dst name the copy to make (else both are -1). */
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
+                      int32_t* cow_dst);
+
+/* Batched append_slot over n sequences, in order: slots[i] for seqs[i];
+ * copy pairs packed into cow_pairs[2*k], cow_pairs[2*k+1] (room for n pairs)
+ * with *num_cow = k.  All or nothing: on failure no sequence changes. */
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int64_t* slots,
+                       int32_t* cow_pairs, int* num_cow);
+
+/* Drop one reference per table entry (table order) and forget seq. */
+int pa_bm_free(pa_bm* bm, int64_t seq);
+
+/* Copy seq's table into out[0..cap) (*n = its length, which may exceed cap:
+ * then only cap entries are written) and its token count into *num_tokens.
+ * Either out pointer may be NULL when cap == 0. */
+int pa_bm_block_table(const pa_bm* bm, int64_t seq, int32_t* out, int cap,
+                      int* n, int64_t* num_tokens);
+
+/* Fill a padded [n, max_blocks] int32 table (-1 past each length) and the
+ * int32 context lengths for seqs[0..n).  INVALID_ARG if a table is longer
+ * than max_blocks. */
+int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int n,
+                       int32_t* tables, int max_blocks, int32_t* context_lens);
+
+/* Pool counts: free blocks, blocks with count >= 1, blocks with count >= 2. */
+int pa_bm_stats(const pa_bm* bm, int64_t* num_free, int64_t* num_used,
+                int64_t* num_shared);
+
+/* Reference count of one block (>= 0), or PA_ERR_INVALID_ARG. */
+int pa_bm_ref_count(const pa_bm* bm, int32_t block);
+
+/* ------------------------------------------------------------------------- */
+const char* pa_strerror(int status);
+const char* pa_last_error(void);
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H_ */

@@ -1,0 +1,320 @@
+"""paged_kv_cache_153_amd — paged-KV decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libpa.so`` (the C ABI declared in
+``include/pa.h``).  This module only marshals arguments: it checks tensor
+dtypes/shapes, passes raw device pointers and the current HIP stream, and
+turns status codes into exceptions.  Every step of the computation runs in
+the library's HIP kernels; there is no Python or CPU fallback, and a missing
+library raises.
+
+PyTorch supplies device memory and streams: outputs and split-context
+workspaces the caller does not pass are allocated with ``torch.empty``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PAError", "lib", "library_path", "cache_write", "decode", "decode_workspace_size",
+    "BlockManager", "KERNELS", "F32", "F16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpa.so")
+_lib = None
+
+F32, F16 = 0, 1
+KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+
+PA_OK = 0
+STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
+          -4: "PA_ERR_OOM", -5: "PA_ERR_NOT_FOUND", -6: "PA_ERR_HIP"}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status, detail=""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}" if detail else self.name)
+
+
+def library_path():
+    return _LIB_PATH
+
+
+_c = ctypes
+_P = _c.c_void_p
+_I32P = _c.POINTER(_c.c_int32)
+_I64P = _c.POINTER(_c.c_int64)
+
+_SIGNATURES = {
+    "pa_cache_write": (_c.c_int, [_P, _P, _P, _P, _c.c_int64, _P, _c.c_int64, _c.c_int64,
+                                  _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P]),
+    "pa_decode": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                             _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float, _c.c_int,
+                             _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t), _c.c_int, _P]),
+    "pa_bm_create": (_P, [_c.c_int64, _c.c_int]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_allocate": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
+    "pa_bm_share": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int, _c.c_int64]),
+    "pa_bm_fork": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
+    "pa_bm_append_slot": (_c.c_int, [_P, _c.c_int64, _I64P, _I32P, _I32P]),
+    "pa_bm_append_slots": (_c.c_int, [_P, _I64P, _c.c_int, _I64P, _I32P,
+                                      _c.POINTER(_c.c_int)]),
+    "pa_bm_free": (_c.c_int, [_P, _c.c_int64]),
+    "pa_bm_block_table": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int, _c.POINTER(_c.c_int),
+                                     _I64P]),
+    "pa_bm_block_tables": (_c.c_int, [_P, _I64P, _c.c_int, _I32P, _c.c_int, _I32P]),
+    "pa_bm_stats": (_c.c_int, [_P, _I64P, _I64P, _I64P]),
+    "pa_bm_ref_count": (_c.c_int, [_P, _c.c_int32]),
+    "pa_strerror": (_c.c_char_p, [_c.c_int]),
+    "pa_last_error": (_c.c_char_p, []),
+    "pa_version": (_c.c_char_p, []),
+}
+
+
+def lib():
+    """Load ``libpa.so`` (built in-tree by ``build.py``); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_153_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != PA_OK:
+        detail = lib().pa_last_error().decode()
+        raise PAError(status, detail)
+    return status
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return _P(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None):
+    """Copy-on-write block copies (``cow_pairs`` [k, 2] int32 on device), then
+    scatter ``key``/``value`` [T, Hkv, D] into ``kv_cache`` [NB, 2, Hkv, bs, D]
+    at ``slot_mapping`` [T] int64 (negative = skip).  Enqueued on ``stream``."""
+    torch = _torch()
+    _need_cuda(key, value, kv_cache, slot_mapping, cow_pairs)
+    nb, two, hkv, bs, d = kv_cache.shape
+    if two != 2 or key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
+        raise ValueError("shape mismatch between key/value and kv_cache")
+    if key.dtype != kv_cache.dtype or value.dtype != kv_cache.dtype:
+        raise TypeError("key, value and kv_cache must share a dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise TypeError("slot_mapping must be int64 [T]")
+    ncow = 0
+    if cow_pairs is not None:
+        if cow_pairs.dtype != torch.int32 or cow_pairs.dim() != 2 or cow_pairs.shape[1] != 2:
+            raise TypeError("cow_pairs must be int32 [k, 2]")
+        ncow = cow_pairs.shape[0]
+    _check(lib().pa_cache_write(key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(),
+                                slot_mapping.data_ptr(), key.shape[0],
+                                cow_pairs.data_ptr() if ncow else None, ncow, nb, hkv, d, bs,
+                                _dtype_code(kv_cache), _stream(kv_cache.device, stream)))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, max_context_len, partition_size=0,
+                          dtype=F16, kernel="auto"):
+    """Bytes of split-context workspace ``decode`` needs for this shape."""
+    need = ctypes.c_size_t(0)
+    _check(lib().pa_decode(None, None, None, None, None, num_seqs, num_q_heads, num_kv_heads,
+                           head_dim, block_size, max_blocks_per_seq, max_context_len, 1, 1.0,
+                           partition_size, KERNELS[kernel], None, 0, ctypes.byref(need), dtype,
+                           None))
+    return need.value
+
+
+def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_len=None,
+           partition_size=0, kernel="auto", out=None, workspace=None, stream=None):
+    """Paged decode attention.
+
+    query [S, Hq, D] (kv dtype), kv_cache [NB, 2, Hkv, bs, D], block_tables
+    [S, MB] int32, context_lens [S] int32, all on the GPU.  Returns ``out``
+    [S, Hq, D] float32.  ``max_context_len`` is a host bound on the lengths
+    (default MB * bs); ``partition_size`` 0 = auto, -1 = single pass.
+    """
+    torch = _torch()
+    _need_cuda(query, kv_cache, block_tables, context_lens, out, workspace)
+    nb, two, hkv, bs, d = kv_cache.shape
+    s, hq, dq = query.shape
+    if two != 2 or dq != d:
+        raise ValueError("query/kv_cache shape mismatch")
+    if query.dtype != kv_cache.dtype:
+        raise TypeError("query and kv_cache must share a dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise TypeError("block_tables must be int32 [S, MB]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (s,):
+        raise TypeError("context_lens must be int32 [S]")
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    if scale is None:
+        scale = d ** -0.5
+    dt = _dtype_code(kv_cache)
+    need = decode_workspace_size(s, hq, hkv, d, bs, mb, int(max_context_len), partition_size,
+                                 dt, kernel)
+    if out is None:
+        out = torch.empty((s, hq, d), dtype=torch.float32, device=query.device)
+    elif out.dtype != torch.float32 or out.shape != (s, hq, d):
+        raise TypeError("out must be float32 [S, Hq, D]")
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
+                           block_tables.data_ptr(), context_lens.data_ptr(), s, hq, hkv, d, bs,
+                           mb, int(max_context_len), nb, float(scale), int(partition_size),
+                           KERNELS[kernel], None if workspace is None else workspace.data_ptr(),
+                           wbytes, None, dt, _stream(query.device, stream)))
+    return out
+
+
+def _ptr(t, ptype):
+    """Raw pointer of a contiguous CPU tensor (no copy)."""
+    if t.is_cuda or not t.is_contiguous():
+        raise ValueError("expected a contiguous CPU tensor")
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ptype)
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------
+class BlockManager:
+    """Handle over the native block manager (``pa_bm_*``; host memory only)."""
+
+    def __init__(self, num_blocks, block_size):
+        self._h = lib().pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise PAError(-1, lib().pa_last_error().decode())
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, seq, num_tokens):
+        _check(lib().pa_bm_allocate(self._h, int(seq), int(num_tokens)))
+        return self.block_table(seq)[0]
+
+    def share(self, seq, blocks, num_tokens):
+        arr = (ctypes.c_int32 * max(1, len(blocks)))(*[int(b) for b in blocks])
+        _check(lib().pa_bm_share(self._h, int(seq), arr, len(blocks), int(num_tokens)))
+
+    def fork(self, parent, child):
+        _check(lib().pa_bm_fork(self._h, int(parent), int(child)))
+
+    def append_slot(self, seq):
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_bm_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
+                                       ctypes.byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def append_slots(self, seqs):
+        """Batched append: returns (slots list, [(src, dst), ...])."""
+        n = len(seqs)
+        sq = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seqs])
+        slots = (ctypes.c_int64 * max(1, n))()
+        pairs = (ctypes.c_int32 * max(2, 2 * n))()
+        k = ctypes.c_int(0)
+        _check(lib().pa_bm_append_slots(self._h, sq, n, slots, pairs, ctypes.byref(k)))
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(k.value)]
+
+    def free(self, seq):
+        _check(lib().pa_bm_free(self._h, int(seq)))
+
+    def block_table(self, seq):
+        n, ntok = ctypes.c_int(0), ctypes.c_int64(0)
+        _check(lib().pa_bm_block_table(self._h, int(seq), None, 0, ctypes.byref(n),
+                                       ctypes.byref(ntok)))
+        buf = (ctypes.c_int32 * max(1, n.value))()
+        _check(lib().pa_bm_block_table(self._h, int(seq), buf, n.value, ctypes.byref(n),
+                                       ctypes.byref(ntok)))
+        return list(buf[:n.value]), ntok.value
+
+    def block_tables(self, seqs, max_blocks):
+        """Padded int32 tables [n, max_blocks] (-1 fill) and int32 lengths, as
+        Python lists of rows (the caller copies them to the device)."""
+        n = len(seqs)
+        sq = (ctypes.c_int64 * max(1, n))(*[int(x) for x in seqs])
+        tab = (ctypes.c_int32 * max(1, n * max_blocks))()
+        lens = (ctypes.c_int32 * max(1, n))()
+        _check(lib().pa_bm_block_tables(self._h, sq, n, tab, int(max_blocks), lens))
+        rows = [list(tab[i * max_blocks:(i + 1) * max_blocks]) for i in range(n)]
+        return rows, list(lens[:n])
+
+    def append_slots_into(self, seqs, slots, cow_pairs):
+        """Batched append writing straight into CPU tensors (e.g. pinned):
+        ``seqs`` int64 [n], ``slots`` int64 [n], ``cow_pairs`` int32 [n, 2].
+        Returns the number of copy pairs written."""
+        n = seqs.numel()
+        k = ctypes.c_int(0)
+        _check(lib().pa_bm_append_slots(self._h, _ptr(seqs, _I64P), n, _ptr(slots, _I64P),
+                                        _ptr(cow_pairs, _I32P), ctypes.byref(k)))
+        return k.value
+
+    def block_tables_into(self, seqs, tables, context_lens):
+        """Fill CPU int32 ``tables`` [n, MB] (-1 padded) and ``context_lens`` [n]."""
+        n = seqs.numel()
+        _check(lib().pa_bm_block_tables(self._h, _ptr(seqs, _I64P), n, _ptr(tables, _I32P),
+                                        tables.shape[1], _ptr(context_lens, _I32P)))
+
+    def stats(self):
+        f, u, s = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(f), ctypes.byref(u), ctypes.byref(s)))
+        return f.value, u.value, s.value
+
+    def ref_count(self, block):
+        r = lib().pa_bm_ref_count(self._h, int(block))
+        if r < 0:
+            _check(r)
+        return r

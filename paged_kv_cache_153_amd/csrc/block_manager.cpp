@@ -1,0 +1,310 @@
+// block_manager.cpp — host block manager behind the pa_bm_* C ABI.
+//
+// A pool of fixed-size physical KV blocks and one block table per sequence
+// ([KVPA] "KV Cache与PagedAttention深度解析" §4.2 block tables, §5.1 block
+// manager duties: free pool, allocate, reclaim, copy-on-write; §5.3 growth
+// by one block when ceil((t+1)/bs) exceeds the table; §8.2-§8.3 reference
+// counts).  Sharing and copy-on-write follow [NANO] (zwxr.cn walkthrough)
+// §2.3: every table holding a block adds one reference; a sequence that is
+// about to write into a block with count > 1 takes a fresh block, copies it
+// (the device copy is the caller's, from the returned pair) and repoints its
+// own table entry, while the other holders keep the original.
+//
+// Policy: the free pool is a stack that starts as [0, 1, ..., NB-1] and hands
+// out from the top, like the pop()/append pool of [KV2P] "KV Cache从原理到实战"
+// §6.2.  Every call checks all its preconditions before it changes anything,
+// so a failing call leaves the manager as it was.  With PA_LOG=1 in the
+// environment every allocation and release is logged to stderr with the
+// sequence, block, count and free-pool size ([NANO] §4.5 logging advice).
+#include <cstdio>
+#include <cstdlib>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "internal.h"
+
+struct pa_bm {
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int64_t num_tokens = 0;
+  };
+  int64_t num_blocks = 0;
+  int block_size = 0;
+  std::vector<int32_t> free_list;  // stack; back() is handed out next
+  std::vector<int32_t> refs;
+  std::unordered_map<int64_t, Seq> seqs;
+  bool log = false;
+
+  int32_t take(int64_t seq) {
+    const int32_t b = free_list.back();
+    free_list.pop_back();
+    refs[b] = 1;
+    if (log)
+      std::fprintf(stderr, "[pa_bm] take seq=%lld block=%d ref=1 free=%zu\n", (long long)seq, b,
+                   free_list.size());
+    return b;
+  }
+  void release(int64_t seq, int32_t b) {
+    refs[b] -= 1;
+    if (refs[b] == 0) free_list.push_back(b);
+    if (log)
+      std::fprintf(stderr, "[pa_bm] drop seq=%lld block=%d ref=%d free=%zu\n", (long long)seq, b,
+                   refs[b], free_list.size());
+  }
+  int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+};
+
+namespace {
+
+using pa::fail;
+
+int need_seq(const pa_bm* bm, int64_t seq) {
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (!bm->seqs.count(seq))
+    return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seq));
+  return PA_OK;
+}
+
+// Fresh blocks the next append of `s` needs, given extra reference drops
+// already planned in this batch (`dropped`).
+int plan_append(const pa_bm* bm, const pa_bm::Seq& s,
+                std::unordered_map<int32_t, int>& dropped) {
+  if (s.num_tokens % bm->block_size == 0) return 1;
+  const int32_t last = s.blocks.back();
+  const int live = bm->refs[last] - dropped[last];
+  if (live > 1) {
+    dropped[last] += 1;
+    return 1;
+  }
+  return 0;
+}
+
+// Apply one append (preconditions already checked).
+void do_append(pa_bm* bm, int64_t seq, pa_bm::Seq& s, int64_t* slot, int32_t* cow_src,
+               int32_t* cow_dst) {
+  const int64_t t = s.num_tokens;
+  const int64_t row = t % bm->block_size;
+  int32_t src = -1, dst = -1;
+  if (row == 0) {
+    s.blocks.push_back(bm->take(seq));
+  } else if (bm->refs[s.blocks.back()] > 1) {
+    src = s.blocks.back();
+    dst = bm->take(seq);
+    bm->release(seq, src);  // stays > 0: another table still holds it
+    s.blocks.back() = dst;
+  }
+  s.num_tokens = t + 1;
+  *slot = (int64_t)s.blocks.back() * bm->block_size + row;
+  *cow_src = src;
+  *cow_dst = dst;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_bm* pa_bm_create(int64_t num_blocks, int block_size) {
+  pa::clear_error();
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || block_size <= 0) {
+    fail(PA_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31) and block_size positive");
+    return nullptr;
+  }
+  pa_bm* bm = new (std::nothrow) pa_bm();
+  if (!bm) return nullptr;
+  try {
+    bm->num_blocks = num_blocks;
+    bm->block_size = block_size;
+    bm->free_list.resize(num_blocks);
+    for (int64_t i = 0; i < num_blocks; ++i) bm->free_list[i] = (int32_t)i;
+    bm->refs.assign(num_blocks, 0);
+    const char* env = std::getenv("PA_LOG");
+    bm->log = env && env[0] == '1';
+  } catch (...) {
+    delete bm;
+    return nullptr;
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+int pa_bm_allocate(pa_bm* bm, int64_t seq, int64_t num_tokens) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "negative token count");
+  if (bm->seqs.count(seq))
+    return fail(PA_ERR_INVALID_ARG, "sequence " + std::to_string(seq) + " already exists");
+  const int64_t needed = bm->blocks_for(num_tokens);
+  if ((int64_t)bm->free_list.size() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
+  try {
+    pa_bm::Seq s;
+    s.blocks.reserve(needed);
+    for (int64_t i = 0; i < needed; ++i) s.blocks.push_back(bm->take(seq));
+    s.num_tokens = num_tokens;
+    bm->seqs.emplace(seq, std::move(s));
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  return PA_OK;
+}
+
+int pa_bm_share(pa_bm* bm, int64_t seq, const int32_t* blocks, int n, int64_t num_tokens) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (n < 0 || (n > 0 && !blocks) || num_tokens < 0 || bm->blocks_for(num_tokens) != n)
+    return fail(PA_ERR_INVALID_ARG, "token count does not match the shared blocks");
+  for (int i = 0; i < n; ++i) {
+    const int32_t b = blocks[i];
+    if (b < 0 || b >= bm->num_blocks || bm->refs[b] == 0)
+      return fail(PA_ERR_INVALID_ARG, "block " + std::to_string(b) + " is not held");
+  }
+  auto it = bm->seqs.find(seq);
+  if (it != bm->seqs.end() && it->second.num_tokens % bm->block_size != 0)
+    return fail(PA_ERR_INVALID_ARG, "sequence ends inside a block");
+  try {
+    pa_bm::Seq& s = bm->seqs[seq];
+    s.blocks.reserve(s.blocks.size() + n);
+    for (int i = 0; i < n; ++i) {
+      bm->refs[blocks[i]] += 1;
+      s.blocks.push_back(blocks[i]);
+    }
+    s.num_tokens += num_tokens;
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  return PA_OK;
+}
+
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+  pa::clear_error();
+  if (int st = need_seq(bm, parent)) return st;
+  if (bm->seqs.count(child))
+    return fail(PA_ERR_INVALID_ARG, "sequence " + std::to_string(child) + " already exists");
+  try {
+    pa_bm::Seq copy = bm->seqs.at(parent);
+    for (int32_t b : copy.blocks) bm->refs[b] += 1;
+    bm->seqs.emplace(child, std::move(copy));
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  return PA_OK;
+}
+
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
+                      int32_t* cow_dst) {
+  pa::clear_error();
+  if (!slot || !cow_src || !cow_dst) return fail(PA_ERR_INVALID_ARG, "null output pointer");
+  if (int st = need_seq(bm, seq)) return st;
+  pa_bm::Seq& s = bm->seqs.at(seq);
+  std::unordered_map<int32_t, int> dropped;
+  if ((int64_t)bm->free_list.size() < plan_append(bm, s, dropped))
+    return fail(PA_ERR_OOM, "out of KV cache blocks");
+  do_append(bm, seq, s, slot, cow_src, cow_dst);
+  return PA_OK;
+}
+
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int64_t* slots,
+                       int32_t* cow_pairs, int* num_cow) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_cow)
+    return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  std::unordered_set<int64_t> seen;
+  std::unordered_map<int32_t, int> dropped;
+  int64_t needed = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!seen.insert(seqs[i]).second)
+      return fail(PA_ERR_INVALID_ARG, "sequence repeated in one batch");
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seqs[i]));
+    // fail at the first sequence that would not fit, as a sequential run would
+    needed += plan_append(bm, it->second, dropped);
+    if ((int64_t)bm->free_list.size() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
+  }
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    int32_t src, dst;
+    do_append(bm, seqs[i], bm->seqs.at(seqs[i]), &slots[i], &src, &dst);
+    if (src >= 0) {
+      cow_pairs[2 * k] = src;
+      cow_pairs[2 * k + 1] = dst;
+      ++k;
+    }
+  }
+  *num_cow = k;
+  return PA_OK;
+}
+
+int pa_bm_free(pa_bm* bm, int64_t seq) {
+  pa::clear_error();
+  if (int st = need_seq(bm, seq)) return st;
+  auto it = bm->seqs.find(seq);
+  for (int32_t b : it->second.blocks) bm->release(seq, b);
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+int pa_bm_block_table(const pa_bm* bm, int64_t seq, int32_t* out, int cap, int* n,
+                      int64_t* num_tokens) {
+  pa::clear_error();
+  if (int st = need_seq(bm, seq)) return st;
+  if (cap < 0 || (cap > 0 && !out)) return fail(PA_ERR_INVALID_ARG, "bad output buffer");
+  const pa_bm::Seq& s = bm->seqs.at(seq);
+  const int len = (int)s.blocks.size();
+  for (int i = 0; i < len && i < cap; ++i) out[i] = s.blocks[i];
+  if (n) *n = len;
+  if (num_tokens) *num_tokens = s.num_tokens;
+  return PA_OK;
+}
+
+int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int n, int32_t* tables,
+                       int max_blocks, int32_t* context_lens) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (n < 0 || max_blocks <= 0 || (n > 0 && (!seqs || !tables || !context_lens)))
+    return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  for (int i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end())
+      return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seqs[i]));
+    if ((int64_t)it->second.blocks.size() > max_blocks)
+      return fail(PA_ERR_INVALID_ARG, "table longer than max_blocks");
+    if (it->second.num_tokens > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "context length does not fit int32");
+  }
+  for (int i = 0; i < n; ++i) {
+    const pa_bm::Seq& s = bm->seqs.at(seqs[i]);
+    int32_t* row = tables + (int64_t)i * max_blocks;
+    const int len = (int)s.blocks.size();
+    for (int j = 0; j < max_blocks; ++j) row[j] = j < len ? s.blocks[j] : -1;
+    context_lens[i] = (int32_t)s.num_tokens;
+  }
+  return PA_OK;
+}
+
+int pa_bm_stats(const pa_bm* bm, int64_t* num_free, int64_t* num_used, int64_t* num_shared) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  int64_t used = 0, shared = 0;
+  for (int32_t c : bm->refs) {
+    used += c >= 1;
+    shared += c >= 2;
+  }
+  if (num_free) *num_free = (int64_t)bm->free_list.size();
+  if (num_used) *num_used = used;
+  if (num_shared) *num_shared = shared;
+  return PA_OK;
+}
+
+int pa_bm_ref_count(const pa_bm* bm, int32_t block) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (block < 0 || block >= bm->num_blocks) return fail(PA_ERR_INVALID_ARG, "block out of range");
+  return bm->refs[block];
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// device_common.h — small gfx950 device helpers shared by the kernels.
+//
+// Wave64 lane reductions use DPP row operations (quad permutes and row
+// mirrors move data between lanes of one 16-lane row inside the VALU
+// instruction itself); steps across rows use ds_swizzle / bpermute, which
+// run on the LDS crossbar without touching LDS memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// log2(e): softmax weights are computed as exp2(z * scale * log2(e) - m).
+constexpr float kLog2e = 1.4426950408889634f;
+// Running-max start value: finite so that exp2(m_old - m_new) never sees
+// (-inf) - (-inf).  Any real scaled score is far above it.
+constexpr float kMaxInit = -1.0e30f;
+
+// DPP controls (gfx9 encoding).
+enum : int {
+  kQuadSwap1 = 0xB1,    // quad_perm [1,0,3,2]: lane ^ 1
+  kQuadSwap2 = 0x4E,    // quad_perm [2,3,0,1]: lane ^ 2
+  kRowHalfMirror = 0x141,  // lane i <-> 7 - i inside each half row
+  kRowMirror = 0x140,      // lane i <-> 15 - i inside each row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of N consecutive lanes (N in {1,2,4,8,16,32,64}); every lane
+// of a group receives the group sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<kQuadSwap1>(x);
+  if constexpr (N >= 4) x += dpp_mov<kQuadSwap2>(x);
+  if constexpr (N >= 8) x += dpp_mov<kRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_mov<kRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Butterfly over lanes that differ in the bits FROM..32 (FROM a power of two):
+// combines the rows of a wave that hold the same columns.
+template <int FROM>
+__device__ __forceinline__ float cross_rows_max(float x) {
+  if constexpr (FROM <= 1) x = fmaxf(x, __shfl_xor(x, 1));
+  if constexpr (FROM <= 2) x = fmaxf(x, __shfl_xor(x, 2));
+  if constexpr (FROM <= 4) x = fmaxf(x, __shfl_xor(x, 4));
+  if constexpr (FROM <= 8) x = fmaxf(x, __shfl_xor(x, 8));
+  if constexpr (FROM <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (FROM <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+template <int FROM>
+__device__ __forceinline__ float cross_rows_sum(float x) {
+  if constexpr (FROM <= 1) x += __shfl_xor(x, 1);
+  if constexpr (FROM <= 2) x += __shfl_xor(x, 2);
+  if constexpr (FROM <= 4) x += __shfl_xor(x, 4);
+  if constexpr (FROM <= 8) x += __shfl_xor(x, 8);
+  if constexpr (FROM <= 16) x += __shfl_xor(x, 16);
+  if constexpr (FROM <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int readlane(int x, int lane) {
+  return __builtin_amdgcn_readlane(x, lane);
+}
+
+// 16-byte global load that bypasses nothing: plain global_load_dwordx4.
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+template <typename T>
+struct DType;
+template <>
+struct DType<float> {
+  static constexpr int kBytes = 4;
+};
+template <>
+struct DType<half_t> {
+  static constexpr int kBytes = 2;
+};
+
+}  // namespace pa

@@ -1,0 +1,273 @@
+// pa_api.cpp — C ABI for the device calls: argument checks, partition
+// choice, workspace sizing and kernel dispatch.
+//
+// The library allocates no device memory.  Split-context partials live in a
+// caller-provided workspace whose size this file computes; every kernel is
+// enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "internal.h"
+#include "kernels.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool check_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_CHECK");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+// Partition size used when the caller passes 0.  Single pass keeps one
+// workgroup per (sequence, KV head); it is chosen only when that already
+// gives several workgroups per compute unit and contexts are short enough
+// that per-workgroup imbalance stays small.
+int choose_partition(int num_seqs, int num_kv_heads, int max_context_len) {
+  const long pairs = (long)num_seqs * num_kv_heads;
+  if (max_context_len <= 512) return -1;
+  if (pairs >= 1024 && max_context_len <= 8192) return -1;
+  return 512;
+}
+
+struct Plan {
+  int single = 1;
+  int part_tokens = 0;
+  int num_parts = 1;
+  size_t ws_bytes = 0;
+  size_t off_m = 0, off_l = 0;
+};
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+Plan make_plan(int num_seqs, int num_q_heads, int head_dim, int max_tokens, int partition) {
+  Plan p;
+  if (partition < 0) {
+    p.single = 1;
+    p.num_parts = 1;
+    p.part_tokens = (max_tokens + kTile - 1) / kTile * kTile + kTile;
+    return p;
+  }
+  p.single = 0;
+  p.part_tokens = partition;
+  p.num_parts = max_tokens <= 0 ? 1 : (max_tokens + partition - 1) / partition;
+  const size_t rows = (size_t)num_seqs * num_q_heads * p.num_parts;
+  const size_t bytes_o = round_up(rows * head_dim * sizeof(float));
+  const size_t bytes_ml = round_up(rows * sizeof(float));
+  p.off_m = bytes_o;
+  p.off_l = bytes_o + bytes_ml;
+  p.ws_bytes = bytes_o + 2 * bytes_ml;
+  return p;
+}
+
+// PA_CHECK=1: copy index arrays to the host and validate them.
+int check_decode_arrays(const int32_t* bt, const int32_t* cl, int num_seqs, int max_blocks,
+                        int block_size, int max_context_len, int64_t num_blocks,
+                        hipStream_t stream) {
+  std::vector<int32_t> lens(num_seqs), table((size_t)num_seqs * max_blocks);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(lens.data(), cl, lens.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(table.data(), bt, table.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(PA_ERR_HIP, "PA_CHECK: copying tables to the host failed");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = lens[s];
+    if (n < 0 || n > max_context_len || (int64_t)n > (int64_t)max_blocks * block_size)
+      return fail(PA_ERR_INVALID_ARG, "PA_CHECK: context_lens[" + std::to_string(s) +
+                                          "] out of range");
+    const int nb = (n + block_size - 1) / block_size;
+    for (int i = 0; i < nb; ++i) {
+      const int32_t b = table[(size_t)s * max_blocks + i];
+      if (b < 0 || b >= num_blocks)
+        return fail(PA_ERR_INVALID_ARG, "PA_CHECK: block_tables[" + std::to_string(s) + "," +
+                                            std::to_string(i) + "] out of range");
+    }
+  }
+  return PA_OK;
+}
+
+int check_write_arrays(const int64_t* slots, int64_t num_tokens, const int32_t* pairs,
+                       int64_t num_cow, int64_t num_blocks, int block_size, hipStream_t stream) {
+  std::vector<int64_t> sl(num_tokens);
+  std::vector<int32_t> pr(2 * num_cow);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      (num_tokens && hipMemcpy(sl.data(), slots, sl.size() * 8, hipMemcpyDeviceToHost)) ||
+      (num_cow && hipMemcpy(pr.data(), pairs, pr.size() * 4, hipMemcpyDeviceToHost)))
+    return fail(PA_ERR_HIP, "PA_CHECK: copying slots to the host failed");
+  std::unordered_set<int64_t> seen;
+  for (int64_t s : sl) {
+    if (s < 0) continue;
+    if (s >= num_blocks * block_size) return fail(PA_ERR_INVALID_ARG, "PA_CHECK: slot out of range");
+    if (!seen.insert(s).second) return fail(PA_ERR_INVALID_ARG, "PA_CHECK: duplicate slot");
+  }
+  std::unordered_set<int32_t> srcs, dsts;
+  for (int64_t k = 0; k < num_cow; ++k) {
+    const int32_t a = pr[2 * k], b = pr[2 * k + 1];
+    if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks || a == b)
+      return fail(PA_ERR_INVALID_ARG, "PA_CHECK: bad copy pair");
+    srcs.insert(a);
+    if (!dsts.insert(b).second) return fail(PA_ERR_INVALID_ARG, "PA_CHECK: repeated destination");
+  }
+  for (int32_t b : dsts)
+    if (srcs.count(b)) return fail(PA_ERR_INVALID_ARG, "PA_CHECK: a destination is also a source");
+  return PA_OK;
+}
+
+}  // namespace
+
+int fail(int status, const std::string& message) {
+  g_last_error = message;
+  return status;
+}
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace pa
+
+using pa::aligned16;
+using pa::fail;
+
+extern "C" {
+
+const char* pa_strerror(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_OOM: return "out of KV cache blocks";
+    case PA_ERR_NOT_FOUND: return "unknown sequence";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
+
+const char* pa_version(void) { return "pa 0.1 gfx950"; }
+
+int pa_cache_write(const void* key, const void* value, void* kv_cache,
+                   const int64_t* slot_mapping, int64_t num_tokens, const int32_t* cow_pairs,
+                   int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                   int block_size, int dtype, void* stream_) {
+  pa::clear_error();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype");
+  const int eb = dtype == PA_F32 ? 4 : 2;
+  if (num_tokens < 0 || num_cow < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
+  if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
+  if ((head_dim * eb) % 16) return fail(PA_ERR_UNSUPPORTED, "head_dim * element size % 16 != 0");
+  if (!kv_cache || !aligned16(kv_cache)) return fail(PA_ERR_INVALID_ARG, "kv_cache null/unaligned");
+  if (num_tokens > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
+    return fail(PA_ERR_INVALID_ARG, "key/value/slot_mapping null or unaligned");
+  if (num_cow > 0 && !cow_pairs) return fail(PA_ERR_INVALID_ARG, "cow_pairs null");
+  if (num_tokens == 0 && num_cow == 0) return PA_OK;
+  if (pa::check_mode()) {
+    if (int st = pa::check_write_arrays(slot_mapping, num_tokens, cow_pairs, num_cow, num_blocks,
+                                        block_size, stream))
+      return st;
+  }
+  const int rc = pa::launch_cache_write(key, value, kv_cache, slot_mapping, num_tokens, cow_pairs,
+                                        num_cow, num_blocks, num_kv_heads, head_dim, block_size,
+                                        eb, stream);
+  if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
+  return rc ? fail(PA_ERR_UNSUPPORTED, "cache write") : PA_OK;
+}
+
+int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+              int head_dim, int block_size, int max_blocks_per_seq, int max_context_len,
+              int64_t num_blocks, float scale, int partition_size, int kernel, void* workspace,
+              size_t workspace_bytes, size_t* workspace_needed, int dtype, void* stream_) {
+  pa::clear_error();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (workspace_needed) *workspace_needed = 0;
+  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype");
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes out of range");
+  if (num_q_heads % num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_q_heads % num_kv_heads");
+  const int group = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim");
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size");
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "group size");
+  if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA) return fail(PA_ERR_INVALID_ARG, "kernel");
+  if (kernel == PA_KERNEL_MFMA && (dtype != PA_F16 || group < 2))
+    return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs f16 and a query group of 2 or more");
+  if (partition_size < -1 ||
+      (partition_size > 0 && (partition_size % pa::kTile || partition_size % block_size)))
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be -1, 0 or a multiple of 16 and "
+                                    "block_size");
+  const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
+  if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  const int max_tokens = (int)max_tokens_ll;
+  const int ctx = max_context_len < max_tokens ? max_context_len : max_tokens;
+  int part = partition_size;
+  if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx);
+  const pa::Plan plan = pa::make_plan(num_seqs, num_q_heads, head_dim, ctx, part);
+  if (workspace_needed) *workspace_needed = plan.ws_bytes;
+  if (!out) return PA_OK;  // size query
+  if (num_seqs == 0) return PA_OK;
+  if (!query || !kv_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache))
+    return fail(PA_ERR_INVALID_ARG, "out/query/kv_cache must be 16-byte aligned");
+  if (plan.ws_bytes && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+    return fail(PA_ERR_WORKSPACE, "workspace of " + std::to_string(plan.ws_bytes) +
+                                      " bytes (16-byte aligned) needed");
+  if (pa::check_mode()) {
+    if (int st = pa::check_decode_arrays(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                         block_size, max_context_len, num_blocks, stream))
+      return st;
+  }
+  pa::DecodeArgs a{};
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
+  a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.q = query;
+  a.kv = kv_cache;
+  a.bt = block_tables;
+  a.cl = context_lens;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_tokens = max_tokens;
+  a.num_parts = plan.num_parts;
+  a.part_tokens = plan.part_tokens;
+  a.single = plan.single;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  int use = kernel;
+  if (use == PA_KERNEL_AUTO) use = PA_KERNEL_VALU;
+  int rc = use == PA_KERNEL_MFMA
+               ? pa::launch_decode_mfma(a, dtype, head_dim, block_size, group, 4, stream)
+               : pa::launch_decode_valu(a, dtype, head_dim, block_size, group, 4, stream);
+  if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
+  if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
+  if (!plan.single) {
+    rc = pa::launch_merge(a, head_dim, stream);
+    if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no merge kernel for this head_dim");
+    if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+"""GPU parity for pa_decode against the fp64 oracle (max-abs error <= 5e-4 in
+fp32), over every supported shape, both kernel families, single pass and
+split context, and the edge cases of the method."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_153_amd as pa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-4
+
+
+def run_decode(x, device, **kw):
+    g = x.to(device)
+    out = pa.decode(g.q, g.kv_cache, g.block_tables, g.context_lens, scale=x.scale,
+                    max_context_len=int(x.context_lens.max()) if len(x.context_lens) else 0, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def ref_decode(x):
+    return oracle.decode_ref(x.q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                             x.context_lens.numpy(), x.scale)
+
+
+MFMA_BUILT = False
+
+
+def kernels_for(x):
+    ks = ["valu"]
+    if MFMA_BUILT and x.kv_cache.dtype == torch.float16 and x.num_q_heads // x.num_kv_heads >= 2:
+        ks.append("mfma")
+    return ks
+
+
+def check(x, device, parts=(-1, 0, 16, 64), kernels=None, tol=TOL):
+    want = ref_decode(x)
+    for kern in kernels or kernels_for(x):
+        for part in parts:
+            if part > 0 and (part % x.block_size or part % 16):
+                continue
+            print(f"  {x.name} kernel={kern} part={part}", flush=True)
+            got = run_decode(x, device, partition_size=part, kernel=kern)
+            err = np.abs(got - want).max() if want.size else 0.0
+            assert np.isfinite(got).all(), (kern, part)
+            assert err <= tol, (kern, part, err)
+
+
+# --------------------------------------------------------------------------
+def test_tiny_fp32_mha(device):
+    """4 seqs, MHA 8 x 64, fp32, block 16, lengths 100/37/16/1, scale 1/8."""
+    check(synth.tiny(seed=0), device, parts=(-1, 0, 16, 32, 48, 64))
+
+
+def test_tiny_unused_rows_poisoned_with_nan(device):
+    """Rows past each context (tail of the partial block and blocks no table
+    uses) hold NaN: the output must not see them."""
+    x = synth.tiny(seed=1, fill_unused=float("nan"))
+    assert torch.isnan(x.kv_cache).any()
+    check(x, device, parts=(-1, 16, 32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
+def test_shapes_ragged(device, dtype, bs, d, hq, hkv):
+    lens = [1, 15, 16, 17, 100, 255, 513, 1030]
+    x = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype=dtype, seed=bs + d + hq,
+                                 fill_unused=float("nan"), name=f"{dtype}-bs{bs}-d{d}-{hq}/{hkv}")
+    check(x, device, parts=(-1, 0, 32, 512))
+
+
+def test_single_token_is_exact(device):
+    """n = 1: the only weight is exp2(0) = 1, so out == V row bit for bit."""
+    for dtype in ("f16", "f32"):
+        x = synth.make_decode_inputs([1] * 5, 16, 2, 128, 16, dtype=dtype, seed=3)
+        for kern in kernels_for(x):
+            got = run_decode(x, device, kernel=kern, partition_size=-1)
+            want = ref_decode(x)
+            assert np.array_equal(got, want), (dtype, kern)
+
+
+def test_zero_length_sequences(device):
+    x = synth.make_decode_inputs([0, 37, 0, 1], 8, 2, 128, 16, dtype="f16", seed=4)
+    for kern in kernels_for(x):
+        for part in (-1, 0, 16):
+            got = run_decode(x, device, kernel=kern, partition_size=part)
+            assert np.all(got[0] == 0) and np.all(got[2] == 0)
+            assert np.abs(got - ref_decode(x)).max() <= TOL
+
+
+def test_scale_zero_gives_mean_of_values(device):
+    x = synth.make_decode_inputs([33, 200], 8, 2, 128, 16, dtype="f16", seed=5, scale=0.0)
+    check(x, device, parts=(-1, 32))
+
+
+def test_physical_permutation_invariance(device):
+    """Moving blocks in the pool and renaming them in the tables changes
+    nothing: the kernel's arithmetic order depends only on logical order."""
+    x = synth.make_decode_inputs([300, 77, 1024], 32, 8, 128, 16, dtype="f16", seed=6)
+    perm = torch.randperm(x.kv_cache.shape[0], generator=synth._gen(99, "cpu"))
+    kv2 = torch.empty_like(x.kv_cache)
+    kv2[perm] = x.kv_cache
+    bt2 = torch.where(x.block_tables >= 0, perm[x.block_tables.clamp(min=0).long()].int(),
+                      x.block_tables)
+    y = synth.DecodeInputs("perm", x.q, kv2, bt2, x.context_lens, x.scale, x.seed)
+    for kern in kernels_for(x):
+        for part in (-1, 512):
+            a = run_decode(x, device, kernel=kern, partition_size=part)
+            b = run_decode(y, device, kernel=kern, partition_size=part)
+            assert np.array_equal(a, b), (kern, part)
+
+
+def test_split_agrees_with_single(device):
+    x = synth.make_decode_inputs([4096, 3000, 17], 32, 8, 128, 16, dtype="f16", seed=7)
+    want = ref_decode(x)
+    for kern in kernels_for(x):
+        single = run_decode(x, device, kernel=kern, partition_size=-1)
+        for part in (16, 256, 512, 4096):
+            split = run_decode(x, device, kernel=kern, partition_size=part)
+            assert np.abs(split - single).max() <= TOL
+            assert np.abs(split - want).max() <= TOL
+
+
+def test_peaked_softmax(device):
+    """Large logits: one token dominates each head; scores ~ +/-100."""
+    x = synth.make_decode_inputs([700, 64], 16, 2, 128, 16, dtype="f16", seed=8, scale=1.0)
+    check(x, device, parts=(-1, 64))
+
+
+def test_table_width_larger_than_needed(device):
+    """Tables padded with -1 beyond each sequence's blocks, max_blocks > needed."""
+    x = synth.make_decode_inputs([40, 3], 8, 8, 64, 8, dtype="f32", seed=9, max_blocks=20)
+    check(x, device, parts=(-1, 16))
+
+
+# --------------------------------------------------------------------------
+# workload-shaped cases at oracle-friendly sizes
+# --------------------------------------------------------------------------
+def test_llama7b_mha_shape_small(device):
+    check(synth.llama7b_mha(seed=0, num_seqs=3, context=700), device, parts=(-1, 0, 512))
+
+
+def test_gqa7b_shape_small(device):
+    check(synth.gqa7b(seed=0, num_seqs=6, lo=128, hi=2100), device, parts=(-1, 0, 512))
+
+
+def test_llama70b_shape_small(device):
+    check(synth.llama70b(seed=0, num_seqs=2, context=2600), device, parts=(-1, 0, 512))
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_shared_prefix_shape_small(device, bs):
+    x = synth.shared_prefix(seed=0, block_size=bs, num_seqs=6, prefix=512, suffix_hi=300)
+    check(x, device, parts=(-1, 0, 512))
+
+
+# --------------------------------------------------------------------------
+# full workload sizes, default (benchmarked) launch, sampled outputs
+# --------------------------------------------------------------------------
+def _sampled_check(x_dev, out, samples):
+    """Oracle one (sequence, head) at a time on the host copy of that
+    sequence's blocks only."""
+    bs = x_dev.block_size
+    for s, h in samples:
+        n = int(x_dev.context_lens[s])
+        nblk = -(-n // bs)
+        ids = x_dev.block_tables[s, :nblk].long()
+        blocks = x_dev.kv_cache[ids].cpu().numpy()
+        q = x_dev.q[s:s + 1].cpu().numpy()
+        want = oracle.decode_ref(q, blocks, np.arange(nblk)[None], np.array([n]), x_dev.scale)
+        got = out[s, h].cpu().numpy().astype(np.float64)
+        err = np.abs(got - want[0, h]).max()
+        assert err <= TOL, (s, h, err)
+
+
+@pytest.mark.parametrize("name", ["llama7b_mha", "gqa7b", "llama70b"])
+def test_full_size_sampled(device, name):
+    print(f"full-size {name}", flush=True)
+    x = synth.WORKLOADS[name](seed=0, device=device)
+    out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
+                    max_context_len=int(x.context_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    S, Hq = x.num_seqs, x.num_q_heads
+    rng = np.random.default_rng(0)
+    samples = [(0, 0), (S - 1, Hq - 1)] + [(int(rng.integers(S)), int(rng.integers(Hq)))
+                                           for _ in range(4)]
+    _sampled_check(x, out, samples)
+    del x, out
+    torch.cuda.empty_cache()

@@ -65,6 +65,39 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def source_fingerprint():
+    """sha256 (first 16 hex) over the device sources and the dispatch code, in
+    name order: the key under which measured counter figures stay valid."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_153_amd", "csrc")
+    files = sorted(f for f in glob.glob(os.path.join(csrc, "*"))
+                   if f.endswith((".hip", ".h")) or f.endswith("pa_api.cpp"))
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode dispatch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none for this workload or the kernels changed since it was taken."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"decode_*_{workload}.md"))):
+        fields = {}
+        for line in open(path):
+            if " = " in line:
+                k, v = line.split(" = ", 1)
+                fields[k.strip()] = v.strip()
+        if "traffic_bytes_per_dispatch" not in fields:
+            continue
+        if fields.get("kernel_source_fingerprint") == source_fingerprint():
+            return int(fields["traffic_bytes_per_dispatch"])
+    return None
+
+
 class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
@@ -229,26 +262,45 @@ class Step:
         return q, pool, bt, np.array(lns), pos_t
 
 
-def cpu_baseline(st, budget_s=12.0):
-    """Time the fp64 oracle on a bounded sample of the step (1 thread)."""
-    import numpy as np
+def cpu_baseline(st, budget_s=10.0, cap_s=30.0):
+    """Time the fp64 oracle (1 thread) on the last step's sequences, cycling
+    through them until about ``budget_s`` of CPU time has been spent."""
     from threadpoolctl import threadpool_limits
     import oracle
-    order = list(range(st.S))
-    done, t_used, nbytes, toks = 0, 0.0, 0, 0
+    runs, t_used, nbytes, toks = 0, 0.0, 0, 0
     with threadpool_limits(1):
-        while done < len(order) and t_used < budget_s:
-            q, pool, bt, lens, _ = st.host_inputs([order[done]])
+        while (runs < st.S and t_used < cap_s) or t_used < budget_s:
+            q, pool, bt, lens, _ = st.host_inputs([runs % st.S])
             t0 = time.perf_counter()
             oracle.decode_ref(q, pool, bt, lens, st.scale)
             t_used += time.perf_counter() - t0
             nbytes += int(lens.sum()) * 2 * st.Hkv * st.D * st.elem
             toks += int(lens.sum())
-            done += 1
+            runs += 1
     return dict(value=round(nbytes / t_used / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"fp64 NumPy oracle, 1 thread, on {done} of {st.S} sequences of the last "
-                       f"timed step ({toks} context tokens, {nbytes} KV bytes) in {t_used:.2f} s; "
+                sample=f"fp64 NumPy oracle, 1 thread, {runs} sequence decodes taken in turn "
+                       f"from the {st.S} sequences of the last timed step ({toks} context "
+                       f"tokens, {nbytes} KV bytes) in {t_used:.2f} s; "
                        f"{toks / t_used:.4g} seq*ctx tokens/s")
+
+
+def calibrate_copy(dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) and as a streaming reference."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / reps
+    return {"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+            "dispatches": reps + 1, "copy_GBps_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}
 
 
 def parity_sample(st, samples=3):
@@ -274,6 +326,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -288,6 +342,9 @@ def main():
         sys.exit(1)
     pa.lib()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        print(json.dumps(calibrate_copy(dev)), flush=True)
+        return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
               args.partition, dev)
     log(f"[bench] warmup {args.warmup} steps")
@@ -352,7 +409,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload)
+            if (args.kernel, args.partition) == ("auto", 0) else None,
         },
         "cpu_baseline": cpu,
     }

@@ -1,6 +1,323 @@
-// decode_mfma.hip — placeholder until the matrix-core kernel lands.
+// decode_mfma.hip — paged decode attention on the matrix cores (gfx950, f16).
+//
+// Same computation and work decomposition as decode_valu.hip ([KVPA] "KV
+// Cache与PagedAttention深度解析" §2.1, §4.3, §7.2; [NANO] zwxr.cn walkthrough
+// §2.4): one workgroup per (sequence, KV head, partition), NW independent
+// waves over 16-token tiles, online softmax per wave, LDS merge at the end.
+// With grouped-query attention ([KV2P] "KV Cache从原理到实战" §5.3) the G query
+// heads that share a KV head make q K^T a real [G x D] x [D x 16] product per
+// tile, so the two contractions run as MFMA tiles with the G heads padded to
+// 16 columns:
+//
+//  * S^T[t][h] = sum_d K[t][d] q[h][d] with v_mfma_f32_16x16x32_f16 over D/32
+//    steps.  A = K (lane l: token l%16, eight consecutive d of the chunk
+//    4j + l/16), B = q (lane l: head l%16, same d).  Each K load instruction
+//    covers 64 contiguous bytes of all 16 rows of the tile.
+//  * The C layout of that product (lane l: tokens 4*(l/16)+i of head l%16)
+//    is exactly the B layout that v_mfma_f32_16x16x16f16 needs for P^T, so
+//    O^T[d][h] += sum_t V^T[d][t] P^T[t][h] needs no lane shuffle.  Its A
+//    operand (lane l: 4 consecutive tokens at one d) comes from V rows loaded
+//    128-bit coalesced (lane l: row 4*(l/16)+i, 16-byte chunk l%16) and
+//    paired with v_perm_b32; the MFMA row index m = l%16 then stands for
+//    d = 8m + e in block e, a relabelling undone when the output is written.
+//  * The softmax weights are split into fp16 hi + lo parts (two MFMAs per V
+//    block) so P.V keeps about 22 significant bits; they are scaled by 2^15
+//    first, so weights down to ~2e-9 of the running max stay normal fp16.
+//    The sum l uses the same scaled weights, so the scale cancels in O / l.
+//  * The running max per head needs one max across the four lane groups
+//    (two butterfly steps); everything else stays in the lane.
+#include "device_common.h"
 #include "kernels.h"
 
 namespace pa {
-int launch_decode_mfma(const DecodeArgs&, int, int, int, int, int, hipStream_t) { return 1; }
+namespace {
+
+constexpr float kPScale = 32768.f;  // 2^15
+
+template <int D>
+struct VRow;  // per-lane share of one V row: 16 bytes (D=128) or 8 bytes (D=64)
+template <>
+struct VRow<128> {
+  using type = u32x4_t;
+  static __device__ __forceinline__ type load(const half_t* p) { return load16(p); }
+  static __device__ __forceinline__ type zero() { return type{0u, 0u, 0u, 0u}; }
+};
+template <>
+struct VRow<64> {
+  using type = u32x2_t;
+  static __device__ __forceinline__ type load(const half_t* p) {
+    return *reinterpret_cast<const u32x2_t*>(p);
+  }
+  static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
+};
+
+template <int D, int BS, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(G >= 1 && G <= 16, "group");
+  constexpr int KS = D / 32;                 // 16x16x32 steps for q.K
+  constexpr int VH = D / 16;                 // halves of one V row per lane
+  constexpr int NE = VH;                     // P.V blocks of 16 output rows
+  constexpr int BPT = BS >= kTile ? 1 : kTile / BS;
+  static_assert(BPT <= 2, "a tile spans at most two blocks");
+  using VR = VRow<D>;
+  using vrow_t = typename VR::type;
+
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int quad = lane >> 4;
+  const int col = lane & 15;
+
+  int bid = blockIdx.x;
+  const int g = bid % a.num_kv_heads;
+  bid /= a.num_kv_heads;
+  const int p = bid % a.num_parts;
+  const int s = bid / a.num_parts;
+  const int Hq = a.num_q_heads;
+
+  int n = a.cl[s];
+  n = n < 0 ? 0 : n;
+  n = min(n, a.max_tokens);
+  const int t_begin = p * a.part_tokens;
+  if (t_begin >= n) {
+    if (a.single) {
+      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
+        a.out[((size_t)s * Hq + g * G) * D + idx] = 0.f;
+    }
+    return;
+  }
+  const int t_end = min(n, t_begin + a.part_tokens);
+  const int tile_begin = t_begin / kTile;
+  const int tile_end = (t_end + kTile - 1) / kTile;
+
+  // ---- q as the B operand of q.K: lane (quad, col) = head col, chunk 4j+quad
+  half8_t qb[KS];
+  {
+    const half_t* qh = reinterpret_cast<const half_t*>(a.q) + ((size_t)s * Hq + g * G) * D;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      if (col < G)
+        qb[j] = __builtin_bit_cast(half8_t, load16(qh + col * D + (4 * j + quad) * 8));
+      else
+        qb[j] = __builtin_bit_cast(half8_t, u32x4_t{0u, 0u, 0u, 0u});
+    }
+  }
+
+  const size_t head_stride = (size_t)BS * D;
+  const size_t block_stride = 2 * (size_t)a.num_kv_heads * head_stride;
+  const size_t v_offset = (size_t)a.num_kv_heads * head_stride;
+  const half_t* kvh = reinterpret_cast<const half_t*>(a.kv) + (size_t)g * head_stride;
+  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
+
+  int ids[BPT];
+  auto load_ids = [&](int k0) {
+    const int tile = tile_begin + w + (k0 + lane) * NW;
+#pragma unroll
+    for (int jj = 0; jj < BPT; ++jj) {
+      const int lb = BS >= kTile ? tile * kTile / BS : tile * BPT + jj;
+      int v = 0;
+      if (tile < tile_end && lb < a.max_blocks) {
+        v = bt_row[lb];
+        if (v < 0 || v >= a.num_blocks) v = 0;
+      }
+      ids[jj] = v;
+    }
+  };
+
+  float m = kMaxInit;  // running max of head `col` (same in all four quads)
+  float l = 0.f;       // this lane's share of the (2^15-scaled) weight sum
+  float4_t acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const float cs = a.scale_log2;
+
+  u32x4_t kA[KS], kB[KS];
+  vrow_t vA[4], vB[4];
+
+  auto issue = [&](int tile, int k_it, u32x4_t (&kr)[KS], vrow_t (&vr)[4]) {
+    const int sel = k_it & 63;
+    int blk[BPT];
+#pragma unroll
+    for (int jj = 0; jj < BPT; ++jj) blk[jj] = readlane(ids[jj], sel);
+    const int row0 = BS > kTile ? (tile % (BS / kTile)) * kTile : 0;
+    {  // K: token `col` of the tile
+      const int b = BPT == 1 ? blk[0] : blk[BPT - 1 < 1 ? 0 : (col >= BS ? 1 : 0)];
+      const int row = BS >= kTile ? row0 + col : col % BS;
+      const half_t* base = kvh + (size_t)b * block_stride + row * D;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kr[j] = load16(base + (4 * j + quad) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // V: row 4*quad + i, chunk col
+      const int t = 4 * quad + i;
+      const int b = BPT == 1 ? blk[0] : blk[BPT - 1 < 1 ? 0 : (t >= BS ? 1 : 0)];
+      const int row = BS >= kTile ? row0 + t : t % BS;
+      vr[i] = VR::load(kvh + (size_t)b * block_stride + v_offset + row * D + col * VH);
+    }
+  };
+
+  auto compute = [&](int tile, u32x4_t (&kr)[KS], vrow_t (&vr)[4]) {
+    float4_t sc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[j]), qb[j], sc,
+                                                   0, 0, 0);
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = sc[i] * cs;
+    if ((tile + 1) * kTile > n) {  // partial tile: rows at or past n
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (tile * kTile + 4 * quad + i >= n) {
+          y[i] = -INFINITY;
+          vr[i] = VR::zero();
+        }
+      }
+    }
+    float ym = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+    ym = fmaxf(ym, __shfl_xor(ym, 16));
+    ym = fmaxf(ym, __shfl_xor(ym, 32));
+    const float m_new = fmaxf(m, ym);
+    const float alpha = fast_exp2(m - m_new);
+    // exp2 first, then an exact power-of-two scale: the max token weighs
+    // exactly 2^15, so a lone token reproduces its V row bit for bit
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = col < G ? fast_exp2(y[i] - m_new) * kPScale : 0.f;
+    l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
+    // fp16 hi + lo split of the weights (B operand of P.V)
+    const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
+    const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
+    const auto l01 = __builtin_amdgcn_cvt_pkrtz(pw[0] - (float)h01[0], pw[1] - (float)h01[1]);
+    const auto l23 = __builtin_amdgcn_cvt_pkrtz(pw[2] - (float)h23[0], pw[3] - (float)h23[1]);
+    const half4_t phi = __builtin_bit_cast(
+        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+    const half4_t plo = __builtin_bit_cast(
+        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      // A operand: tokens 4*quad .. 4*quad+3 of dim (chunk col, half e)
+      const int wd = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t d0 = __builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel);
+      const uint32_t d1 = __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel);
+      const half4_t av = __builtin_bit_cast(half4_t, u32x2_t{d0, d1});
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[e], 0, 0, 0);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[e], 0, 0, 0);
+    }
+    m = m_new;
+  };
+
+  int tile = tile_begin + w;
+  int k_it = 0;
+  load_ids(0);
+  if (tile < tile_end) issue(tile, 0, kA, vA);
+  while (tile < tile_end) {
+    int nxt = tile + NW;
+    if (nxt < tile_end) {
+      if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
+      issue(nxt, k_it + 1, kB, vB);
+    }
+    compute(tile, kA, vA);
+    tile = nxt;
+    ++k_it;
+    if (tile >= tile_end) break;
+    nxt = tile + NW;
+    if (nxt < tile_end) {
+      if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
+      issue(nxt, k_it + 1, kA, vA);
+    }
+    compute(tile, kB, vB);
+    tile = nxt;
+    ++k_it;
+  }
+
+  // ---- wave totals, then the NW-wave merge through LDS --------------------
+  float lt = l;
+  lt += __shfl_xor(lt, 16);
+  lt += __shfl_xor(lt, 32);
+  if (col < G) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[w][col][VH * (4 * quad + i) + e] = acc[e][i];
+    }
+    if (quad == 0) {
+      s_m[w][col] = m;
+      s_l[w][col] = lt;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float mx = s_m[0][h];
+#pragma unroll
+    for (int k = 1; k < NW; ++k) mx = fmaxf(mx, s_m[k][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float wgt = fast_exp2(s_m[k][h] - mx);
+      L = fmaf(s_l[k][h], wgt, L);
+      O = fmaf(s_acc[k][h][d], wgt, O);
+    }
+    const float o = L > 0.f ? O / L : 0.f;
+    const size_t row = (size_t)s * Hq + g * G + h;
+    if (a.single) {
+      a.out[row * D + d] = o;
+    } else {
+      const size_t prow = row * a.num_parts + p;
+      a.ws_o[prow * D + d] = o;
+      if (d == 0) {
+        a.ws_m[prow] = mx;
+        a.ws_l[prow] = L;
+      }
+    }
+  }
+}
+
+template <int D, int BS, int G, int NW>
+int launch_one(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+template <int D, int BS, int NW>
+int by_group(const DecodeArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 2: return launch_one<D, BS, 2, NW>(a, stream);
+    case 4: return launch_one<D, BS, 4, NW>(a, stream);
+    case 8: return launch_one<D, BS, 8, NW>(a, stream);
+  }
+  return 1;
+}
+
+template <int D, int NW>
+int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream) {
+  switch (block_size) {
+    case 8: return by_group<D, 8, NW>(a, group, stream);
+    case 16: return by_group<D, 16, NW>(a, group, stream);
+    case 32: return by_group<D, 32, NW>(a, group, stream);
+  }
+  return 1;
+}
+
+}  // namespace
+
+int launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
+                       int waves, hipStream_t stream) {
+  if (dtype != 1 || waves != 4) return 1;
+  if (head_dim == 64) return by_block<64, 4>(a, block_size, group, stream);
+  if (head_dim == 128) return by_block<128, 4>(a, block_size, group, stream);
+  return 1;
+}
+
 }  // namespace pa

@@ -30,7 +30,7 @@ def ref_decode(x):
                              x.context_lens.numpy(), x.scale)
 
 
-MFMA_BUILT = False
+MFMA_BUILT = True
 
 
 def kernels_for(x):

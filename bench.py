@@ -180,22 +180,28 @@ class Step:
         ws = pa.decode_workspace_size(S, Hq, Hkv, D, bs, self.mb, self.mb * bs, partition,
                                       pa.F32 if w["dtype"] == "f32" else pa.F16, kernel)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.d_slots = torch.empty(S, dtype=torch.int64, device=dev)
-        self.d_pairs = torch.empty((S, 2), dtype=torch.int32, device=dev)
-        self.d_tables = torch.empty((S, self.mb), dtype=torch.int32, device=dev)
-        self.d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+        # one packed host->device transfer per step: slots | pairs | lens | tables
+        self.n_i32 = 2 * S + 2 * S + S + S * self.mb
+        self.d_pack = torch.empty(self.n_i32, dtype=torch.int32, device=dev)
+        self.d_slots, self.d_pairs, self.d_lens, self.d_tables = self._views(self.d_pack)
         self.bufs = []
         for _ in range(2):
-            self.bufs.append(dict(
-                slots=torch.empty(S, dtype=torch.int64).pin_memory(),
-                pairs=torch.empty((S, 2), dtype=torch.int32).pin_memory(),
-                tables=torch.empty((S, self.mb), dtype=torch.int32).pin_memory(),
-                lens=torch.empty(S, dtype=torch.int32).pin_memory(),
-                event=torch.cuda.Event()))
+            h = torch.empty(self.n_i32, dtype=torch.int32).pin_memory()
+            slots, pairs, lens, tables = self._views(h)
+            self.bufs.append(dict(pack=h, slots=slots, pairs=pairs, lens=lens, tables=tables,
+                                  event=torch.cuda.Event()))
         self.k = 0
         self.kv_bytes = []       # algorithmic decode bytes per step
         self.ctx_tokens = []
         self.ncow = []
+
+    def _views(self, flat):
+        S, mb = self.S, self.mb
+        slots = flat[0:2 * S].view(self.torch.int64)
+        pairs = flat[2 * S:4 * S].view(S, 2)
+        lens = flat[4 * S:5 * S]
+        tables = flat[5 * S:5 * S + S * mb].view(S, mb)
+        return slots, pairs, lens, tables
 
     def run(self, timed_events=None):
         torch, pa = self.torch, self.pa
@@ -216,11 +222,7 @@ class Step:
         ncow = self.bm.append_slots_into(self.seqs, buf["slots"], buf["pairs"])
         self.bm.block_tables_into(self.seqs, buf["tables"], buf["lens"])
         maxlen = int(buf["lens"].max())
-        self.d_slots.copy_(buf["slots"], non_blocking=True)
-        self.d_tables.copy_(buf["tables"], non_blocking=True)
-        self.d_lens.copy_(buf["lens"], non_blocking=True)
-        if ncow:
-            self.d_pairs[:ncow].copy_(buf["pairs"][:ncow], non_blocking=True)
+        self.d_pack.copy_(buf["pack"], non_blocking=True)
         buf["event"].record()
         pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
                        cow_pairs=self.d_pairs[:ncow] if ncow else None)

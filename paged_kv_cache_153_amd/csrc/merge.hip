@@ -8,20 +8,28 @@
 //   M = max_p m_p,  w_p = l_p * exp2(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
 // Partitions at or past ceil(n / P) were never written and are not read.
 //
-// One wave per (sequence, query head); lane j owns dims j, j+64, ...  The
-// partition weights are computed once per wave: lane p reads (m_p, l_p) for
-// p < 64 at a time and the wave reduces the max, then broadcasts each weight
-// with readlane while all lanes stream o_p.
+// One 256-thread workgroup per (sequence, query head).  D/4 threads cover
+// one partition row with float4 loads (a 512-byte coalesced row at D = 128);
+// the 256 / (D/4) thread groups take partitions round robin, so every thread
+// has several independent loads in flight, and the groups' partial sums are
+// combined through LDS.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace pa {
 namespace {
 
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
-  constexpr int DPL = D / 64;  // dims per lane
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
+  constexpr int TPR = D / 4;                  // threads per partition row
+  constexpr int NG = kMergeThreads / TPR;     // partition groups
+  __shared__ float s_red[NG][D];
+  __shared__ float s_w[NG];
+  __shared__ float s_max[kMergeThreads / 64];
+
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;  // s * Hq + h
   const int s = row / a.num_q_heads;
   int n = a.cl[s];
@@ -31,37 +39,44 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a) {
   np = min(np, a.num_parts);
   float* out = a.out + (size_t)row * D;
   if (np == 0) {
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = 0.f;
+    for (int d = tid; d < D; d += kMergeThreads) out[d] = 0.f;
     return;
   }
   const size_t prow = (size_t)row * a.num_parts;
-  // pass 1: global max over the live partitions
+
+  // global max over the live partitions
   float mx = kMaxInit;
-  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, a.ws_m[prow + p]);
+  for (int p = tid; p < np; p += kMergeThreads) mx = fmaxf(mx, a.ws_m[prow + p]);
   mx = cross_rows_max<1>(mx);
-  // pass 2: weights and weighted sum
-  float acc[DPL];
+  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
+  __syncthreads();
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+  for (int k = 0; k < kMergeThreads / 64; ++k) mx = fmaxf(mx, s_max[k]);
+
+  // weighted sum of the partition outputs
+  const int grp = tid / TPR;
+  const int c4 = (tid % TPR) * 4;
+  float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const int p = p0 + lane;
-    float wl = 0.f;
-    if (p < np) wl = a.ws_l[prow + p] * fast_exp2(a.ws_m[prow + p] - mx);
-    wsum += wl;
-    const int cnt = min(64, np - p0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __builtin_bit_cast(float, readlane(__builtin_bit_cast(int, wl), j));
-      const float* o = a.ws_o + (prow + p0 + j) * D;
-#pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wj, o[lane + 64 * k], acc[k]);
-    }
+  for (int p = grp; p < np; p += NG) {
+    const float w = a.ws_l[prow + p] * fast_exp2(a.ws_m[prow + p] - mx);
+    const float4_t o = *reinterpret_cast<const float4_t*>(a.ws_o + (prow + p) * D + c4);
+    acc += w * o;
+    wsum += w;
   }
-  wsum = cross_rows_sum<1>(wsum);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-  for (int k = 0; k < DPL; ++k) out[lane + 64 * k] = acc[k] * inv;
+  for (int j = 0; j < 4; ++j) s_red[grp][c4 + j] = acc[j];
+  if (tid % TPR == 0) s_w[grp] = wsum;
+  __syncthreads();
+  for (int d = tid; d < D; d += kMergeThreads) {
+    float o = 0.f, wt = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+      o += s_red[k][d];
+      wt += s_w[k];
+    }
+    out[d] = wt > 0.f ? o / wt : 0.f;
+  }
 }
 
 }  // namespace
@@ -70,9 +85,9 @@ int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * a.num_q_heads;
   if (grid == 0) return 0;
   if (head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else
     return 1;
   return hipGetLastError() == hipSuccess ? 0 : 2;

@@ -31,15 +31,28 @@ bool check_mode() {
   return on;
 }
 
-// Partition size used when the caller passes 0.  Single pass keeps one
-// workgroup per (sequence, KV head); it is chosen only when that already
-// gives several workgroups per compute unit and contexts are short enough
-// that per-workgroup imbalance stays small.
+// Partition size used when the caller passes 0 (measured on MI355X with
+// 16 KiB-per-token MHA and 4 KiB-per-token GQA layers at block 16):
+//  * single pass when one workgroup per (sequence, KV head) already fills the
+//    chip (>= 1024 pairs) and contexts are moderate: no merge traffic;
+//  * otherwise 512-token partitions, or 2048 for contexts beyond 16K, where
+//    fewer, longer workgroups cut the per-workgroup start-up and the merge
+//    traffic while still giving >= 8 workgroups per compute unit.
 int choose_partition(int num_seqs, int num_kv_heads, int max_context_len) {
   const long pairs = (long)num_seqs * num_kv_heads;
   if (max_context_len <= 512) return -1;
   if (pairs >= 1024 && max_context_len <= 8192) return -1;
+  if (max_context_len > 16384 && pairs * (max_context_len / 2048) >= 2048) return 2048;
   return 512;
+}
+
+// Kernel family used when the caller passes PA_KERNEL_AUTO: the matrix-core
+// kernel once q.K^T is a real [G x D] x [D x 16] product per tile with G >= 8
+// (the vector kernel spends more VALU time than it has at G = 8); at G = 4
+// the two run within a few percent of each other and the vector kernel,
+// which wastes no padded MFMA rows, is kept.
+int choose_kernel(int dtype, int group) {
+  return (dtype == PA_F16 && group >= 8) ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
 }
 
 struct Plan {
@@ -256,7 +269,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   a.scale_log2 = scale * 1.4426950408889634f;
 
   int use = kernel;
-  if (use == PA_KERNEL_AUTO) use = PA_KERNEL_VALU;
+  if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);
   int rc = use == PA_KERNEL_MFMA
                ? pa::launch_decode_mfma(a, dtype, head_dim, block_size, group, 4, stream)
                : pa::launch_decode_valu(a, dtype, head_dim, block_size, group, 4, stream);

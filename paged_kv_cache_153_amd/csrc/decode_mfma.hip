@@ -27,6 +27,7 @@
 //  * The running max per head needs one max across the four lane groups
 //    (two butterfly steps); everything else stays in the lane.
 #include "device_common.h"
+#include "decode_epilogue.h"
 #include "kernels.h"
 
 namespace pa {
@@ -63,9 +64,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   using VR = VRow<D>;
   using vrow_t = typename VR::type;
 
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
+  __shared__ DecodeSmem<G, D, NW> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -82,12 +81,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   int n = a.cl[s];
   n = n < 0 ? 0 : n;
   n = min(n, a.max_tokens);
+  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
   const int t_begin = p * a.part_tokens;
   if (t_begin >= n) {
-    if (a.single) {
-      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
-        a.out[((size_t)s * Hq + g * G) * D + idx] = 0.f;
-    }
+    if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
     return;
   }
   const int t_end = min(n, t_begin + a.part_tokens);
@@ -246,40 +243,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[w][col][VH * (4 * quad + i) + e] = acc[e][i];
+      for (int i = 0; i < 4; ++i) sm.acc[w][col][VH * (4 * quad + i) + e] = acc[e][i];
     }
     if (quad == 0) {
-      s_m[w][col] = m;
-      s_l[w][col] = lt;
+      sm.m[w][col] = m;
+      sm.l[w][col] = lt;
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float mx = s_m[0][h];
-#pragma unroll
-    for (int k = 1; k < NW; ++k) mx = fmaxf(mx, s_m[k][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float wgt = fast_exp2(s_m[k][h] - mx);
-      L = fmaf(s_l[k][h], wgt, L);
-      O = fmaf(s_acc[k][h][d], wgt, O);
-    }
-    const float o = L > 0.f ? O / L : 0.f;
-    const size_t row = (size_t)s * Hq + g * G + h;
-    if (a.single) {
-      a.out[row * D + d] = o;
-    } else {
-      const size_t prow = row * a.num_parts + p;
-      a.ws_o[prow * D + d] = o;
-      if (d == 0) {
-        a.ws_m[prow] = mx;
-        a.ws_l[prow] = L;
-      }
-    }
-  }
+  finish_workgroup<G, D, NW>(a, sm, s, g, p, (n + a.part_tokens - 1) / a.part_tokens);
 }
 
 template <int D, int BS, int G, int NW>

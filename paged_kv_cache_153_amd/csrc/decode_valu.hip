@@ -33,6 +33,7 @@
 //    kernel never reads outside the pool and never lets unused rows — even
 //    NaN ones — reach the output.
 #include "device_common.h"
+#include "decode_epilogue.h"
 #include "kernels.h"
 
 namespace pa {
@@ -49,9 +50,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "unsupported row width");
   static_assert(RPI <= BS, "a load instruction must stay inside one block");
 
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
+  __shared__ DecodeSmem<G, D, NW> sm;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -68,12 +67,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   int n = a.cl[s];
   n = n < 0 ? 0 : n;
   n = min(n, a.max_tokens);
+  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
   const int t_begin = p * a.part_tokens;
   if (t_begin >= n) {
-    if (a.single) {
-      for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
-        a.out[((size_t)s * Hq + g * G) * D + idx] = 0.f;
-    }
+    if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
     return;
   }
   const int t_end = min(n, t_begin + a.part_tokens);
@@ -250,42 +247,15 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[w][h][c * EPL + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) sm.acc[w][h][c * EPL + e] = acc[h][e];
       if (c == 0) {
-        s_m[w][h] = m[h];
-        s_l[w][h] = l[h];
+        sm.m[w][h] = m[h];
+        sm.l[w][h] = l[h];
       }
     }
   }
   __syncthreads();
-
-  // ---- merge the NW waves and write ---------------------------------------
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float mx = s_m[0][h];
-#pragma unroll
-    for (int k = 1; k < NW; ++k) mx = fmaxf(mx, s_m[k][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float wgt = fast_exp2(s_m[k][h] - mx);
-      L = fmaf(s_l[k][h], wgt, L);
-      O = fmaf(s_acc[k][h][d], wgt, O);
-    }
-    const float o = L > 0.f ? O / L : 0.f;
-    const size_t row = (size_t)s * Hq + g * G + h;
-    if (a.single) {
-      a.out[row * D + d] = o;
-    } else {
-      const size_t prow = row * a.num_parts + p;
-      a.ws_o[prow * D + d] = o;
-      if (d == 0) {
-        a.ws_m[prow] = mx;
-        a.ws_l[prow] = L;
-      }
-    }
-  }
+  finish_workgroup<G, D, NW>(a, sm, s, g, p, (n + a.part_tokens - 1) / a.part_tokens);
 }
 
 template <typename T, int D, int BS, int G, int NW>

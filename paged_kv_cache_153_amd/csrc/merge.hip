@@ -6,7 +6,8 @@
 // same algebra across partitions: with partition max m_p (log2 units), sum
 // l_p and normalised output o_p,
 //   M = max_p m_p,  w_p = l_p * exp2(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
-// Partitions at or past ceil(n / P) were never written and are not read.
+// Partitions at or past ceil(n / P) were never written and are not read; a
+// sequence that fits one partition was finished by the decode kernel itself.
 //
 // One 256-thread workgroup per (sequence, query head).  D/4 threads cover
 // one partition row with float4 loads (a 512-byte coalesced row at D = 128);
@@ -38,10 +39,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   int np = (n + a.part_tokens - 1) / a.part_tokens;
   np = min(np, a.num_parts);
   float* out = a.out + (size_t)row * D;
-  if (np == 0) {
-    for (int d = tid; d < D; d += kMergeThreads) out[d] = 0.f;
-    return;
-  }
+  // 0 partitions: the decode kernel wrote zeros; 1: it wrote the output
+  if (np <= 1) return;
   const size_t prow = (size_t)row * a.num_parts;
 
   // global max over the live partitions

@@ -35,24 +35,23 @@ bool check_mode() {
 // 16 KiB-per-token MHA and 4 KiB-per-token GQA layers at block 16):
 //  * single pass when one workgroup per (sequence, KV head) already fills the
 //    chip (>= 1024 pairs) and contexts are moderate: no merge traffic;
-//  * otherwise 512-token partitions, or 2048 for contexts beyond 16K, where
-//    fewer, longer workgroups cut the per-workgroup start-up and the merge
-//    traffic while still giving >= 8 workgroups per compute unit.
+//  * otherwise 1024-token partitions, or 2048 beyond 16K tokens: fewer,
+//    longer workgroups cut the per-workgroup start-up and the merge traffic
+//    while still leaving several workgroups per compute unit.
 int choose_partition(int num_seqs, int num_kv_heads, int max_context_len) {
   const long pairs = (long)num_seqs * num_kv_heads;
-  if (max_context_len <= 512) return -1;
+  if (max_context_len <= 1024) return -1;
   if (pairs >= 1024 && max_context_len <= 8192) return -1;
-  if (max_context_len > 16384 && pairs * (max_context_len / 2048) >= 2048) return 2048;
-  return 512;
+  if (max_context_len > 16384) return 2048;
+  return 1024;
 }
 
 // Kernel family used when the caller passes PA_KERNEL_AUTO: the matrix-core
-// kernel once q.K^T is a real [G x D] x [D x 16] product per tile with G >= 8
-// (the vector kernel spends more VALU time than it has at G = 8); at G = 4
-// the two run within a few percent of each other and the vector kernel,
-// which wastes no padded MFMA rows, is kept.
+// kernel once the query group makes q.K^T a real [G x D] x [D x 16] product
+// (G >= 4 measured faster: its VALU work per tile does not grow with G); the
+// vector kernel for MHA / G = 2, where MFMA rows would be mostly padding.
 int choose_kernel(int dtype, int group) {
-  return (dtype == PA_F16 && group >= 8) ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+  return (dtype == PA_F16 && group >= 4) ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
 }
 
 struct Plan {
@@ -62,6 +61,7 @@ struct Plan {
   size_t ws_bytes = 0;
   size_t off_m = 0, off_l = 0;
 };
+
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

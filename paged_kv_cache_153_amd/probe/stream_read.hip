@@ -1,0 +1,71 @@
+// stream_read.hip — HBM read-bandwidth probes used as the measured ceiling
+// that decode bandwidth is compared with.  Built into libpa_probe.so, apart
+// from libpa.so; not part of the attention library.
+//
+//  * pa_probe_read_linear: a grid-stride read of a buffer, 16 bytes per lane.
+//  * pa_probe_read_tiles: reads 4 KiB tiles in the order given by a device
+//    index array — the access pattern of a paged K or V tile at block 16,
+//    head_dim 128, fp16.
+// Both fold what they read into one value that is stored only if it matches
+// an impossible constant, so the loads cannot be optimised away and nothing
+// is written in practice.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void read_linear(const u4* __restrict__ p, size_t n16,
+                                                   uint32_t* out) {
+  uint32_t acc = 0;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const u4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+// blockDim 256 = one 4 KiB tile per load instruction; 8 tiles in flight
+__global__ __launch_bounds__(256) void read_tiles(const u4* __restrict__ p,
+                                                  const int32_t* __restrict__ idx, int per_wg,
+                                                  int64_t num_tiles, uint32_t* out) {
+  uint32_t acc = 0;
+  const int32_t* my = idx + (size_t)blockIdx.x * per_wg;
+  for (int t = 0; t < per_wg; t += 8) {
+    u4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      int64_t tile = t + u < per_wg ? my[t + u] : 0;
+      tile = tile < 0 || tile >= num_tiles ? 0 : tile;
+      v[u] = p[tile * 256 + threadIdx.x];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16) from `buf` with `workgroups` x 256 threads.
+int pa_probe_read_linear(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
+                         void* stream) {
+  if (!buf || !sink || bytes % 16 || workgroups <= 0) return -1;
+  hipLaunchKernelGGL(read_linear, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                     (const u4*)buf, bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// Reads the 4 KiB tiles of `buf` listed in `tiles` ([num_listed] int32 on the
+// device, each in [0, num_tiles)), `per_wg` consecutive entries per workgroup.
+int pa_probe_read_tiles(const void* buf, int64_t num_tiles, const int32_t* tiles,
+                        int64_t num_listed, int per_wg, uint32_t* sink, void* stream) {
+  if (!buf || !tiles || !sink || per_wg <= 0 || num_listed % per_wg) return -1;
+  const int64_t wgs = num_listed / per_wg;
+  if (wgs <= 0 || wgs > INT32_MAX) return -1;
+  hipLaunchKernelGGL(read_tiles, dim3((unsigned)wgs), dim3(256), 0, (hipStream_t)stream,
+                     (const u4*)buf, tiles, per_wg, num_tiles, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

@@ -101,7 +101,7 @@ def measured_traffic(workload):
 class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
-    def __init__(self, name, bs, seed, steps_total, kernel, partition, device):
+    def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -121,6 +121,8 @@ class Step:
             self.prefix = 512
             suffix = torch.randint(1, 2049, (S - 1,), generator=g_cpu).tolist()
             lens0 = [self.prefix + n for n in suffix]           # sequences 0..S-2
+        elif context:
+            lens0 = [context] * S
         elif isinstance(w["ctx"], tuple):
             lens0 = synth.gqa_lengths(S, w["ctx"][0], w["ctx"][1], seed)
         elif isinstance(w["ctx"], list):
@@ -203,10 +205,9 @@ class Step:
         tables = flat[5 * S:5 * S + S * mb].view(S, mb)
         return slots, pairs, lens, tables
 
-    def run(self, timed_events=None):
-        torch, pa = self.torch, self.pa
-        buf = self.bufs[self.k % 2]
-        buf["event"].synchronize()          # its previous copies have left pinned memory
+    def host_step(self, buf):
+        """Block-manager part of a step: fork/COW bookkeeping, slots, tables."""
+        pa = self.pa
         if self.name == "shared_prefix":
             child = self.fork_child
             try:
@@ -214,13 +215,24 @@ class Step:
             except pa.PAError:
                 pass
             while True:
-                parent = int(torch.randint(0, self.S - 1, (1,), generator=self.rng))
+                parent = int(self.torch.randint(0, self.S - 1, (1,), generator=self.rng))
                 _, n = self.bm.block_table(parent)
                 if n % self.bs:
                     break
             self.bm.fork(parent, child)
         ncow = self.bm.append_slots_into(self.seqs, buf["slots"], buf["pairs"])
         self.bm.block_tables_into(self.seqs, buf["tables"], buf["lens"])
+        tokens = int(buf["lens"].sum())
+        self.ctx_tokens.append(tokens)
+        self.kv_bytes.append(tokens * 2 * self.Hkv * self.D * self.elem)
+        self.ncow.append(ncow)
+        return ncow
+
+    def run(self, timed_events=None):
+        torch, pa = self.torch, self.pa
+        buf = self.bufs[self.k % 2]
+        buf["event"].synchronize()          # its previous copies have left pinned memory
+        ncow = self.host_step(buf)
         maxlen = int(buf["lens"].max())
         self.d_pack.copy_(buf["pack"], non_blocking=True)
         buf["event"].record()
@@ -233,10 +245,6 @@ class Step:
                   out=self.out, workspace=self.ws)
         if timed_events is not None:
             timed_events[1].record()
-        tokens = int(buf["lens"].sum())
-        self.ctx_tokens.append(tokens)
-        self.kv_bytes.append(tokens * 2 * self.Hkv * self.D * self.elem)
-        self.ncow.append(ncow)
         self.k += 1
         return buf
 
@@ -370,6 +378,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--context", type=int, default=0,
+                    help="override: every sequence at this context length (not shared_prefix)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured HBM read ceiling (libpa_probe.so)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -392,10 +402,11 @@ def main():
         print(json.dumps(calibrate_copy(dev)), flush=True)
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
-              args.partition, dev)
+              args.partition, dev, context=args.context)
+    step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        st.run()
+        step_fn()
     torch.cuda.synchronize()
     st.kv_bytes.clear()
     st.ctx_tokens.clear()
@@ -406,7 +417,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        st.run(ev[i])
+        step_fn(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in ev]
@@ -442,6 +453,7 @@ def main():
             "block_size": st.bs, "pool_blocks": st.num_blocks,
             "mean_context": round(total_tokens / args.steps / st.S, 1),
             "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
+            "context_override": args.context or None,
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),

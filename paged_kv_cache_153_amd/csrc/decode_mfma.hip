@@ -52,8 +52,11 @@ struct VRow<64> {
   static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
 };
 
-template <int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+// DEPTH 2: the next tile's loads are issued before the current tile is
+// computed (register double buffer, 2 waves per SIMD).  DEPTH 1: one tile
+// per wave in flight and twice the waves per SIMD to hide the latency.
+template <int D, int BS, int G, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int KS = D / 32;                 // 16x16x32 steps for q.K
@@ -61,8 +64,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NE = VH;                     // P.V blocks of 16 output rows
   constexpr int BPT = BS >= kTile ? 1 : kTile / BS;
   static_assert(BPT <= 2, "a tile spans at most two blocks");
-  using VR = VRow<D>;
-  using vrow_t = typename VR::type;
+  using vrow_t = typename VRow<D>::type;
 
   __shared__ DecodeSmem<G, D, NW> sm;
 
@@ -117,7 +119,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     for (int jj = 0; jj < BPT; ++jj) {
       const int lb = BS >= kTile ? tile * kTile / BS : tile * BPT + jj;
       int v = 0;
-      if (tile < tile_end && lb < a.max_blocks) {
+      // bounded by the table width only, so this load does not wait for
+      // the context length; ids of tiles past the context are never used
+      if (lb < a.max_blocks) {
         v = bt_row[lb];
         if (v < 0 || v >= a.num_blocks) v = 0;
       }
@@ -141,19 +145,39 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int jj = 0; jj < BPT; ++jj) blk[jj] = readlane(ids[jj], sel);
     const int row0 = BS > kTile ? (tile % (BS / kTile)) * kTile : 0;
-    {  // K: token `col` of the tile
-      const int b = BPT == 1 ? blk[0] : blk[BPT - 1 < 1 ? 0 : (col >= BS ? 1 : 0)];
-      const int row = BS >= kTile ? row0 + col : col % BS;
-      const half_t* base = kvh + (size_t)b * block_stride + row * D;
+    if constexpr (BPT == 1) {
+      // one block: wave-uniform base, per-lane unsigned offsets
+      const half_t* kb = kvh + (size_t)blk[0] * block_stride;
+      const half_t* vb = kb + v_offset;
+      const uint32_t krow = (uint32_t)(row0 + col) * (D * 2);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) kr[j] = load16(base + (4 * j + quad) * 8);
-    }
+      for (int j = 0; j < KS; ++j) kr[j] = load16_at(kb, krow + (4 * j + quad) * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // V: row 4*quad + i, chunk col
-      const int t = 4 * quad + i;
-      const int b = BPT == 1 ? blk[0] : blk[BPT - 1 < 1 ? 0 : (t >= BS ? 1 : 0)];
-      const int row = BS >= kTile ? row0 + t : t % BS;
-      vr[i] = VR::load(kvh + (size_t)b * block_stride + v_offset + row * D + col * VH);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)(row0 + 4 * quad + i) * (D * 2) + col * (VH * 2);
+        if constexpr (D == 128)
+          vr[i] = load16_at(vb, off);
+        else
+          vr[i] = load8_at(vb, off);
+      }
+    } else {
+      // a tile spans two 8-row blocks: lanes pick their block
+      const int bk = col >= BS ? blk[BPT - 1] : blk[0];
+      const half_t* kb = kvh + (size_t)bk * block_stride;
+      const uint32_t krow = (uint32_t)(col % BS) * (D * 2);
+#pragma unroll
+      for (int j = 0; j < KS; ++j) kr[j] = load16_at(kb, krow + (4 * j + quad) * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * quad + i;
+        const half_t* vb = kvh + (size_t)(t >= BS ? blk[BPT - 1] : blk[0]) * block_stride +
+                           v_offset;
+        const uint32_t off = (uint32_t)(t % BS) * (D * 2) + col * (VH * 2);
+        if constexpr (D == 128)
+          vr[i] = load16_at(vb, off);
+        else
+          vr[i] = load8_at(vb, off);
+      }
     }
   };
 
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         if (tile * kTile + 4 * quad + i >= n) {
           y[i] = -INFINITY;
-          vr[i] = VR::zero();
+          vr[i] = VRow<D>::zero();
         }
       }
     }
@@ -195,8 +219,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
         half4_t, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
     const half4_t plo = __builtin_bit_cast(
         half4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+    // rescale only when some head's running max moved (alpha == 1 otherwise)
+    if (wave_any(alpha != 1.f)) {
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+    }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       // A operand: tokens 4*quad .. 4*quad+3 of dim (chunk col, half e)
@@ -214,25 +241,33 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   int tile = tile_begin + w;
   int k_it = 0;
   load_ids(0);
-  if (tile < tile_end) issue(tile, 0, kA, vA);
-  while (tile < tile_end) {
-    int nxt = tile + NW;
-    if (nxt < tile_end) {
-      if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-      issue(nxt, k_it + 1, kB, vB);
+  if constexpr (DEPTH == 1) {
+    for (; tile < tile_end; tile += NW, ++k_it) {
+      if (k_it > 0 && (k_it & 63) == 0) load_ids(k_it);
+      issue(tile, k_it, kA, vA);
+      compute(tile, kA, vA);
     }
-    compute(tile, kA, vA);
-    tile = nxt;
-    ++k_it;
-    if (tile >= tile_end) break;
-    nxt = tile + NW;
-    if (nxt < tile_end) {
-      if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-      issue(nxt, k_it + 1, kA, vA);
+  } else {
+    if (tile < tile_end) issue(tile, 0, kA, vA);
+    while (tile < tile_end) {
+      int nxt = tile + NW;
+      if (nxt < tile_end) {
+        if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
+        issue(nxt, k_it + 1, kB, vB);
+      }
+      compute(tile, kA, vA);
+      tile = nxt;
+      ++k_it;
+      if (tile >= tile_end) break;
+      nxt = tile + NW;
+      if (nxt < tile_end) {
+        if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
+        issue(nxt, k_it + 1, kA, vA);
+      }
+      compute(tile, kB, vB);
+      tile = nxt;
+      ++k_it;
     }
-    compute(tile, kB, vB);
-    tile = nxt;
-    ++k_it;
   }
 
   // ---- wave totals, then the NW-wave merge through LDS --------------------
@@ -258,7 +293,12 @@ template <int D, int BS, int G, int NW>
 int launch_one(const DecodeArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW>), dim3(grid), dim3(NW * 64), 0, stream, a);
+  if (a.variant == 1)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

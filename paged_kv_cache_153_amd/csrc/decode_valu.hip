@@ -97,7 +97,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     for (int jj = 0; jj < BPT; ++jj) {
       const int lb = BS >= kTile ? tile * kTile / BS : tile * BPT + jj;
       int v = 0;
-      if (tile < tile_end && lb < a.max_blocks) {
+      // bounded by the table width only, so this load does not wait for
+      // the context length; ids of tiles past the context are never used
+      if (lb < a.max_blocks) {
         v = bt_row[lb];
         if (v < 0 || v >= a.num_blocks) v = 0;
       }
@@ -128,10 +130,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     for (int i = 0; i < NI; ++i) {
       const int jj = BS >= kTile ? 0 : (i * RPI) / BS;
       const int row = BS >= kTile ? row0 + i * RPI + r : (i * RPI) % BS + r;
-      const T* base = kvh + (size_t)blk[jj] * block_stride;
-      const int off = row * D + c * EPL;
-      kr[i] = load16(base + off);
-      vr[i] = load16(base + v_offset + off);
+      const T* base = kvh + (size_t)blk[jj] * block_stride;   // wave-uniform
+      const uint32_t off = (uint32_t)(row * D + c * EPL) * (uint32_t)sizeof(T);
+      kr[i] = load16_at(base, off);
+      vr[i] = load16_at(base + v_offset, off);
     }
   };
 
@@ -189,8 +191,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
         ps += pv[i];
       }
       l[h] = fmaf(l[h], alpha, ps);
+      if (wave_any(alpha != 1.f)) {  // the row's running max moved
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if constexpr (E == 2) {

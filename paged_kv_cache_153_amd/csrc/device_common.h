@@ -81,9 +81,23 @@ __device__ __forceinline__ int readlane(int x, int lane) {
   return __builtin_amdgcn_readlane(x, lane);
 }
 
-// 16-byte global load that bypasses nothing: plain global_load_dwordx4.
+// 16-byte global load: plain global_load_dwordx4.
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Loads at a wave-uniform base plus a per-lane unsigned 32-bit byte offset,
+// the shape the SGPR-base (saddr) form of global loads encodes directly.
+__device__ __forceinline__ u32x4_t load16_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ __forceinline__ u32x2_t load8_at(const void* base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+// True when any lane of the wave has `pred` set (wave-uniform).
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
 template <typename T>

@@ -31,6 +31,7 @@ struct DecodeArgs {
   int part_tokens;          // P (multiple of kTile and of BS); huge when single
   int single;               // 1: write `out` directly; 0: write ws_*
   float scale_log2;         // scale * log2(e)
+  int variant;              // MFMA: 1 = one tile in flight per wave, 0 = two
 };
 
 // Each returns 0 on success, 1 if the (dtype, D, BS, G) combination has no

@@ -11,9 +11,11 @@
 //
 // One 256-thread workgroup per (sequence, query head).  D/4 threads cover
 // one partition row with float4 loads (a 512-byte coalesced row at D = 128);
-// the 256 / (D/4) thread groups take partitions round robin, so every thread
-// has several independent loads in flight, and the groups' partial sums are
-// combined through LDS.
+// the 256 / (D/4) thread groups take partitions round robin and each keeps
+// a running (max, sum, weighted row) over its partitions, so every load a
+// thread needs — m_p, l_p and its slice of o_p — is issued at once and the
+// only dependent round trip is the context length.  The groups' states are
+// combined through LDS with the same rescaling.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,9 +28,9 @@ template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   constexpr int TPR = D / 4;                  // threads per partition row
   constexpr int NG = kMergeThreads / TPR;     // partition groups
-  __shared__ float s_red[NG][D];
-  __shared__ float s_w[NG];
-  __shared__ float s_max[kMergeThreads / 64];
+  __shared__ float s_o[NG][D];
+  __shared__ float s_m[NG];
+  __shared__ float s_l[NG];
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x;  // s * Hq + h
@@ -36,43 +38,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   int n = a.cl[s];
   n = n < 0 ? 0 : n;
   n = min(n, a.max_tokens);
-  int np = (n + a.part_tokens - 1) / a.part_tokens;
-  np = min(np, a.num_parts);
-  float* out = a.out + (size_t)row * D;
+  n = min(n, a.num_parts * a.part_tokens);
+  const int np = (n + a.part_tokens - 1) / a.part_tokens;
   // 0 partitions: the decode kernel wrote zeros; 1: it wrote the output
   if (np <= 1) return;
   const size_t prow = (size_t)row * a.num_parts;
 
-  // global max over the live partitions
-  float mx = kMaxInit;
-  for (int p = tid; p < np; p += kMergeThreads) mx = fmaxf(mx, a.ws_m[prow + p]);
-  mx = cross_rows_max<1>(mx);
-  if ((tid & 63) == 0) s_max[tid >> 6] = mx;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < kMergeThreads / 64; ++k) mx = fmaxf(mx, s_max[k]);
-
-  // weighted sum of the partition outputs
   const int grp = tid / TPR;
   const int c4 = (tid % TPR) * 4;
+  float mx = kMaxInit, lsum = 0.f;
   float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   for (int p = grp; p < np; p += NG) {
-    const float w = a.ws_l[prow + p] * fast_exp2(a.ws_m[prow + p] - mx);
+    const float mp = a.ws_m[prow + p];
+    const float lp = a.ws_l[prow + p];
     const float4_t o = *reinterpret_cast<const float4_t*>(a.ws_o + (prow + p) * D + c4);
-    acc += w * o;
-    wsum += w;
+    const float m_new = fmaxf(mx, mp);
+    const float keep = fast_exp2(mx - m_new);
+    const float w = lp * fast_exp2(mp - m_new);
+    lsum = fmaf(lsum, keep, w);
+    acc = acc * keep + w * o;
+    mx = m_new;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) s_red[grp][c4 + j] = acc[j];
-  if (tid % TPR == 0) s_w[grp] = wsum;
+  for (int j = 0; j < 4; ++j) s_o[grp][c4 + j] = acc[j];
+  if (tid % TPR == 0) {
+    s_m[grp] = mx;
+    s_l[grp] = lsum;
+  }
   __syncthreads();
+  float* out = a.out + (size_t)row * D;
   for (int d = tid; d < D; d += kMergeThreads) {
+    float big = s_m[0];
+#pragma unroll
+    for (int k = 1; k < NG; ++k) big = fmaxf(big, s_m[k]);
     float o = 0.f, wt = 0.f;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
-      o += s_red[k][d];
-      wt += s_w[k];
+      const float f = fast_exp2(s_m[k] - big);
+      o = fmaf(s_o[k][d], f, o);
+      wt = fmaf(s_l[k], f, wt);
     }
     out[d] = wt > 0.f ? o / wt : 0.f;
   }

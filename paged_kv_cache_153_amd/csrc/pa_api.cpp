@@ -35,15 +35,17 @@ bool check_mode() {
 // 16 KiB-per-token MHA and 4 KiB-per-token GQA layers at block 16):
 //  * single pass when one workgroup per (sequence, KV head) already fills the
 //    chip (>= 1024 pairs) and contexts are moderate: no merge traffic;
-//  * otherwise 1024-token partitions, or 2048 beyond 16K tokens: fewer,
-//    longer workgroups cut the per-workgroup start-up and the merge traffic
-//    while still leaving several workgroups per compute unit.
+//  * otherwise partitions of 512 tokens up to 4K contexts, 1024 up to 16K and
+//    2048 beyond: longer contexts take longer partitions, which cut the
+//    per-workgroup start-up and the merge traffic while still leaving several
+//    workgroups per compute unit.
 int choose_partition(int num_seqs, int num_kv_heads, int max_context_len) {
   const long pairs = (long)num_seqs * num_kv_heads;
-  if (max_context_len <= 1024) return -1;
+  if (max_context_len <= 512) return -1;
   if (pairs >= 1024 && max_context_len <= 8192) return -1;
-  if (max_context_len > 16384) return 2048;
-  return 1024;
+  if (max_context_len <= 4096) return 512;
+  if (max_context_len <= 16384) return 1024;
+  return 2048;
 }
 
 // Kernel family used when the caller passes PA_KERNEL_AUTO: the matrix-core
@@ -267,6 +269,10 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   a.part_tokens = plan.part_tokens;
   a.single = plan.single;
   a.scale_log2 = scale * 1.4426950408889634f;
+  // MFMA kernel: one tile per wave in flight at twice the occupancy for
+  // single pass (long-lived workgroups), the register double buffer for
+  // split partitions (measured faster there).
+  a.variant = plan.single ? 1 : 0;
 
   int use = kernel;
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);

@@ -110,6 +110,9 @@ class Step:
         if name == "shared_prefix":
             w["bs"] = bs
         self.w, self.name, self.kernel, self.partition = w, name, kernel, partition
+        # a pool whose prefix blocks every sequence shares is read with cached
+        # loads (the block manager knows it shares); streaming loads otherwise
+        self.cached_kv = name == "shared_prefix"
         S, Hq, Hkv, D, bs = w["S"], w["Hq"], w["Hkv"], w["D"], w["bs"]
         self.S, self.Hq, self.Hkv, self.D, self.bs = S, Hq, Hkv, D, bs
         tdt = synth.DTYPES[w["dtype"]]
@@ -242,7 +245,7 @@ class Step:
             timed_events[0].record()
         pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
                   max_context_len=maxlen, partition_size=self.partition, kernel=self.kernel,
-                  out=self.out, workspace=self.ws)
+                  out=self.out, workspace=self.ws, cached_kv=self.cached_kv)
         if timed_events is not None:
             timed_events[1].record()
         self.k += 1
@@ -297,15 +300,16 @@ def cpu_baseline(st, budget_s=10.0, cap_s=30.0):
 def stream_ceiling(dev, nbytes=4 << 30, reps=5):
     """Measured HBM read ceiling on this GPU (libpa_probe.so): a linear
     grid-stride read and a read of 4 KiB tiles in random order — the access
-    pattern of paged K/V tiles.  GB/s, best over a few launch shapes."""
+    pattern of paged K/V tiles.  GB/s, best over launch shapes and over
+    plain / non-temporal loads."""
     import ctypes
     import torch
     probe = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_153_amd", "libpa_probe.so"))
     probe.pa_probe_read_linear.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                           ctypes.c_void_p, ctypes.c_void_p]
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     probe.pa_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                          ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                                          ctypes.c_void_p]
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     buf = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     ntiles = nbytes // 4096
@@ -325,12 +329,12 @@ def stream_ceiling(dev, nbytes=4 << 30, reps=5):
         torch.cuda.synchronize()
         return nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
 
-    lin = max(timed(lambda: probe.pa_probe_read_linear(buf.data_ptr(), nbytes, w,
+    lin = max(timed(lambda: probe.pa_probe_read_linear(buf.data_ptr(), nbytes, w, nt,
                                                        sink.data_ptr(), st))
-              for w in (1024, 2048, 4096))
+              for w in (1024, 2048, 4096) for nt in (0, 1))
     til = max(timed(lambda: probe.pa_probe_read_tiles(buf.data_ptr(), ntiles, order.data_ptr(),
-                                                      ntiles, per, sink.data_ptr(), st))
-              for per in (16, 64))
+                                                      ntiles, per, nt, sink.data_ptr(), st))
+              for per in (16, 64) for nt in (0, 1))
     del buf, order
     torch.cuda.empty_cache()
     return {"linear_read_GBps": round(lin, 1), "random_4KiB_tile_read_GBps": round(til, 1)}
@@ -454,6 +458,7 @@ def main():
             "mean_context": round(total_tokens / args.steps / st.S, 1),
             "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
             "context_override": args.context or None,
+            "kv_loads": "cached" if st.cached_kv else "streaming (non-temporal)",
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),

@@ -64,6 +64,12 @@ typedef enum pa_kernel {
   PA_KERNEL_MFMA = 2  /* matrix-core q.K^T and P.V tiles (f16, GQA only)  */
 } pa_kernel;
 
+/* Flag OR-ed into pa_decode's `kernel`: read K/V with plain (cached) loads.
+ * By default K/V are streamed with non-temporal loads, since each byte is
+ * read once per call; when many sequences share blocks (a common prefix),
+ * keeping them cached lets the repeated reads hit on-chip caches. */
+#define PA_KV_CACHED 0x100
+
 /* -------------------------------------------------------------------------
  * 1. Cache write ([KVPA] §2.2 and §5.3; [KV2P] §2.1; [NANO] §2.3)
  *
@@ -114,10 +120,13 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  *   max_context_len host bound on context_lens (sizes the partition grid)
  *   scale          softmax scale, normally 1/sqrt(head_dim)
  *   partition_size 0 = choose; -1 = single pass (one workgroup per (s, KV
- *                  head)); > 0 = split each context into partitions of this
- *                  many tokens (a multiple of 16 and of block_size), combined
- *                  by a log-sum-exp merge kernel
- *   kernel         a pa_kernel value
+ *                  head)); -2 = balanced: one grid of as many workgroups as
+ *                  fit on the GPU at once, each taking an equal slice of all
+ *                  (s, KV head, 16-token tile) work, for batches of at most
+ *                  1024 sequences; > 0 = split each context into partitions
+ *                  of this many tokens (a multiple of 16 and of block_size).
+ *                  Split work is combined by a log-sum-exp merge kernel.
+ *   kernel         a pa_kernel value, optionally | PA_KV_CACHED
  *   workspace      device scratch for split partials (caller-owned), may be
  *                  NULL when *workspace_needed is 0
  *   workspace_needed  out (may be NULL): bytes this call needs.  Calling with

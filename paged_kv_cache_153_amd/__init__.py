@@ -28,6 +28,7 @@ _lib = None
 
 F32, F16 = 0, 1
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
+KV_CACHED = 0x100   # flag: plain cached K/V loads instead of streaming loads
 
 PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED", -3: "PA_ERR_WORKSPACE",
@@ -168,13 +169,16 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 
 
 def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_len=None,
-           partition_size=0, kernel="auto", out=None, workspace=None, stream=None):
+           partition_size=0, kernel="auto", out=None, workspace=None, stream=None,
+           cached_kv=False):
     """Paged decode attention.
 
     query [S, Hq, D] (kv dtype), kv_cache [NB, 2, Hkv, bs, D], block_tables
     [S, MB] int32, context_lens [S] int32, all on the GPU.  Returns ``out``
     [S, Hq, D] float32.  ``max_context_len`` is a host bound on the lengths
     (default MB * bs); ``partition_size`` 0 = auto, -1 = single pass.
+    ``cached_kv``: read K/V with cached loads (for pools whose blocks many
+    sequences share); default streams them with non-temporal loads.
     """
     torch = _torch()
     _need_cuda(query, kv_cache, block_tables, context_lens, out, workspace)
@@ -206,7 +210,8 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     _check(lib().pa_decode(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
                            block_tables.data_ptr(), context_lens.data_ptr(), s, hq, hkv, d, bs,
                            mb, int(max_context_len), nb, float(scale), int(partition_size),
-                           KERNELS[kernel], None if workspace is None else workspace.data_ptr(),
+                           KERNELS[kernel] | (KV_CACHED if cached_kv else 0),
+                           None if workspace is None else workspace.data_ptr(),
                            wbytes, None, dt, _stream(query.device, stream)))
     return out
 

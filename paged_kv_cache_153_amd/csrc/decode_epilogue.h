@@ -1,7 +1,7 @@
-// decode_epilogue.h — end of a decode workgroup, shared by the VALU and MFMA
+// decode_epilogue.h — end of a decode range, shared by the VALU and MFMA
 // kernels: merge the waves' online-softmax states, then write either the
-// output (the workgroup saw the whole sequence) or this partition's partial
-// for the log-sum-exp merge kernel.
+// output (the range was a whole sequence) or a partial (m, l, normalised o)
+// for a merge kernel.
 //
 // The merge algebra is the pages' running-max / running-sum rescaling
 // ([KVPA] "KV Cache与PagedAttention深度解析" §7.2; [NANO] zwxr.cn walkthrough
@@ -27,7 +27,22 @@ struct DecodeSmem {
   float l[NW][G];
 };
 
-// Zero output for an empty sequence (written by partition 0 only).
+// Where a range's result goes.  Head h of the group writes o[h * o_stride +
+// d]; a partial (m != nullptr) also writes m[h * ml_stride] and l[...].
+struct Sink {
+  float* o;
+  float* m;
+  float* l;
+  long o_stride;
+  long ml_stride;
+};
+
+template <int G, int D>
+__device__ __forceinline__ Sink output_sink(const DecodeArgs& a, int s, int g) {
+  return Sink{a.out + ((size_t)s * a.num_q_heads + g * G) * D, nullptr, nullptr, D, 0};
+}
+
+// Zero output for an empty sequence.
 template <int G, int D, int NW>
 __device__ __forceinline__ void write_zero_output(const DecodeArgs& a, int s, int g) {
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64)
@@ -35,12 +50,9 @@ __device__ __forceinline__ void write_zero_output(const DecodeArgs& a, int s, in
 }
 
 // All threads call this after every wave has stored its state in `sm` and a
-// barrier has made it visible.  `np` = live partitions of this sequence.
+// barrier has made it visible.
 template <int G, int D, int NW>
-__device__ void finish_workgroup(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, int s, int g,
-                                 int p, int np) {
-  const int Hq = a.num_q_heads;
-  const size_t row0 = (size_t)s * Hq + g * G;  // first query head of this group
+__device__ void finish_range(const DecodeSmem<G, D, NW>& sm, const Sink& sink) {
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int h = idx / D;
     const int d = idx % D;
@@ -54,16 +66,10 @@ __device__ void finish_workgroup(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, 
       L = fmaf(sm.l[k][h], wgt, L);
       O = fmaf(sm.acc[k][h][d], wgt, O);
     }
-    const float o = L > 0.f ? O / L : 0.f;
-    if (a.single || np == 1) {  // the workgroup saw the whole sequence
-      a.out[(row0 + h) * D + d] = o;
-    } else {
-      const size_t prow = (row0 + h) * a.num_parts + p;
-      a.ws_o[prow * D + d] = o;
-      if (d == 0) {
-        a.ws_m[prow] = mx;
-        a.ws_l[prow] = L;
-      }
+    sink.o[h * sink.o_stride + d] = L > 0.f ? O / L : 0.f;
+    if (sink.m && d == 0) {
+      sink.m[h * sink.ml_stride] = mx;
+      sink.l[h * sink.ml_stride] = L;
     }
   }
 }

@@ -28,6 +28,7 @@
 //    (two butterfly steps); everything else stays in the lane.
 #include "device_common.h"
 #include "decode_epilogue.h"
+#include "decode_schedule.h"
 #include "kernels.h"
 
 namespace pa {
@@ -55,8 +56,10 @@ struct VRow<64> {
 // DEPTH 2: the next tile's loads are issued before the current tile is
 // computed (register double buffer, 2 waves per SIMD).  DEPTH 1: one tile
 // per wave in flight and twice the waves per SIMD to hide the latency.
-template <int D, int BS, int G, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, int BS, int G, int NW, int DEPTH, bool NT>
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, int s,
+                                             int g, int n, int tile_begin, int tile_end,
+                                             const Sink& sink) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int KS = D / 32;                 // 16x16x32 steps for q.K
@@ -66,32 +69,11 @@ __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kerne
   static_assert(BPT <= 2, "a tile spans at most two blocks");
   using vrow_t = typename VRow<D>::type;
 
-  __shared__ DecodeSmem<G, D, NW> sm;
-
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int quad = lane >> 4;
   const int col = lane & 15;
-
-  int bid = blockIdx.x;
-  const int g = bid % a.num_kv_heads;
-  bid /= a.num_kv_heads;
-  const int p = bid % a.num_parts;
-  const int s = bid / a.num_parts;
   const int Hq = a.num_q_heads;
-
-  int n = a.cl[s];
-  n = n < 0 ? 0 : n;
-  n = min(n, a.max_tokens);
-  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= n) {
-    if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
-    return;
-  }
-  const int t_end = min(n, t_begin + a.part_tokens);
-  const int tile_begin = t_begin / kTile;
-  const int tile_end = (t_end + kTile - 1) / kTile;
 
   // ---- q as the B operand of q.K: lane (quad, col) = head col, chunk 4j+quad
   half8_t qb[KS];
@@ -151,14 +133,14 @@ __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kerne
       const half_t* vb = kb + v_offset;
       const uint32_t krow = (uint32_t)(row0 + col) * (D * 2);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) kr[j] = load16_at(kb, krow + (4 * j + quad) * 16);
+      for (int j = 0; j < KS; ++j) kr[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t off = (uint32_t)(row0 + 4 * quad + i) * (D * 2) + col * (VH * 2);
         if constexpr (D == 128)
-          vr[i] = load16_at(vb, off);
+          vr[i] = kv_load16<NT>(vb, off);
         else
-          vr[i] = load8_at(vb, off);
+          vr[i] = kv_load8<NT>(vb, off);
       }
     } else {
       // a tile spans two 8-row blocks: lanes pick their block
@@ -166,7 +148,7 @@ __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kerne
       const half_t* kb = kvh + (size_t)bk * block_stride;
       const uint32_t krow = (uint32_t)(col % BS) * (D * 2);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) kr[j] = load16_at(kb, krow + (4 * j + quad) * 16);
+      for (int j = 0; j < KS; ++j) kr[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * quad + i;
@@ -174,9 +156,9 @@ __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kerne
                            v_offset;
         const uint32_t off = (uint32_t)(t % BS) * (D * 2) + col * (VH * 2);
         if constexpr (D == 128)
-          vr[i] = load16_at(vb, off);
+          vr[i] = kv_load16<NT>(vb, off);
         else
-          vr[i] = load8_at(vb, off);
+          vr[i] = kv_load8<NT>(vb, off);
       }
     }
   };
@@ -286,39 +268,74 @@ __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kerne
     }
   }
   __syncthreads();
-  finish_workgroup<G, D, NW>(a, sm, s, g, p, (n + a.part_tokens - 1) / a.part_tokens);
+  finish_range<G, D, NW>(sm, sink);
 }
 
+template <int D, int BS, int G, int NW, int DEPTH, bool NT>
+__global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem<G, D, NW> sm;
+  __shared__ int prefix[kBalancedMaxSeqs];
+  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int n, int ta, int tb, const Sink& sink) {
+    decode_range<D, BS, G, NW, DEPTH, NT>(a, sm, s, g, n, ta, tb, sink);
+  });
+}
+
+unsigned grid_of(const DecodeArgs& a) {
+  if (a.schedule == kScheduleBalanced) return (unsigned)a.num_workgroups;
+  return (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
+}
+
+// mode 0: launch; mode 1: report resident workgroups per CU in *occ
 template <int D, int BS, int G, int NW>
-int launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
+int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
+  if (mode == 1) {
+    int n = 0;
+    const void* fn =
+        a.variant == 1 ? reinterpret_cast<const void*>(&decode_mfma_kernel<D, BS, G, NW, 1, true>)
+                       : reinterpret_cast<const void*>(&decode_mfma_kernel<D, BS, G, NW, 2, true>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 2;
+    *occ = n;
+    return 0;
+  }
+  const unsigned grid = grid_of(a);
   if (grid == 0) return 0;
-  if (a.variant == 1)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a);
+  const dim3 g(grid), b(NW * 64);
+  if (a.variant == 1 && a.cached_kv)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, false>), g, b, 0, stream, a);
+  else if (a.variant == 1)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, true>), g, b, 0, stream, a);
+  else if (a.cached_kv)
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, false>), g, b, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, true>), g, b, 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 template <int D, int BS, int NW>
-int by_group(const DecodeArgs& a, int group, hipStream_t stream) {
+int by_group(const DecodeArgs& a, int group, hipStream_t stream, int mode, int* occ) {
   switch (group) {
-    case 2: return launch_one<D, BS, 2, NW>(a, stream);
-    case 4: return launch_one<D, BS, 4, NW>(a, stream);
-    case 8: return launch_one<D, BS, 8, NW>(a, stream);
+    case 2: return launch_one<D, BS, 2, NW>(a, stream, mode, occ);
+    case 4: return launch_one<D, BS, 4, NW>(a, stream, mode, occ);
+    case 8: return launch_one<D, BS, 8, NW>(a, stream, mode, occ);
   }
   return 1;
 }
 
 template <int D, int NW>
-int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream) {
+int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream, int mode,
+             int* occ) {
   switch (block_size) {
-    case 8: return by_group<D, 8, NW>(a, group, stream);
-    case 16: return by_group<D, 16, NW>(a, group, stream);
-    case 32: return by_group<D, 32, NW>(a, group, stream);
+    case 8: return by_group<D, 8, NW>(a, group, stream, mode, occ);
+    case 16: return by_group<D, 16, NW>(a, group, stream, mode, occ);
+    case 32: return by_group<D, 32, NW>(a, group, stream, mode, occ);
   }
+  return 1;
+}
+
+int dispatch(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream,
+             int mode, int* occ) {
+  if (head_dim == 64) return by_block<64, 4>(a, block_size, group, stream, mode, occ);
+  if (head_dim == 128) return by_block<128, 4>(a, block_size, group, stream, mode, occ);
   return 1;
 }
 
@@ -327,9 +344,12 @@ int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream)
 int launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
                        int waves, hipStream_t stream) {
   if (dtype != 1 || waves != 4) return 1;
-  if (head_dim == 64) return by_block<64, 4>(a, block_size, group, stream);
-  if (head_dim == 128) return by_block<128, 4>(a, block_size, group, stream);
-  return 1;
+  return dispatch(a, head_dim, block_size, group, stream, 0, nullptr);
+}
+
+int decode_mfma_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group) {
+  int occ = 0;
+  return dispatch(a, head_dim, block_size, group, nullptr, 1, &occ) == 0 ? occ : 0;
 }
 
 }  // namespace pa

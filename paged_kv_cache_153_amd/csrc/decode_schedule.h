@@ -1,0 +1,146 @@
+// decode_schedule.h — how decode work is cut into workgroups.
+//
+// The unit of work is a 16-token tile of one (sequence, KV head).  Three
+// schedules share the same per-range code (decode_range in the kernels):
+//
+//  * single:    one workgroup per (sequence, KV head), whole context;
+//  * partition: one workgroup per (sequence, KV head, P-token partition);
+//  * balanced:  W workgroups, each given an equal, contiguous slice of the
+//               global tile list ordered (sequence, KV head, tile).  A
+//               workgroup walks the (sequence, KV head) segments its slice
+//               covers; a segment it covers completely is finished in place,
+//               a segment cut by a slice boundary leaves a partial (at most
+//               two per workgroup: its first and its last segment) that the
+//               balanced merge kernel combines.  Every workgroup does the
+//               same number of tiles whatever the length distribution, which
+//               removes the tail that ragged batches leave with the other
+//               schedules.
+//
+// The decode and the merge kernels derive the slices from the context
+// lengths with the same integer arithmetic (tiles(s) = ceil(n_s / 16), n_s
+// clamped exactly as the decode clamps it), so they agree on every boundary
+// without exchanging anything.
+#pragma once
+
+#include "decode_epilogue.h"
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pa {
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
+  int n = a.cl[s];
+  n = n < 0 ? 0 : n;
+  return min(n, a.max_tokens);
+}
+
+__device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
+
+// Fills prefix[s] = sum_{s' <= s} tiles(s') for s < S (per KV head) with the
+// whole workgroup; every thread sees the result after the final barrier.
+// Scans in chunks of blockDim.x with a running carry.
+__device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
+  const int nt = blockDim.x;
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += nt) {
+    const int s = base + (int)threadIdx.x;
+    if (s < a.num_seqs) prefix[s] = tiles_of(clamp_len(a, s));
+    __syncthreads();
+    for (int off = 1; off < nt; off <<= 1) {  // inclusive Hillis-Steele scan
+      int v = 0;
+      if (s < a.num_seqs && (int)threadIdx.x >= off) v = prefix[s - off];
+      __syncthreads();
+      if (s < a.num_seqs) prefix[s] += v;
+      __syncthreads();
+    }
+    if (s < a.num_seqs) prefix[s] += carry;
+    const int last = min(a.num_seqs, base + nt) - 1;
+    __syncthreads();
+    carry = prefix[last];
+    __syncthreads();
+  }
+}
+
+// Smallest s with hkv * prefix[s] > t (the sequence holding global tile t).
+__device__ __forceinline__ int owner_of(const int* prefix, int num_seqs, int hkv, int64_t t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)hkv * prefix[mid] > t) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Slice of workgroup w: [w * chunk, min((w + 1) * chunk, total)).
+__device__ __forceinline__ int64_t balanced_chunk(int64_t total, int workgroups) {
+  const int64_t c = (total + workgroups - 1) / workgroups;
+  return c > 0 ? c : 1;
+}
+
+}  // namespace pa
+
+namespace pa {
+
+// Maps this workgroup to its range(s) and calls
+// range(s, g, n, tile_begin, tile_end, sink) for each; ranges are processed
+// one after another by the whole workgroup (sm is reused in between).
+template <int G, int D, int NW, typename RangeFn>
+__device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) {
+  if (a.schedule == kScheduleBalanced) {
+    build_tile_prefix(a, prefix);
+    const int S = a.num_seqs, hkv = a.num_kv_heads;
+    const int64_t total = (int64_t)hkv * prefix[S - 1];
+    const int64_t chunk = balanced_chunk(total, a.num_workgroups);
+    int64_t t = (int64_t)blockIdx.x * chunk;
+    const int64_t t1 = min(t + chunk, total);
+    bool first = true;
+    while (t < t1) {
+      const int s = owner_of(prefix, S, hkv, t);
+      const int before_tiles = s ? prefix[s - 1] : 0;
+      const int nt = prefix[s] - before_tiles;  // > 0: s owns tile t
+      const int64_t before = (int64_t)hkv * before_tiles;
+      const int g = (int)((t - before) / nt);
+      const int64_t seg0 = before + (int64_t)g * nt;
+      const int ta = (int)(t - seg0);
+      const int tb = (int)min((int64_t)nt, t1 - seg0);
+      Sink sink;
+      if (ta == 0 && tb == nt) {
+        sink = output_sink<G, D>(a, s, g);
+      } else {  // slot 2w: the workgroup's first segment, 2w + 1: its last
+        const size_t slot = 2 * (size_t)blockIdx.x + (first ? 0 : 1);
+        sink = Sink{a.ws_o + slot * G * D, a.ws_m + slot * G, a.ws_l + slot * G, D, 1};
+      }
+      range(s, g, clamp_len(a, s), ta, tb, sink);
+      __syncthreads();
+      t = seg0 + tb;
+      first = false;
+    }
+    return;
+  }
+  int bid = blockIdx.x;
+  const int g = bid % a.num_kv_heads;
+  bid /= a.num_kv_heads;
+  const int p = bid % a.num_parts;
+  const int s = bid / a.num_parts;
+  int n = clamp_len(a, s);
+  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
+  const int t_begin = p * a.part_tokens;
+  if (t_begin >= n) {
+    if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
+    return;
+  }
+  const int t_end = min(n, t_begin + a.part_tokens);
+  const int np = (n + a.part_tokens - 1) / a.part_tokens;
+  Sink sink;
+  if (a.schedule == kScheduleSingle || np == 1) {
+    sink = output_sink<G, D>(a, s, g);
+  } else {
+    const size_t row0 = (size_t)s * a.num_q_heads + g * G;
+    sink = Sink{a.ws_o + (row0 * a.num_parts + p) * D, a.ws_m + row0 * a.num_parts + p,
+                a.ws_l + row0 * a.num_parts + p, (long)a.num_parts * D, a.num_parts};
+  }
+  range(s, g, n, t_begin / kTile, (t_end + kTile - 1) / kTile, sink);
+}
+
+}  // namespace pa

@@ -34,13 +34,18 @@
 //    NaN ones — reach the output.
 #include "device_common.h"
 #include "decode_epilogue.h"
+#include "decode_schedule.h"
 #include "kernels.h"
 
 namespace pa {
 namespace {
 
-template <typename T, int D, int BS, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+// One range: tiles [tile_begin, tile_end) of (sequence s, KV head g), whose
+// context holds n tokens; the result goes to `sink`.
+template <typename T, int D, int BS, int G, int NW, bool NT>
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, int s,
+                                             int g, int n, int tile_begin, int tile_end,
+                                             const Sink& sink) {
   constexpr int E = DType<T>::kBytes;
   constexpr int EPL = 16 / E;        // elements per 16-byte chunk
   constexpr int LPT = D / EPL;       // lanes per token row
@@ -50,32 +55,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "unsupported row width");
   static_assert(RPI <= BS, "a load instruction must stay inside one block");
 
-  __shared__ DecodeSmem<G, D, NW> sm;
-
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int r = lane / LPT;
   const int c = lane % LPT;
-
-  int bid = blockIdx.x;
-  const int g = bid % a.num_kv_heads;
-  bid /= a.num_kv_heads;
-  const int p = bid % a.num_parts;
-  const int s = bid / a.num_parts;
   const int Hq = a.num_q_heads;
-
-  int n = a.cl[s];
-  n = n < 0 ? 0 : n;
-  n = min(n, a.max_tokens);
-  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= n) {
-    if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
-    return;
-  }
-  const int t_end = min(n, t_begin + a.part_tokens);
-  const int tile_begin = t_begin / kTile;
-  const int tile_end = (t_end + kTile - 1) / kTile;
 
   // ---- query chunk of each grouped head, held in registers ----------------
   const T* qbase = reinterpret_cast<const T*>(a.q) + ((size_t)s * Hq + g * G) * D + c * EPL;
@@ -132,8 +116,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
       const int row = BS >= kTile ? row0 + i * RPI + r : (i * RPI) % BS + r;
       const T* base = kvh + (size_t)blk[jj] * block_stride;   // wave-uniform
       const uint32_t off = (uint32_t)(row * D + c * EPL) * (uint32_t)sizeof(T);
-      kr[i] = load16_at(base, off);
-      vr[i] = load16_at(base + v_offset, off);
+      kr[i] = kv_load16<NT>(base, off);
+      vr[i] = kv_load16<NT>(base + v_offset, off);
     }
   };
 
@@ -259,45 +243,82 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish_workgroup<G, D, NW>(a, sm, s, g, p, (n + a.part_tokens - 1) / a.part_tokens);
+  finish_range<G, D, NW>(sm, sink);
 }
 
+template <typename T, int D, int BS, int G, int NW, bool NT>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem<G, D, NW> sm;
+  __shared__ int prefix[kBalancedMaxSeqs];
+  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int n, int ta, int tb, const Sink& sink) {
+    decode_range<T, D, BS, G, NW, NT>(a, sm, s, g, n, ta, tb, sink);
+  });
+}
+
+unsigned grid_of(const DecodeArgs& a) {
+  if (a.schedule == kScheduleBalanced) return (unsigned)a.num_workgroups;
+  return (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
+}
+
+// mode 0: launch; mode 1: report resident workgroups per CU in *occ
 template <typename T, int D, int BS, int G, int NW>
-int launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
+int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
+  if (mode == 1) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&decode_valu_kernel<T, D, BS, G, NW, true>),
+            NW * 64, 0) != hipSuccess)
+      return 2;
+    *occ = n;
+    return 0;
+  }
+  const unsigned grid = grid_of(a);
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, NW>), dim3(grid), dim3(NW * 64), 0, stream,
-                     a);
+  if (a.cached_kv)
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, NW, false>), dim3(grid), dim3(NW * 64),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, BS, G, NW, true>), dim3(grid), dim3(NW * 64),
+                       0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 template <typename T, int D, int BS, int NW>
-int by_group(const DecodeArgs& a, int group, hipStream_t stream) {
+int by_group(const DecodeArgs& a, int group, hipStream_t stream, int mode, int* occ) {
   switch (group) {
-    case 1: return launch_one<T, D, BS, 1, NW>(a, stream);
-    case 2: return launch_one<T, D, BS, 2, NW>(a, stream);
-    case 4: return launch_one<T, D, BS, 4, NW>(a, stream);
-    case 8: return launch_one<T, D, BS, 8, NW>(a, stream);
+    case 1: return launch_one<T, D, BS, 1, NW>(a, stream, mode, occ);
+    case 2: return launch_one<T, D, BS, 2, NW>(a, stream, mode, occ);
+    case 4: return launch_one<T, D, BS, 4, NW>(a, stream, mode, occ);
+    case 8: return launch_one<T, D, BS, 8, NW>(a, stream, mode, occ);
   }
   return 1;
 }
 
 template <typename T, int D, int NW>
-int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream) {
+int by_block(const DecodeArgs& a, int block_size, int group, hipStream_t stream, int mode,
+             int* occ) {
   switch (block_size) {
-    case 8: return by_group<T, D, 8, NW>(a, group, stream);
-    case 16: return by_group<T, D, 16, NW>(a, group, stream);
-    case 32: return by_group<T, D, 32, NW>(a, group, stream);
+    case 8: return by_group<T, D, 8, NW>(a, group, stream, mode, occ);
+    case 16: return by_group<T, D, 16, NW>(a, group, stream, mode, occ);
+    case 32: return by_group<T, D, 32, NW>(a, group, stream, mode, occ);
   }
   return 1;
 }
 
 template <typename T, int NW>
-int by_dim(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream) {
+int by_dim(const DecodeArgs& a, int head_dim, int block_size, int group, hipStream_t stream,
+           int mode, int* occ) {
   switch (head_dim) {
-    case 64: return by_block<T, 64, NW>(a, block_size, group, stream);
-    case 128: return by_block<T, 128, NW>(a, block_size, group, stream);
+    case 64: return by_block<T, 64, NW>(a, block_size, group, stream, mode, occ);
+    case 128: return by_block<T, 128, NW>(a, block_size, group, stream, mode, occ);
   }
+  return 1;
+}
+
+int dispatch(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
+             hipStream_t stream, int mode, int* occ) {
+  if (dtype == 0) return by_dim<float, 4>(a, head_dim, block_size, group, stream, mode, occ);
+  if (dtype == 1) return by_dim<half_t, 4>(a, head_dim, block_size, group, stream, mode, occ);
   return 1;
 }
 
@@ -306,9 +327,13 @@ int by_dim(const DecodeArgs& a, int head_dim, int block_size, int group, hipStre
 int launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
                        int waves, hipStream_t stream) {
   if (waves != 4) return 1;
-  if (dtype == 0) return by_dim<float, 4>(a, head_dim, block_size, group, stream);
-  if (dtype == 1) return by_dim<half_t, 4>(a, head_dim, block_size, group, stream);
-  return 1;
+  return dispatch(a, dtype, head_dim, block_size, group, stream, 0, nullptr);
+}
+
+int decode_valu_occupancy(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                          int group) {
+  int occ = 0;
+  return dispatch(a, dtype, head_dim, block_size, group, nullptr, 1, &occ) == 0 ? occ : 0;
 }
 
 }  // namespace pa

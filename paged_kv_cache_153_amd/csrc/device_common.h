@@ -95,6 +95,29 @@ __device__ __forceinline__ u32x2_t load8_at(const void* base, uint32_t byte_off)
   return *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const char*>(base) + byte_off);
 }
 
+// Streaming variants: every K/V byte is read once per call, so these carry
+// the non-temporal hint (global_load ... nt) to keep them from displacing
+// cached data.
+__device__ __forceinline__ u32x4_t load16_nt(const void* base, uint32_t byte_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+__device__ __forceinline__ u32x2_t load8_nt(const void* base, uint32_t byte_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x2_t*>(reinterpret_cast<const char*>(base) + byte_off));
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t kv_load16(const void* base, uint32_t byte_off) {
+  if constexpr (NT) return load16_nt(base, byte_off);
+  else return load16_at(base, byte_off);
+}
+template <bool NT>
+__device__ __forceinline__ u32x2_t kv_load8(const void* base, uint32_t byte_off) {
+  if constexpr (NT) return load8_nt(base, byte_off);
+  else return load8_at(base, byte_off);
+}
+
 // True when any lane of the wave has `pred` set (wave-uniform).
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;

@@ -12,6 +12,13 @@ namespace pa {
 // are whole tiles.
 constexpr int kTile = 16;
 
+// How decode work is cut into workgroups (see decode_schedule.h).
+constexpr int kScheduleSingle = 0;     // one workgroup per (sequence, KV head)
+constexpr int kSchedulePartition = 1;  // ... per (sequence, KV head, partition)
+constexpr int kScheduleBalanced = 2;   // W workgroups, equal tile slices
+// Sequences the balanced schedule handles: its tile prefix lives in LDS.
+constexpr int kBalancedMaxSeqs = 1024;
+
 struct DecodeArgs {
   float* out;               // [S, Hq, D] final output (single pass)
   float* ws_o;              // [S, Hq, NP, D] partition outputs (normalised)
@@ -29,9 +36,11 @@ struct DecodeArgs {
   int max_tokens;           // MB * BS: context lengths are clamped to this
   int num_parts;            // NP
   int part_tokens;          // P (multiple of kTile and of BS); huge when single
-  int single;               // 1: write `out` directly; 0: write ws_*
+  int schedule;             // kScheduleSingle / kSchedulePartition / kScheduleBalanced
+  int num_workgroups;       // balanced: W workgroups (grid size)
   float scale_log2;         // scale * log2(e)
   int variant;              // MFMA: 1 = one tile in flight per wave, 0 = two
+  int cached_kv;            // 1: plain K/V loads; 0: non-temporal (streaming) loads
 };
 
 // Each returns 0 on success, 1 if the (dtype, D, BS, G) combination has no
@@ -41,6 +50,12 @@ int launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int block_s
 int launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
                        int waves, hipStream_t stream);
 int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream);
+int launch_merge_balanced(const DecodeArgs& a, int head_dim, hipStream_t stream);
+// Resident workgroups per compute unit of the kernel a launch would pick
+// (0 if none): sizes the balanced grid.
+int decode_valu_occupancy(const DecodeArgs& a, int dtype, int head_dim, int block_size,
+                          int group);
+int decode_mfma_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
 int launch_cache_write(const void* key, const void* value, void* kv, const int64_t* slots,
                        int64_t num_tokens, const int32_t* cow_pairs, int64_t num_cow,
                        int64_t num_blocks, int num_kv_heads, int head_dim, int block_size,

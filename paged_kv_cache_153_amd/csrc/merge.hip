@@ -16,6 +16,7 @@
 // thread needs — m_p, l_p and its slice of o_p — is issued at once and the
 // only dependent round trip is the context length.  The groups' states are
 // combined through LDS with the same rescaling.
+#include "decode_schedule.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -82,6 +83,51 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   }
 }
 
+// Balanced schedule: one workgroup per (sequence, KV head) merges the
+// partials that the workgroups whose slices cut this segment left in their
+// slots (slot 2w if the segment was workgroup w's first, 2w + 1 if its last),
+// for all G query heads of the group.  It recomputes the slices from the
+// context lengths exactly as the decode did.  A segment inside one slice was
+// finished by the decode; an empty sequence gets zeros here.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
+  __shared__ int prefix[kBalancedMaxSeqs];
+  build_tile_prefix(a, prefix);
+  const int S = a.num_seqs, hkv = a.num_kv_heads, G = a.num_q_heads / hkv;
+  const int s = blockIdx.x / hkv;
+  const int g = blockIdx.x % hkv;
+  const int before_tiles = s ? prefix[s - 1] : 0;
+  const int nt = prefix[s] - before_tiles;
+  float* out = a.out + ((size_t)s * a.num_q_heads + (size_t)g * G) * D;
+  if (nt == 0) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kMergeThreads) out[idx] = 0.f;
+    return;
+  }
+  const int64_t total = (int64_t)hkv * prefix[S - 1];
+  const int64_t chunk = balanced_chunk(total, a.num_workgroups);
+  const int64_t off = (int64_t)hkv * before_tiles + (int64_t)g * nt;
+  const int64_t w_lo = off / chunk;
+  const int64_t w_hi = (off + nt - 1) / chunk;
+  if (w_lo == w_hi) return;
+  for (int idx = threadIdx.x; idx < G * D; idx += kMergeThreads) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float mx = kMaxInit;
+    for (int64_t w = w_lo; w <= w_hi; ++w) {
+      const size_t slot = 2 * (size_t)w + (w * chunk >= off ? 0 : 1);
+      mx = fmaxf(mx, a.ws_m[slot * G + h]);
+    }
+    float L = 0.f, O = 0.f;
+    for (int64_t w = w_lo; w <= w_hi; ++w) {
+      const size_t slot = 2 * (size_t)w + (w * chunk >= off ? 0 : 1);
+      const float wgt = a.ws_l[slot * G + h] * fast_exp2(a.ws_m[slot * G + h] - mx);
+      L += wgt;
+      O = fmaf(wgt, a.ws_o[(slot * G + h) * D + d], O);
+    }
+    out[idx] = L > 0.f ? O / L : 0.f;
+  }
+}
+
 }  // namespace
 
 int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream) {
@@ -91,6 +137,18 @@ int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream) {
     hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
+  else
+    return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int launch_merge_balanced(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+  const unsigned grid = (unsigned)a.num_seqs * a.num_kv_heads;
+  if (grid == 0) return 0;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(merge_balanced_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(merge_balanced_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else
     return 1;
   return hipGetLastError() == hipSuccess ? 0 : 2;

@@ -6,6 +6,7 @@
 // enqueued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -19,6 +20,7 @@
 namespace pa {
 
 namespace {
+
 thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -31,18 +33,24 @@ bool check_mode() {
   return on;
 }
 
-// Partition size used when the caller passes 0 (measured on MI355X with
-// 16 KiB-per-token MHA and 4 KiB-per-token GQA layers at block 16):
-//  * single pass when one workgroup per (sequence, KV head) already fills the
-//    chip (>= 1024 pairs) and contexts are moderate: no merge traffic;
-//  * otherwise partitions of 512 tokens up to 4K contexts, 1024 up to 16K and
-//    2048 beyond: longer contexts take longer partitions, which cut the
-//    per-workgroup start-up and the merge traffic while still leaving several
-//    workgroups per compute unit.
-int choose_partition(int num_seqs, int num_kv_heads, int max_context_len) {
+// Schedule used when the caller passes partition_size 0 (measured on
+// MI355X with 16 KiB-per-token MHA and 4 KiB-per-token GQA layers):
+//  * single pass (-1) when one workgroup per (sequence, KV head) already fills
+//    the chip (>= 1024 pairs) and contexts are moderate, or contexts are
+//    short: no partials, no merge;
+//  * pools read with cached loads (blocks shared by many sequences, e.g. a
+//    common prefix): fixed partitions, so every sequence's first partition —
+//    the shared prefix — is read by all workgroups at the same time and hits
+//    in cache;
+//  * otherwise the balanced schedule (-2): equal tile slices per workgroup
+//    whatever the length mix (it needs S <= kBalancedMaxSeqs);
+//  * fixed partitions are 512 tokens up to 4K contexts, 1024 up to 16K and
+//    2048 beyond.
+int choose_partition(int num_seqs, int num_kv_heads, int max_context_len, int cached_kv) {
   const long pairs = (long)num_seqs * num_kv_heads;
   if (max_context_len <= 512) return -1;
   if (pairs >= 1024 && max_context_len <= 8192) return -1;
+  if (!cached_kv && num_seqs <= kBalancedMaxSeqs) return -2;
   if (max_context_len <= 4096) return 512;
   if (max_context_len <= 16384) return 1024;
   return 2048;
@@ -57,26 +65,60 @@ int choose_kernel(int dtype, int group) {
 }
 
 struct Plan {
-  int single = 1;
+  int schedule = kScheduleSingle;
   int part_tokens = 0;
   int num_parts = 1;
+  int workgroups = 0;  // balanced: grid size upper bound used for the workspace
   size_t ws_bytes = 0;
   size_t off_m = 0, off_l = 0;
 };
 
-
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-Plan make_plan(int num_seqs, int num_q_heads, int head_dim, int max_tokens, int partition) {
+// Compute units of the current device (cached per device id); 0 if unknown.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// At most this many 256-thread workgroups fit on one compute unit; the
+// balanced workspace is sized for it so the size does not depend on which
+// kernel variant is picked.
+constexpr int kMaxWorkgroupsPerCU = 8;
+
+Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_tokens,
+               int partition, int cus) {
   Plan p;
-  if (partition < 0) {
-    p.single = 1;
+  if (partition == -1) {
+    p.schedule = kScheduleSingle;
     p.num_parts = 1;
     p.part_tokens = (max_tokens + kTile - 1) / kTile * kTile + kTile;
     return p;
   }
-  p.single = 0;
+  if (partition == -2) {
+    p.schedule = kScheduleBalanced;
+    p.num_parts = 1;
+    p.part_tokens = (max_tokens + kTile - 1) / kTile * kTile + kTile;
+    p.workgroups = cus * kMaxWorkgroupsPerCU;
+    const int group = num_q_heads / num_kv_heads;
+    const size_t slots = 2 * (size_t)p.workgroups * group;
+    const size_t bytes_o = round_up(slots * head_dim * sizeof(float));
+    const size_t bytes_ml = round_up(slots * sizeof(float));
+    p.off_m = bytes_o;
+    p.off_l = bytes_o + bytes_ml;
+    p.ws_bytes = bytes_o + 2 * bytes_ml;
+    return p;
+  }
+  p.schedule = kSchedulePartition;
   p.part_tokens = partition;
   p.num_parts = max_tokens <= 0 ? 1 : (max_tokens + partition - 1) / partition;
   const size_t rows = (size_t)num_seqs * num_q_heads * p.num_parts;
@@ -220,20 +262,33 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
     return fail(PA_ERR_UNSUPPORTED, "block_size");
   if (group != 1 && group != 2 && group != 4 && group != 8)
     return fail(PA_ERR_UNSUPPORTED, "group size");
+  const int cached_kv = (kernel & PA_KV_CACHED) != 0;
+  if (kernel & ~(0xFF | PA_KV_CACHED)) return fail(PA_ERR_INVALID_ARG, "kernel flags");
+  kernel &= 0xFF;
   if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA) return fail(PA_ERR_INVALID_ARG, "kernel");
   if (kernel == PA_KERNEL_MFMA && (dtype != PA_F16 || group < 2))
     return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs f16 and a query group of 2 or more");
-  if (partition_size < -1 ||
+  if (partition_size < -2 ||
       (partition_size > 0 && (partition_size % pa::kTile || partition_size % block_size)))
-    return fail(PA_ERR_INVALID_ARG, "partition_size must be -1, 0 or a multiple of 16 and "
+    return fail(PA_ERR_INVALID_ARG, "partition_size must be -2, -1, 0 or a multiple of 16 and "
                                     "block_size");
   const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
   if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   const int max_tokens = (int)max_tokens_ll;
   const int ctx = max_context_len < max_tokens ? max_context_len : max_tokens;
   int part = partition_size;
-  if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx);
-  const pa::Plan plan = pa::make_plan(num_seqs, num_q_heads, head_dim, ctx, part);
+  if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx, cached_kv);
+  // the balanced schedule keeps an int32 tile prefix of all sequences in LDS
+  if (part == -2 && (num_seqs > pa::kBalancedMaxSeqs ||
+                     (long long)num_seqs * ((max_tokens + pa::kTile - 1) / pa::kTile) >= (1LL << 31)))
+    part = 2048;
+  int cus = 0;
+  if (part == -2) {
+    cus = pa::device_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+  }
+  const pa::Plan plan = pa::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, part,
+                                      cus);
   if (workspace_needed) *workspace_needed = plan.ws_bytes;
   if (!out) return PA_OK;  // size query
   if (num_seqs == 0) return PA_OK;
@@ -267,22 +322,39 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   a.max_tokens = max_tokens;
   a.num_parts = plan.num_parts;
   a.part_tokens = plan.part_tokens;
-  a.single = plan.single;
+  a.schedule = plan.schedule;
   a.scale_log2 = scale * 1.4426950408889634f;
-  // MFMA kernel: one tile per wave in flight at twice the occupancy for
-  // single pass (long-lived workgroups), the register double buffer for
-  // split partitions (measured faster there).
-  a.variant = plan.single ? 1 : 0;
+  // MFMA kernel: the register double buffer when K/V stream from HBM; one
+  // tile per wave in flight at twice the occupancy when they are read through
+  // the caches (shared blocks): measured faster in each case.
+  a.variant = cached_kv ? 1 : 0;
+  {  // PA_TUNE_VARIANT=0|1 overrides the choice (tuning experiments only)
+    static const int forced = [] {
+      const char* e = std::getenv("PA_TUNE_VARIANT");
+      return e ? std::atoi(e) : -1;
+    }();
+    if (forced == 0 || forced == 1) a.variant = forced;
+  }
+  a.cached_kv = cached_kv;
 
   int use = kernel;
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);
+  if (plan.schedule == pa::kScheduleBalanced) {
+    // as many workgroups as are resident at once: one wave of the grid
+    const int occ = use == PA_KERNEL_MFMA
+                        ? pa::decode_mfma_occupancy(a, head_dim, block_size, group)
+                        : pa::decode_valu_occupancy(a, dtype, head_dim, block_size, group);
+    if (occ <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
+    a.num_workgroups = std::min(plan.workgroups, cus * std::min(occ, pa::kMaxWorkgroupsPerCU));
+  }
   int rc = use == PA_KERNEL_MFMA
                ? pa::launch_decode_mfma(a, dtype, head_dim, block_size, group, 4, stream)
                : pa::launch_decode_valu(a, dtype, head_dim, block_size, group, 4, stream);
   if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
-  if (!plan.single) {
-    rc = pa::launch_merge(a, head_dim, stream);
+  if (plan.schedule != pa::kScheduleSingle) {
+    rc = plan.schedule == pa::kScheduleBalanced ? pa::launch_merge_balanced(a, head_dim, stream)
+                                                : pa::launch_merge(a, head_dim, stream);
     if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no merge kernel for this head_dim");
     if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
   }

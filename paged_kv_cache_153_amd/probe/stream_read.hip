@@ -6,6 +6,8 @@
 //  * pa_probe_read_tiles: reads 4 KiB tiles in the order given by a device
 //    index array — the access pattern of a paged K or V tile at block 16,
 //    head_dim 128, fp16.
+// Each reads either with plain loads or with non-temporal (streaming) loads,
+// the two policies pa_decode can use for K/V.
 // Both fold what they read into one value that is stored only if it matches
 // an impossible constant, so the loads cannot be optimised away and nothing
 // is written in practice.
@@ -14,18 +16,26 @@
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+template <bool NT>
+__device__ __forceinline__ u4 ld(const u4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(256) void read_linear(const u4* __restrict__ p, size_t n16,
                                                    uint32_t* out) {
   uint32_t acc = 0;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
        i += (size_t)gridDim.x * blockDim.x) {
-    const u4 v = p[i];
+    const u4 v = ld<NT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
 // blockDim 256 = one 4 KiB tile per load instruction; 8 tiles in flight
+template <bool NT>
 __global__ __launch_bounds__(256) void read_tiles(const u4* __restrict__ p,
                                                   const int32_t* __restrict__ idx, int per_wg,
                                                   int64_t num_tiles, uint32_t* out) {
@@ -37,7 +47,7 @@ __global__ __launch_bounds__(256) void read_tiles(const u4* __restrict__ p,
     for (int u = 0; u < 8; ++u) {
       int64_t tile = t + u < per_wg ? my[t + u] : 0;
       tile = tile < 0 || tile >= num_tiles ? 0 : tile;
-      v[u] = p[tile * 256 + threadIdx.x];
+      v[u] = ld<NT>(p + tile * 256 + threadIdx.x);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -47,24 +57,34 @@ __global__ __launch_bounds__(256) void read_tiles(const u4* __restrict__ p,
 
 extern "C" {
 
-// Reads `bytes` (a multiple of 16) from `buf` with `workgroups` x 256 threads.
-int pa_probe_read_linear(const void* buf, size_t bytes, int workgroups, uint32_t* sink,
-                         void* stream) {
+// Reads `bytes` (a multiple of 16) from `buf` with `workgroups` x 256 threads;
+// `streaming` != 0 uses non-temporal loads.
+int pa_probe_read_linear(const void* buf, size_t bytes, int workgroups, int streaming,
+                         uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes % 16 || workgroups <= 0) return -1;
-  hipLaunchKernelGGL(read_linear, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
-                     (const u4*)buf, bytes / 16, sink);
+  if (streaming)
+    hipLaunchKernelGGL(read_linear<true>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                       (const u4*)buf, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_linear<false>, dim3(workgroups), dim3(256), 0, (hipStream_t)stream,
+                       (const u4*)buf, bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
 // Reads the 4 KiB tiles of `buf` listed in `tiles` ([num_listed] int32 on the
 // device, each in [0, num_tiles)), `per_wg` consecutive entries per workgroup.
 int pa_probe_read_tiles(const void* buf, int64_t num_tiles, const int32_t* tiles,
-                        int64_t num_listed, int per_wg, uint32_t* sink, void* stream) {
+                        int64_t num_listed, int per_wg, int streaming, uint32_t* sink,
+                        void* stream) {
   if (!buf || !tiles || !sink || per_wg <= 0 || num_listed % per_wg) return -1;
   const int64_t wgs = num_listed / per_wg;
   if (wgs <= 0 || wgs > INT32_MAX) return -1;
-  hipLaunchKernelGGL(read_tiles, dim3((unsigned)wgs), dim3(256), 0, (hipStream_t)stream,
-                     (const u4*)buf, tiles, per_wg, num_tiles, sink);
+  if (streaming)
+    hipLaunchKernelGGL(read_tiles<true>, dim3((unsigned)wgs), dim3(256), 0, (hipStream_t)stream,
+                       (const u4*)buf, tiles, per_wg, num_tiles, sink);
+  else
+    hipLaunchKernelGGL(read_tiles<false>, dim3((unsigned)wgs), dim3(256), 0,
+                       (hipStream_t)stream, (const u4*)buf, tiles, per_wg, num_tiles, sink);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

@@ -65,8 +65,8 @@ def _decode_status(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), -2), (dict(bs=24), -2), (dict(Hq=6, Hkv=2), -2), (dict(Hq=7), -1),
     (dict(dtype=5), -2), (dict(kernel=2, dtype=0), -2), (dict(kernel=2, Hq=2), -2),
-    (dict(part=24), -1), (dict(part=8, bs=16), -1), (dict(part=-2), -1), (dict(MB=0), -1),
-    (dict(kernel=7), -1), (dict(NB=0), -1),
+    (dict(part=24), -1), (dict(part=8, bs=16), -1), (dict(part=-3), -1), (dict(MB=0), -1),
+    (dict(kernel=7), -1), (dict(NB=0), -1), (dict(kernel=0x200), -1), (dict(kernel=0x103), -1),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert _decode_status(**kw) == status

@@ -40,7 +40,7 @@ def kernels_for(x):
     return ks
 
 
-def check(x, device, parts=(-1, 0, 16, 64), kernels=None, tol=TOL):
+def check(x, device, parts=(-1, -2, 0, 16, 64), kernels=None, tol=TOL):
     want = ref_decode(x)
     for kern in kernels or kernels_for(x):
         for part in parts:
@@ -56,7 +56,7 @@ def check(x, device, parts=(-1, 0, 16, 64), kernels=None, tol=TOL):
 # --------------------------------------------------------------------------
 def test_tiny_fp32_mha(device):
     """4 seqs, MHA 8 x 64, fp32, block 16, lengths 100/37/16/1, scale 1/8."""
-    check(synth.tiny(seed=0), device, parts=(-1, 0, 16, 32, 48, 64))
+    check(synth.tiny(seed=0), device, parts=(-1, -2, 0, 16, 32, 48, 64))
 
 
 def test_tiny_unused_rows_poisoned_with_nan(device):
@@ -64,7 +64,7 @@ def test_tiny_unused_rows_poisoned_with_nan(device):
     uses) hold NaN: the output must not see them."""
     x = synth.tiny(seed=1, fill_unused=float("nan"))
     assert torch.isnan(x.kv_cache).any()
-    check(x, device, parts=(-1, 16, 32))
+    check(x, device, parts=(-1, -2, 16, 32))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
@@ -75,7 +75,7 @@ def test_shapes_ragged(device, dtype, bs, d, hq, hkv):
     lens = [1, 15, 16, 17, 100, 255, 513, 1030]
     x = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype=dtype, seed=bs + d + hq,
                                  fill_unused=float("nan"), name=f"{dtype}-bs{bs}-d{d}-{hq}/{hkv}")
-    check(x, device, parts=(-1, 0, 32, 512))
+    check(x, device, parts=(-1, -2, 0, 32, 512))
 
 
 def test_single_token_is_exact(device):
@@ -91,7 +91,7 @@ def test_single_token_is_exact(device):
 def test_zero_length_sequences(device):
     x = synth.make_decode_inputs([0, 37, 0, 1], 8, 2, 128, 16, dtype="f16", seed=4)
     for kern in kernels_for(x):
-        for part in (-1, 0, 16):
+        for part in (-1, -2, 0, 16):
             got = run_decode(x, device, kernel=kern, partition_size=part)
             assert np.all(got[0] == 0) and np.all(got[2] == 0)
             assert np.abs(got - ref_decode(x)).max() <= TOL
@@ -99,7 +99,7 @@ def test_zero_length_sequences(device):
 
 def test_scale_zero_gives_mean_of_values(device):
     x = synth.make_decode_inputs([33, 200], 8, 2, 128, 16, dtype="f16", seed=5, scale=0.0)
-    check(x, device, parts=(-1, 32))
+    check(x, device, parts=(-1, -2, 32))
 
 
 def test_physical_permutation_invariance(device):
@@ -113,7 +113,7 @@ def test_physical_permutation_invariance(device):
                       x.block_tables)
     y = synth.DecodeInputs("perm", x.q, kv2, bt2, x.context_lens, x.scale, x.seed)
     for kern in kernels_for(x):
-        for part in (-1, 512):
+        for part in (-1, -2, 512):
             a = run_decode(x, device, kernel=kern, partition_size=part)
             b = run_decode(y, device, kernel=kern, partition_size=part)
             assert np.array_equal(a, b), (kern, part)
@@ -124,7 +124,7 @@ def test_split_agrees_with_single(device):
     want = ref_decode(x)
     for kern in kernels_for(x):
         single = run_decode(x, device, kernel=kern, partition_size=-1)
-        for part in (16, 256, 512, 4096):
+        for part in (-2, 16, 256, 512, 4096):
             split = run_decode(x, device, kernel=kern, partition_size=part)
             assert np.abs(split - single).max() <= TOL
             assert np.abs(split - want).max() <= TOL
@@ -133,34 +133,34 @@ def test_split_agrees_with_single(device):
 def test_peaked_softmax(device):
     """Large logits: one token dominates each head; scores ~ +/-100."""
     x = synth.make_decode_inputs([700, 64], 16, 2, 128, 16, dtype="f16", seed=8, scale=1.0)
-    check(x, device, parts=(-1, 64))
+    check(x, device, parts=(-1, -2, 64))
 
 
 def test_table_width_larger_than_needed(device):
     """Tables padded with -1 beyond each sequence's blocks, max_blocks > needed."""
     x = synth.make_decode_inputs([40, 3], 8, 8, 64, 8, dtype="f32", seed=9, max_blocks=20)
-    check(x, device, parts=(-1, 16))
+    check(x, device, parts=(-1, -2, 16))
 
 
 # --------------------------------------------------------------------------
 # workload-shaped cases at oracle-friendly sizes
 # --------------------------------------------------------------------------
 def test_llama7b_mha_shape_small(device):
-    check(synth.llama7b_mha(seed=0, num_seqs=3, context=700), device, parts=(-1, 0, 512))
+    check(synth.llama7b_mha(seed=0, num_seqs=3, context=700), device, parts=(-1, -2, 0, 512))
 
 
 def test_gqa7b_shape_small(device):
-    check(synth.gqa7b(seed=0, num_seqs=6, lo=128, hi=2100), device, parts=(-1, 0, 512))
+    check(synth.gqa7b(seed=0, num_seqs=6, lo=128, hi=2100), device, parts=(-1, -2, 0, 512))
 
 
 def test_llama70b_shape_small(device):
-    check(synth.llama70b(seed=0, num_seqs=2, context=2600), device, parts=(-1, 0, 512))
+    check(synth.llama70b(seed=0, num_seqs=2, context=2600), device, parts=(-1, -2, 0, 512))
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_shared_prefix_shape_small(device, bs):
     x = synth.shared_prefix(seed=0, block_size=bs, num_seqs=6, prefix=512, suffix_hi=300)
-    check(x, device, parts=(-1, 0, 512))
+    check(x, device, parts=(-1, -2, 0, 512))
 
 
 # --------------------------------------------------------------------------
@@ -197,3 +197,36 @@ def test_full_size_sampled(device, name):
     _sampled_check(x, out, samples)
     del x, out
     torch.cuda.empty_cache()
+
+
+def test_cached_and_streaming_loads_agree(device):
+    """The load policy changes no arithmetic where the schedule is the same
+    (single pass, fixed partitions): bitwise equal.  Under the balanced
+    schedule the MFMA kernel's cached variant fits more workgroups, so the
+    slices (and the summation order) differ: equal within tolerance."""
+    x = synth.make_decode_inputs([700, 33, 2049], 32, 8, 128, 16, dtype="f16", seed=12)
+    want = ref_decode(x)
+    for kern in kernels_for(x):
+        for part in (-1, -2, 512):
+            a = run_decode(x, device, kernel=kern, partition_size=part)
+            b = run_decode(x, device, kernel=kern, partition_size=part, cached_kv=True)
+            if part == -2 and kern == "mfma":
+                assert np.abs(a - b).max() <= 1e-5 and np.abs(b - want).max() <= TOL
+            else:
+                assert np.array_equal(a, b), (kern, part)
+    y = synth.tiny(seed=2)
+    assert np.array_equal(run_decode(y, device), run_decode(y, device, cached_kv=True))
+
+
+@pytest.mark.parametrize("kern", ["valu", "mfma"])
+def test_balanced_schedule_many_short_and_long(device, kern):
+    """Balanced slices cut sequences at arbitrary tiles: many slices per long
+    sequence, many whole short sequences per slice, and empty ones."""
+    rng = np.random.default_rng(13)
+    lens = [0, 1] + rng.integers(1, 64, 40).tolist() + [5000, 0, 3, 2049, 16, 17]
+    x = synth.make_decode_inputs(lens, 16, 4, 128, 16, dtype="f16", seed=14,
+                                 fill_unused=float("nan"))
+    want = ref_decode(x)
+    got = run_decode(x, device, kernel=kern, partition_size=-2)
+    assert np.isfinite(got).all() and np.abs(got - want).max() <= TOL
+    assert np.all(got[0] == 0) and np.all(got[len(lens) - 5] == 0)

@@ -1,0 +1,212 @@
+"""Pin checks for a decode-attention implementation, shared by the oracle's
+pin tests and the mutation tests that show the pins catch plausible
+mistakes.  Each check returns True when `decode` agrees with something other
+than itself: values printed on the pages, a library routine on contiguous
+data, exact special cases or invariants.  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def page_example():
+    with open(os.path.join(GOLDEN, "paging_example.json")) as f:
+        return json.load(f)
+
+
+def _slot_id_pool(num_blocks, block_size, heads=1, head_dim=4):
+    kv = np.zeros((num_blocks, 2, heads, block_size, head_dim))
+    for b in range(num_blocks):
+        for r in range(block_size):
+            kv[b, 0, :, r, :] = b * 1000 + r
+            kv[b, 1, :, r, :] = -(b * 1000 + r)
+    return kv
+
+
+def scale_zero_page_example(decode):
+    """scale 0: the mean of the V rows the page's table maps (printed ranges)."""
+    ex = page_example()
+    kv = _slot_id_pool(10, ex["block_size"])
+    expect = []
+    for rng in ex["ranges"]:
+        lo, hi = rng["tokens"]
+        expect += [-(rng["physical"] * 1000 + (t - lo)) for t in range(lo, hi + 1)]
+    out = decode(np.ones((1, 1, 4)), kv, np.array([ex["block_table"]]), np.array([100]), 0.0)
+    return bool(np.allclose(out[0, 0], np.mean(expect), rtol=0, atol=1e-9))
+
+
+def dominant_key_token_99(decode):
+    """A dominant key at token 99 (block 3, row 3 on the page) picks its V row;
+    with 99 tokens it must not count."""
+    ex = page_example()
+    bs = ex["block_size"]
+    kv = np.random.default_rng(0).standard_normal((10, 2, 1, bs, 4)) * 0.01
+    kv[3, 0, 0, 3, :] = [100.0, 0, 0, 0]
+    kv[3, 1, 0, 3, :] = [7.0, -7.0, 3.0, 1.0]
+    q = np.array([[[1.0, 0, 0, 0]]])
+    a = decode(q, kv, np.array([ex["block_table"]]), np.array([100]), 1.0)
+    b = decode(q, kv, np.array([ex["block_table"]]), np.array([99]), 1.0)
+    return bool(np.allclose(a[0, 0], [7.0, -7.0, 3.0, 1.0], atol=1e-9)
+                and np.abs(b[0, 0]).max() < 0.1)
+
+
+def sdpa_on_contiguous(decode, seed=1, lens=(5, 64, 33), hq=8, hkv=2, d=16, bs=8):
+    """Agreement with torch SDPA on contiguous K/V scattered into a random pool."""
+    rng = np.random.default_rng(seed)
+    ks = [rng.standard_normal((n, hkv, d)) for n in lens]
+    vs = [rng.standard_normal((n, hkv, d)) for n in lens]
+    q = rng.standard_normal((len(lens), hq, d))
+    nbs = [-(-n // bs) for n in lens]
+    nb = sum(nbs) + 5
+    pool = rng.standard_normal((nb, 2, hkv, bs, d))
+    perm = rng.permutation(nb)
+    tables = np.full((len(lens), max(nbs)), -1, dtype=np.int64)
+    pos = 0
+    for s, (k, v) in enumerate(zip(ks, vs)):
+        for i in range(nbs[s]):
+            b = perm[pos]
+            pos += 1
+            tables[s, i] = b
+            rows = k[i * bs:(i + 1) * bs]
+            pool[b, 0, :, :rows.shape[0], :] = rows.transpose(1, 0, 2)
+            pool[b, 1, :, :rows.shape[0], :] = v[i * bs:(i + 1) * bs].transpose(1, 0, 2)
+    scale = 1.0 / math.sqrt(d)
+    out = decode(q, pool, tables, np.array(lens), scale)
+    for s in range(len(lens)):
+        kt = torch.from_numpy(ks[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vs[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[s])[:, None, :], kt, vt, scale=scale)[:, 0, :]
+        if not np.allclose(out[s], ref.numpy(), rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def single_token_exact(decode):
+    """n = 1 returns the V row exactly."""
+    rng = np.random.default_rng(5)
+    kv = rng.standard_normal((4, 2, 2, 8, 16))
+    q = rng.standard_normal((2, 4, 16))
+    bt = np.array([[2], [0]])
+    out = decode(q, kv, bt, np.array([1, 1]), 0.25)
+    return bool(np.array_equal(out[0, 3], kv[2, 1, 1, 0]) and np.array_equal(out[1, 0], kv[0, 1, 0, 0]))
+
+
+def rows_past_context_ignored(decode):
+    """NaN in every row no context covers changes nothing."""
+    rng = np.random.default_rng(6)
+    kv = rng.standard_normal((6, 2, 2, 8, 16))
+    q = rng.standard_normal((2, 2, 16))
+    bt = np.array([[4, 1], [3, -1]])
+    lens = np.array([11, 3])
+    a = decode(q, kv, bt, lens, 0.3)
+    kv2 = kv.copy()
+    kv2[4, :, :, :, :] = kv[4]
+    kv2[1, :, :, 3:, :] = np.nan
+    kv2[3, :, :, 3:, :] = np.nan
+    kv2[[0, 2, 5]] = np.nan
+    b = decode(q, kv2, bt, lens, 0.3)
+    return bool(np.array_equal(a, b))
+
+
+ALL = [scale_zero_page_example, dominant_key_token_99, sdpa_on_contiguous, single_token_exact,
+       rows_past_context_ignored]
+
+
+def failing(decode):
+    """Names of the pins `decode` fails (an exception counts as a failure)."""
+    bad = []
+    for pin in ALL:
+        try:
+            ok = pin(decode)
+        except Exception:
+            ok = False
+        if not ok:
+            bad.append(pin.__name__)
+    return bad
+
+
+# --------------------------------------------------------------------------
+# cache write pins
+# --------------------------------------------------------------------------
+def cache_round_trip(cache_write, gather):
+    """Rows written at the slots of the page's printed ranges read back, in
+    order, through the page's table; untouched rows stay."""
+    ex = page_example()
+    bs, n = ex["block_size"], ex["num_tokens"]
+    rng = np.random.default_rng(0)
+    pool = rng.standard_normal((10, 2, 3, bs, 8)).astype(np.float16)
+    key = rng.standard_normal((n, 3, 8)).astype(np.float16)
+    value = rng.standard_normal((n, 3, 8)).astype(np.float16)
+    slots = np.empty(n, dtype=np.int64)
+    for r in ex["ranges"]:
+        lo, hi = r["tokens"]
+        slots[lo:hi + 1] = r["physical"] * bs + np.arange(hi - lo + 1)
+    out = cache_write(pool, key, value, slots)
+    k, v = gather(out, np.array(ex["block_table"]), n)
+    return bool(np.array_equal(k, key) and np.array_equal(v, value)
+                and np.array_equal(out[3, :, :, 4:], pool[3, :, :, 4:])
+                and np.array_equal(out[0], pool[0]))
+
+
+def cow_before_scatter(cache_write):
+    rng = np.random.default_rng(1)
+    pool = rng.standard_normal((6, 2, 2, 8, 4)).astype(np.float16)
+    key = rng.standard_normal((1, 2, 4)).astype(np.float16)
+    value = rng.standard_normal((1, 2, 4)).astype(np.float16)
+    out = cache_write(pool, key, value, np.array([5 * 8 + 3]), cow_pairs=[(2, 5)])
+    expect = pool[2].copy()
+    expect[0, :, 3] = key[0]
+    expect[1, :, 3] = value[0]
+    return bool(np.array_equal(out[5], expect) and np.array_equal(out[2], pool[2]))
+
+
+# --------------------------------------------------------------------------
+# block-manager pins
+# --------------------------------------------------------------------------
+def invariants_hold(bm):
+    refs = [0] * bm.num_blocks
+    for seq, table in bm.tables.items():
+        if len(table) != -(-bm.num_tokens[seq] // bm.block_size):
+            return False
+        for b in table:
+            refs[b] += 1
+    free = set(bm.free_blocks)
+    held = {b for b in range(bm.num_blocks) if refs[b] > 0}
+    return (refs == list(bm.ref_counts) and len(free) == len(bm.free_blocks)
+            and free.isdisjoint(held) and free | held == set(range(bm.num_blocks)))
+
+
+def bm_fork_cow_example(model_cls):
+    """B forks from A (30 tokens, block 16); B's first write copies the shared
+    partial block, A keeps the original; freeing both restores the pool."""
+    bm = model_cls(8, 16)
+    bm.allocate("A", 30)
+    bm.fork("A", "B")
+    slot, src, dst = bm.append_slot("B")
+    ok = (src, dst) == (6, 5) and slot == 5 * 16 + 14 and bm.block_table("A") == ([7, 6], 30)
+    ok = ok and bm.append_slot("A") == (6 * 16 + 14, -1, -1) and invariants_hold(bm)
+    bm.free("A")
+    bm.free("B")
+    return bool(ok and sorted(bm.free_blocks) == list(range(8)) and list(bm.ref_counts) == [0] * 8)
+
+
+def bm_scripted_lifecycle(model_cls):
+    """A fixed lifecycle (allocate, share, fork, appends across block
+    boundaries and copies, frees) keeps every invariant after every step."""
+    bm = model_cls(12, 4)
+    steps = [lambda: bm.allocate(0, 6), lambda: bm.share(1, bm.block_table(0)[0][:1], 4),
+             lambda: bm.fork(0, 2), lambda: bm.append_slot(2), lambda: bm.append_slot(0),
+             lambda: bm.append_slot(1), lambda: bm.append_slot(2), lambda: bm.append_slot(2),
+             lambda: bm.free(0), lambda: bm.append_slot(1), lambda: bm.free(2),
+             lambda: bm.free(1)]
+    for st in steps:
+        st()
+        if not invariants_hold(bm):
+            return False
+    return sorted(bm.free_blocks) == list(range(12))

@@ -1,0 +1,144 @@
+"""The pins are strong enough: plant plausible mistakes in copies of the
+oracle (on the CPU) and check that at least one pin fails for each, while the
+real oracle passes them all."""
+
+import copy
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import BlockManagerError, BlockManagerModel
+from tests import pins
+
+
+def plain_decode(mistake=None):
+    """The decode definition with one planted mistake (None = correct)."""
+    def decode(q, kv, bt, cl, scale):
+        q = np.asarray(q, dtype=np.float64)
+        S, Hq, D = q.shape
+        Hkv, bs = kv.shape[2], kv.shape[3]
+        G = Hq // Hkv
+        out = np.zeros((S, Hq, D))
+        for s in range(S):
+            n = int(cl[s])
+            if mistake == "whole_last_block":
+                n = -(-n // bs) * bs
+            if n == 0:
+                continue
+            t = np.arange(n)
+            row = (t + 1) % bs if mistake == "row_off_by_one" else t % bs
+            blk = np.asarray(bt[s])[t // bs]
+            k = kv[blk, 0, :, row, :].astype(np.float64)
+            v = kv[blk, 1, :, row, :].astype(np.float64)
+            if mistake == "k_v_swapped":
+                k, v = v, k
+            for h in range(Hq):
+                g = h % Hkv if mistake == "gqa_modulo" else h // G
+                sc = 1.0 if mistake == "scale_dropped" else scale
+                z = sc * (k[:, g] @ q[s, h])
+                if mistake == "per_block_softmax":   # the block loop some pages print
+                    o = np.zeros(D)
+                    for b0 in range(0, n, bs):
+                        zz = z[b0:b0 + bs]
+                        w = np.exp(zz - zz.max())
+                        o += (w / w.sum()) @ v[b0:b0 + bs, g]
+                    out[s, h] = o
+                    continue
+                w = np.exp(z.max() - z) if mistake == "sign_flipped" else np.exp(z - z.max())
+                out[s, h] = (w @ v[:, g]) / w.sum()
+        return out
+    return decode
+
+
+DECODE_MISTAKES = ["whole_last_block", "row_off_by_one", "k_v_swapped", "gqa_modulo",
+                   "scale_dropped", "per_block_softmax", "sign_flipped"]
+
+
+def test_real_oracle_passes_every_decode_pin():
+    assert pins.failing(oracle.decode_ref) == []
+    assert pins.failing(plain_decode(None)) == []
+
+
+@pytest.mark.parametrize("mistake", DECODE_MISTAKES)
+def test_decode_pins_catch_planted_mistake(mistake):
+    assert pins.failing(plain_decode(mistake)), mistake
+
+
+def cache_write_mutant(mistake):
+    def write(kv, key, value, slots, cow_pairs=()):
+        out = np.array(kv, copy=True)
+        bs = out.shape[3]
+
+        def copies():
+            for src, dst in cow_pairs:
+                out[int(dst)] = out[int(src)]
+        if mistake != "copy_after_scatter":
+            copies()
+        for i, slot in enumerate(np.asarray(slots).tolist()):
+            if slot < 0:
+                continue
+            b, o = divmod(int(slot), bs)
+            if mistake == "row_from_block":
+                b, o = o % out.shape[0], b % bs
+            kk, vv = (value[i], key[i]) if mistake == "k_v_swapped" else (key[i], value[i])
+            out[b, 0, :, o, :] = kk
+            out[b, 1, :, o, :] = vv
+        if mistake == "copy_after_scatter":
+            copies()
+        return out
+    return write
+
+
+def test_real_cache_write_passes_its_pins():
+    assert pins.cache_round_trip(oracle.cache_write_ref, oracle.gather_sequence)
+    assert pins.cow_before_scatter(oracle.cache_write_ref)
+
+
+@pytest.mark.parametrize("mistake", ["row_from_block", "k_v_swapped", "copy_after_scatter"])
+def test_cache_pins_catch_planted_mistake(mistake):
+    w = cache_write_mutant(mistake)
+    assert not (pins.cache_round_trip(w, oracle.gather_sequence) and pins.cow_before_scatter(w))
+
+
+class ForkWithoutRefs(BlockManagerModel):
+    def fork(self, parent, child):
+        self._need(parent)
+        self.tables[child] = list(self.tables[parent])
+        self.num_tokens[child] = self.num_tokens[parent]
+
+
+class NoCopyOnWrite(BlockManagerModel):
+    def append_slot(self, seq):
+        self._need(seq)
+        table = self.tables[seq]
+        t = self.num_tokens[seq]
+        if t % self.block_size == 0:
+            table.append(self._take())
+        self.num_tokens[seq] = t + 1
+        return table[-1] * self.block_size + t % self.block_size, -1, -1
+
+
+class FreeIgnoresRefs(BlockManagerModel):
+    def free(self, seq):
+        self._need(seq)
+        for b in self.tables.pop(seq):
+            self.ref_counts[b] = 0
+            if b not in self.free_blocks:
+                self.free_blocks.append(b)
+        del self.num_tokens[seq]
+
+
+def test_real_block_manager_passes_its_pins():
+    assert pins.bm_fork_cow_example(BlockManagerModel)
+    assert pins.bm_scripted_lifecycle(BlockManagerModel)
+
+
+@pytest.mark.parametrize("cls", [ForkWithoutRefs, NoCopyOnWrite, FreeIgnoresRefs])
+def test_block_manager_pins_catch_planted_mistake(cls):
+    def passes(pin):
+        try:
+            return pin(cls)
+        except (BlockManagerError, KeyError, IndexError, AssertionError):
+            return False
+    assert not (passes(pins.bm_fork_cow_example) and passes(pins.bm_scripted_lifecycle))

@@ -32,6 +32,13 @@ Readings where the pages are silent or inconsistent
 * A sequence with context length 0 has output 0 (the pages' loop would end
   with 0/0).
 
+Sliding window
+--------------
+[KV2P] §7.2 lists sliding-window attention among the remedies for long
+contexts: each new token attends only to the last W tokens.  With
+``window = W > 0`` the keys are tokens ``t`` with ``max(0, n - W) <= t < n``;
+``window = 0`` means the whole context.
+
 Split-context partials
 ----------------------
 The pages merge block results with decay factors ([KVPA] §7.2 running max /
@@ -74,7 +81,7 @@ def _attend(qvec, keys, values, scale):
     return (w @ values) / w.sum()
 
 
-def decode_ref(q, kv_cache, block_tables, context_lens, scale):
+def decode_ref(q, kv_cache, block_tables, context_lens, scale, window=0):
     """Reference decode attention.
 
     q:             [S, Hq, D]  (any float dtype; upcast exactly to float64)
@@ -82,6 +89,7 @@ def decode_ref(q, kv_cache, block_tables, context_lens, scale):
     block_tables:  [S, max_blocks] integer, physical block ids
     context_lens:  [S] integer
     scale:         softmax scale (the pages use 1/sqrt(head_dim))
+    window:        0 = whole context; W > 0 = only the last W tokens
     returns        [S, Hq, D] float64
     """
     q = np.asarray(q)
@@ -96,8 +104,9 @@ def decode_ref(q, kv_cache, block_tables, context_lens, scale):
         if n == 0:
             continue
         k, v = gather_sequence(kv_cache, block_tables[s], n)
-        k = k.astype(np.float64)
-        v = v.astype(np.float64)
+        start = max(0, n - window) if window > 0 else 0
+        k = k[start:].astype(np.float64)
+        v = v[start:].astype(np.float64)
         for h in range(num_q_heads):
             g = h // group
             out[s, h] = _attend(q[s, h].astype(np.float64), k[:, g, :], v[:, g, :], scale)

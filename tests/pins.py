@@ -210,3 +210,50 @@ def bm_scripted_lifecycle(model_cls):
         if not invariants_hold(bm):
             return False
     return sorted(bm.free_blocks) == list(range(12))
+
+
+# --------------------------------------------------------------------------
+# sliding-window pins
+# --------------------------------------------------------------------------
+def window_is_sdpa_on_last_tokens(decode, window):
+    """With a window W, attention over the last W tokens only: SDPA on the
+    contiguous slice [n - W, n) of each sequence (whole context when n <= W)."""
+    rng = np.random.default_rng(21)
+    lens, hq, hkv, d, bs = (37, 5, 64, 100), 8, 2, 16, 8
+    ks = [rng.standard_normal((n, hkv, d)) for n in lens]
+    vs = [rng.standard_normal((n, hkv, d)) for n in lens]
+    q = rng.standard_normal((len(lens), hq, d))
+    nbs = [-(-n // bs) for n in lens]
+    pool = rng.standard_normal((sum(nbs) + 3, 2, hkv, bs, d))
+    tables = np.full((len(lens), max(nbs)), -1, dtype=np.int64)
+    perm = rng.permutation(pool.shape[0])
+    pos = 0
+    for s, (k, v) in enumerate(zip(ks, vs)):
+        for i in range(nbs[s]):
+            b = perm[pos]
+            pos += 1
+            tables[s, i] = b
+            r = k[i * bs:(i + 1) * bs]
+            pool[b, 0, :, :r.shape[0]] = r.transpose(1, 0, 2)
+            pool[b, 1, :, :r.shape[0]] = v[i * bs:(i + 1) * bs].transpose(1, 0, 2)
+    scale = 0.25
+    out = decode(q, pool, tables, np.array(lens), scale, window=window)
+    for s, n in enumerate(lens):
+        lo = max(0, n - window)
+        kt = torch.from_numpy(ks[s][lo:]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vs[s][lo:]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[s])[:, None, :], kt, vt, scale=scale)[:, 0, :]
+        if not np.allclose(out[s], ref.numpy(), rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def window_one_is_last_value(decode):
+    """W = 1: each head returns the V row of the newest token exactly."""
+    rng = np.random.default_rng(22)
+    kv = rng.standard_normal((5, 2, 2, 8, 16))
+    q = rng.standard_normal((2, 4, 16))
+    bt = np.array([[3, 1], [4, 0]])
+    out = decode(q, kv, bt, np.array([12, 8]), 0.5, window=1)
+    return bool(np.array_equal(out[0, 2], kv[1, 1, 1, 3]) and np.array_equal(out[1, 0], kv[4, 1, 0, 7]))

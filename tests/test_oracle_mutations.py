@@ -14,7 +14,7 @@ from tests import pins
 
 def plain_decode(mistake=None):
     """The decode definition with one planted mistake (None = correct)."""
-    def decode(q, kv, bt, cl, scale):
+    def decode(q, kv, bt, cl, scale, window=0):
         q = np.asarray(q, dtype=np.float64)
         S, Hq, D = q.shape
         Hkv, bs = kv.shape[2], kv.shape[3]
@@ -26,7 +26,10 @@ def plain_decode(mistake=None):
                 n = -(-n // bs) * bs
             if n == 0:
                 continue
-            t = np.arange(n)
+            lo = max(0, n - window) if window > 0 else 0
+            if mistake == "window_off_by_one" and window > 0:
+                lo = max(0, n - window - 1)
+            t = np.arange(lo, n)
             row = (t + 1) % bs if mistake == "row_off_by_one" else t % bs
             blk = np.asarray(bt[s])[t // bs]
             k = kv[blk, 0, :, row, :].astype(np.float64)
@@ -39,7 +42,7 @@ def plain_decode(mistake=None):
                 z = sc * (k[:, g] @ q[s, h])
                 if mistake == "per_block_softmax":   # the block loop some pages print
                     o = np.zeros(D)
-                    for b0 in range(0, n, bs):
+                    for b0 in range(0, len(t), bs):
                         zz = z[b0:b0 + bs]
                         w = np.exp(zz - zz.max())
                         o += (w / w.sum()) @ v[b0:b0 + bs, g]
@@ -53,6 +56,17 @@ def plain_decode(mistake=None):
 
 DECODE_MISTAKES = ["whole_last_block", "row_off_by_one", "k_v_swapped", "gqa_modulo",
                    "scale_dropped", "per_block_softmax", "sign_flipped"]
+
+
+def window_pins_fail(decode):
+    ok = all(pins.window_is_sdpa_on_last_tokens(decode, w) for w in (1, 7, 33))
+    return not (ok and pins.window_one_is_last_value(decode))
+
+
+def test_window_pins_catch_off_by_one_and_pass_the_oracle():
+    assert not window_pins_fail(oracle.decode_ref)
+    assert not window_pins_fail(plain_decode(None))
+    assert window_pins_fail(plain_decode("window_off_by_one"))
 
 
 def test_real_oracle_passes_every_decode_pin():

@@ -273,3 +273,26 @@ def test_merge_of_one_partition_is_identity_and_empty_is_zero():
     l[1, 2, 0] = 0
     m[1, 2, 0] = -np.inf
     assert np.all(oracle.merge_ref(m, l, o)[1, 2] == 0)
+
+
+# --------------------------------------------------------------------------
+# sliding window ([KV2P] §7.2)
+# --------------------------------------------------------------------------
+from tests import pins as _pins
+
+
+@pytest.mark.parametrize("window", [1, 7, 16, 33, 64, 1000])
+def test_window_equals_sdpa_on_last_tokens(window):
+    assert _pins.window_is_sdpa_on_last_tokens(oracle.decode_ref, window)
+
+
+def test_window_one_returns_newest_value_row():
+    assert _pins.window_one_is_last_value(oracle.decode_ref)
+
+
+def test_window_larger_than_context_is_full_attention():
+    x = synth.make_decode_inputs([20, 300], 4, 2, 16, 16, dtype="f32", seed=23)
+    args = (x.q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(), x.context_lens.numpy(),
+            x.scale)
+    assert np.array_equal(oracle.decode_ref(*args, window=300), oracle.decode_ref(*args))
+    assert not np.allclose(oracle.decode_ref(*args, window=299), oracle.decode_ref(*args))

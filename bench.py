@@ -101,7 +101,8 @@ def measured_traffic(workload):
 class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
-    def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0):
+    def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
+                 window=0):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -110,6 +111,7 @@ class Step:
         if name == "shared_prefix":
             w["bs"] = bs
         self.w, self.name, self.kernel, self.partition = w, name, kernel, partition
+        self.window = window
         # a pool whose prefix blocks every sequence shares is read with cached
         # loads (the block manager knows it shares); streaming loads otherwise
         self.cached_kv = name == "shared_prefix"
@@ -225,11 +227,18 @@ class Step:
             self.bm.fork(parent, child)
         ncow = self.bm.append_slots_into(self.seqs, buf["slots"], buf["pairs"])
         self.bm.block_tables_into(self.seqs, buf["tables"], buf["lens"])
-        tokens = int(buf["lens"].sum())
+        tokens = self.key_tokens(buf["lens"])
         self.ctx_tokens.append(tokens)
         self.kv_bytes.append(tokens * 2 * self.Hkv * self.D * self.elem)
         self.ncow.append(ncow)
         return ncow
+
+    def key_tokens(self, lens):
+        """Tokens the decode attends to: the whole context, or at most the
+        last ``window`` tokens of each sequence."""
+        if self.window > 0:
+            return int(lens.clamp(max=self.window).sum())
+        return int(lens.sum())
 
     def run(self, timed_events=None):
         torch, pa = self.torch, self.pa
@@ -245,7 +254,8 @@ class Step:
             timed_events[0].record()
         pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
                   max_context_len=maxlen, partition_size=self.partition, kernel=self.kernel,
-                  out=self.out, workspace=self.ws, cached_kv=self.cached_kv)
+                  out=self.out, workspace=self.ws, cached_kv=self.cached_kv,
+                  sliding_window=self.window)
         if timed_events is not None:
             timed_events[1].record()
         self.k += 1
@@ -279,20 +289,22 @@ def cpu_baseline(st, budget_s=10.0, cap_s=30.0):
     """Time the fp64 oracle (1 thread) on the last step's sequences, cycling
     through them until about ``budget_s`` of CPU time has been spent."""
     from threadpoolctl import threadpool_limits
+    import numpy as np
     import oracle
     runs, t_used, nbytes, toks = 0, 0.0, 0, 0
     with threadpool_limits(1):
         while (runs < st.S and t_used < cap_s) or t_used < budget_s:
             q, pool, bt, lens, _ = st.host_inputs([runs % st.S])
             t0 = time.perf_counter()
-            oracle.decode_ref(q, pool, bt, lens, st.scale)
+            oracle.decode_ref(q, pool, bt, lens, st.scale, window=st.window)
             t_used += time.perf_counter() - t0
-            nbytes += int(lens.sum()) * 2 * st.Hkv * st.D * st.elem
-            toks += int(lens.sum())
+            keys = int(np.minimum(lens, st.window).sum()) if st.window > 0 else int(lens.sum())
+            nbytes += keys * 2 * st.Hkv * st.D * st.elem
+            toks += keys
             runs += 1
     return dict(value=round(nbytes / t_used / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample=f"fp64 NumPy oracle, 1 thread, {runs} sequence decodes taken in turn "
-                       f"from the {st.S} sequences of the last timed step ({toks} context "
+                       f"from the {st.S} sequences of the last timed step ({toks} key "
                        f"tokens, {nbytes} KV bytes) in {t_used:.2f} s; "
                        f"{toks / t_used:.4g} seq*ctx tokens/s")
 
@@ -365,7 +377,7 @@ def parity_sample(st, samples=3):
     import oracle
     picks = sorted({0, st.S - 1, st.S // 2})[:samples]
     q, pool, bt, lens, pos = st.host_inputs(picks)
-    want = oracle.decode_ref(q, pool, bt, lens, st.scale)
+    want = oracle.decode_ref(q, pool, bt, lens, st.scale, window=st.window)
     got = st.out[pos].cpu().numpy().astype(np.float64)
     return float(np.abs(got - want).max())
 
@@ -384,6 +396,8 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--context", type=int, default=0,
                     help="override: every sequence at this context length (not shared_prefix)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured HBM read ceiling (libpa_probe.so)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -406,7 +420,7 @@ def main():
         print(json.dumps(calibrate_copy(dev)), flush=True)
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
-              args.partition, dev, context=args.context)
+              args.partition, dev, context=args.context, window=args.window)
     step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -455,9 +469,10 @@ def main():
             "workload": w["desc"] + (f" (block {st.bs})" if args.workload == "shared_prefix" else ""),
             "num_seqs": st.S, "num_q_heads": st.Hq, "num_kv_heads": st.Hkv, "head_dim": st.D,
             "block_size": st.bs, "pool_blocks": st.num_blocks,
-            "mean_context": round(total_tokens / args.steps / st.S, 1),
+            "mean_key_tokens": round(total_tokens / args.steps / st.S, 1),
             "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
             "context_override": args.context or None,
+            "sliding_window": args.window or None,
             "kv_loads": "cached" if st.cached_kv else "streaming (non-temporal)",
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
@@ -476,8 +491,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload)
-            if (args.kernel, args.partition) == ("auto", 0) else None,
+            "traffic": measured_traffic(args.workload + (f"_w{args.window}" if args.window
+                                                         else ""))
+            if (args.kernel, args.partition, args.context) == ("auto", 0, 0) else None,
         },
         "cpu_baseline": cpu,
     }

@@ -108,6 +108,9 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  * where token t is row t%block_size of physical block
  * block_tables[s, t/block_size]; K_t = kv_cache[b,0,g,row,:],
  * V_t = kv_cache[b,1,g,row,:].  Rows past n are never read; n == 0 gives 0.
+ * With sliding_window = W > 0 only the last W tokens are keys:
+ * max(0, n - W) <= t < n ([KV2P] §7.2, sliding-window attention); the
+ * tiles before the window are not read.
  * Accumulation is float32; the output is float32.
  *
  *   out            device, [num_seqs, num_q_heads, head_dim] float32
@@ -119,6 +122,8 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  *                  n <= max_blocks_per_seq * block_size
  *   max_context_len host bound on context_lens (sizes the partition grid)
  *   scale          softmax scale, normally 1/sqrt(head_dim)
+ *   sliding_window 0 = attend to the whole context; W > 0 = the last W
+ *                  tokens; < 0 is PA_ERR_INVALID_ARG
  *   partition_size 0 = choose; -1 = single pass (one workgroup per (s, KV
  *                  head)); -2 = balanced: one grid of as many workgroups as
  *                  fit on the GPU at once, each taking an equal slice of all
@@ -139,9 +144,10 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
               const int32_t* block_tables, const int32_t* context_lens,
               int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
               int block_size, int max_blocks_per_seq, int max_context_len,
-              int64_t num_blocks, float scale, int partition_size, int kernel,
-              void* workspace, size_t workspace_bytes, size_t* workspace_needed,
-              int dtype, void* stream);
+              int64_t num_blocks, float scale, int sliding_window,
+              int partition_size, int kernel, void* workspace,
+              size_t workspace_bytes, size_t* workspace_needed, int dtype,
+              void* stream);
 
 /* -------------------------------------------------------------------------
  * 3. Host block manager ([KVPA] §5.1-§5.3, §8.2; [KV2P] §6.2; [NANO] §2.3,

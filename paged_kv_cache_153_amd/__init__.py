@@ -56,7 +56,8 @@ _SIGNATURES = {
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P]),
     "pa_decode": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                              _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float, _c.c_int,
-                             _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t), _c.c_int, _P]),
+                             _c.c_int, _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t),
+                             _c.c_int, _P]),
     "pa_bm_create": (_P, [_c.c_int64, _c.c_int]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_allocate": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
@@ -158,19 +159,19 @@ def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None)
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                           max_blocks_per_seq, max_context_len, partition_size=0,
-                          dtype=F16, kernel="auto"):
+                          dtype=F16, kernel="auto", sliding_window=0):
     """Bytes of split-context workspace ``decode`` needs for this shape."""
     need = ctypes.c_size_t(0)
     _check(lib().pa_decode(None, None, None, None, None, num_seqs, num_q_heads, num_kv_heads,
                            head_dim, block_size, max_blocks_per_seq, max_context_len, 1, 1.0,
-                           partition_size, KERNELS[kernel], None, 0, ctypes.byref(need), dtype,
-                           None))
+                           int(sliding_window), partition_size, KERNELS[kernel], None, 0,
+                           ctypes.byref(need), dtype, None))
     return need.value
 
 
 def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_len=None,
            partition_size=0, kernel="auto", out=None, workspace=None, stream=None,
-           cached_kv=False):
+           cached_kv=False, sliding_window=0):
     """Paged decode attention.
 
     query [S, Hq, D] (kv dtype), kv_cache [NB, 2, Hkv, bs, D], block_tables
@@ -179,6 +180,8 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     (default MB * bs); ``partition_size`` 0 = auto, -1 = single pass.
     ``cached_kv``: read K/V with cached loads (for pools whose blocks many
     sequences share); default streams them with non-temporal loads.
+    ``sliding_window`` W > 0: each query attends to its sequence's last W
+    tokens only; 0 = the whole context.
     """
     torch = _torch()
     _need_cuda(query, kv_cache, block_tables, context_lens, out, workspace)
@@ -199,7 +202,7 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
         scale = d ** -0.5
     dt = _dtype_code(kv_cache)
     need = decode_workspace_size(s, hq, hkv, d, bs, mb, int(max_context_len), partition_size,
-                                 dt, kernel)
+                                 dt, kernel, sliding_window)
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=query.device)
     elif out.dtype != torch.float32 or out.shape != (s, hq, d):
@@ -209,7 +212,8 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_decode(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
                            block_tables.data_ptr(), context_lens.data_ptr(), s, hq, hkv, d, bs,
-                           mb, int(max_context_len), nb, float(scale), int(partition_size),
+                           mb, int(max_context_len), nb, float(scale), int(sliding_window),
+                           int(partition_size),
                            KERNELS[kernel] | (KV_CACHED if cached_kv else 0),
                            None if workspace is None else workspace.data_ptr(),
                            wbytes, None, dt, _stream(query.device, stream)))

@@ -58,8 +58,8 @@ struct VRow<64> {
 // per wave in flight and twice the waves per SIMD to hide the latency.
 template <int D, int BS, int G, int NW, int DEPTH, bool NT>
 __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, int s,
-                                             int g, int n, int tile_begin, int tile_end,
-                                             const Sink& sink) {
+                                             int g, int lo, int n, int tile_begin,
+                                             int tile_end, const Sink& sink) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
   constexpr int KS = D / 32;                 // 16x16x32 steps for q.K
@@ -172,10 +172,11 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = sc[i] * cs;
-    if ((tile + 1) * kTile > n) {  // partial tile: rows at or past n
+    if ((tile + 1) * kTile > n || tile * kTile < lo) {  // partial tile: non-keys
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (tile * kTile + 4 * quad + i >= n) {
+        const int tok = tile * kTile + 4 * quad + i;
+        if (tok >= n || tok < lo) {
           y[i] = -INFINITY;
           vr[i] = VRow<D>::zero();
         }
@@ -275,8 +276,9 @@ template <int D, int BS, int G, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G, D, NW> sm;
   __shared__ int prefix[kBalancedMaxSeqs];
-  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int n, int ta, int tb, const Sink& sink) {
-    decode_range<D, BS, G, NW, DEPTH, NT>(a, sm, s, g, n, ta, tb, sink);
+  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int lo, int n, int ta, int tb,
+                                         const Sink& sink) {
+    decode_range<D, BS, G, NW, DEPTH, NT>(a, sm, s, g, lo, n, ta, tb, sink);
   });
 }
 

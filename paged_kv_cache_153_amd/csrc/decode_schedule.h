@@ -16,10 +16,12 @@
 //               removes the tail that ragged batches leave with the other
 //               schedules.
 //
-// The decode and the merge kernels derive the slices from the context
-// lengths with the same integer arithmetic (tiles(s) = ceil(n_s / 16), n_s
-// clamped exactly as the decode clamps it), so they agree on every boundary
-// without exchanging anything.
+// A sequence's work is the tile span that holds its keys: tiles
+// [t0, t0 + nt) with t0 = floor(lo / 16) and t0 + nt = ceil(n / 16), where
+// lo is the first key (0, or n - W under a sliding window of W tokens).  The
+// decode and the merge kernels derive spans, partitions and slices from the
+// context lengths with the same integer arithmetic (seq_span), so they agree
+// on every boundary without exchanging anything.
 #pragma once
 
 #include "decode_epilogue.h"
@@ -36,7 +38,28 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
 
 __device__ __forceinline__ int tiles_of(int n) { return (n + kTile - 1) / kTile; }
 
-// Fills prefix[s] = sum_{s' <= s} tiles(s') for s < S (per KV head) with the
+// Keys of one sequence: tokens [lo, n); the tiles [t0, t0 + nt) cover them.
+struct Span {
+  int lo;
+  int n;
+  int t0;
+  int nt;
+};
+
+// The span is also cut to the tiles the launch covers (num_parts partitions
+// of part_tokens; a context longer than the caller's bound loses its last
+// tiles rather than reading past what the grid and the workspace hold).
+__device__ __forceinline__ Span seq_span(const DecodeArgs& a, int s) {
+  Span sp;
+  sp.n = clamp_len(a, s);
+  sp.lo = (a.window > 0 && sp.n > a.window) ? sp.n - a.window : 0;
+  sp.t0 = sp.lo / kTile;
+  const int covered = a.num_parts * (a.part_tokens / kTile);
+  sp.nt = sp.n > 0 ? min(tiles_of(sp.n) - sp.t0, covered) : 0;
+  return sp;
+}
+
+// Fills prefix[s] = sum_{s' <= s} nt(s') for s < S (per KV head) with the
 // whole workgroup; every thread sees the result after the final barrier.
 // Scans in chunks of blockDim.x with a running carry.
 __device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
@@ -44,7 +67,7 @@ __device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += nt) {
     const int s = base + (int)threadIdx.x;
-    if (s < a.num_seqs) prefix[s] = tiles_of(clamp_len(a, s));
+    if (s < a.num_seqs) prefix[s] = seq_span(a, s).nt;
     __syncthreads();
     for (int off = 1; off < nt; off <<= 1) {  // inclusive Hillis-Steele scan
       int v = 0;
@@ -83,8 +106,9 @@ __device__ __forceinline__ int64_t balanced_chunk(int64_t total, int workgroups)
 namespace pa {
 
 // Maps this workgroup to its range(s) and calls
-// range(s, g, n, tile_begin, tile_end, sink) for each; ranges are processed
-// one after another by the whole workgroup (sm is reused in between).
+// range(s, g, lo, n, tile_begin, tile_end, sink) for each (absolute tile
+// indices; keys are tokens [lo, n)); ranges are processed one after another
+// by the whole workgroup (sm is reused in between).
 template <int G, int D, int NW, typename RangeFn>
 __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) {
   if (a.schedule == kScheduleBalanced) {
@@ -111,7 +135,8 @@ __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) 
         const size_t slot = 2 * (size_t)blockIdx.x + (first ? 0 : 1);
         sink = Sink{a.ws_o + slot * G * D, a.ws_m + slot * G, a.ws_l + slot * G, D, 1};
       }
-      range(s, g, clamp_len(a, s), ta, tb, sink);
+      const Span sp = seq_span(a, s);
+      range(s, g, sp.lo, sp.n, sp.t0 + ta, sp.t0 + tb, sink);
       __syncthreads();
       t = seg0 + tb;
       first = false;
@@ -123,15 +148,15 @@ __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) 
   bid /= a.num_kv_heads;
   const int p = bid % a.num_parts;
   const int s = bid / a.num_parts;
-  int n = clamp_len(a, s);
-  n = min(n, a.num_parts * a.part_tokens);  // the grid covers no more
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= n) {
+  const Span sp = seq_span(a, s);
+  const int pt = a.part_tokens / kTile;  // tiles per partition
+  const int t_begin = p * pt;            // relative to the span
+  if (t_begin >= sp.nt) {
     if (p == 0) write_zero_output<G, D, NW>(a, s, g);  // empty sequence
     return;
   }
-  const int t_end = min(n, t_begin + a.part_tokens);
-  const int np = (n + a.part_tokens - 1) / a.part_tokens;
+  const int t_end = min(sp.nt, t_begin + pt);
+  const int np = (sp.nt + pt - 1) / pt;
   Sink sink;
   if (a.schedule == kScheduleSingle || np == 1) {
     sink = output_sink<G, D>(a, s, g);
@@ -140,7 +165,7 @@ __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) 
     sink = Sink{a.ws_o + (row0 * a.num_parts + p) * D, a.ws_m + row0 * a.num_parts + p,
                 a.ws_l + row0 * a.num_parts + p, (long)a.num_parts * D, a.num_parts};
   }
-  range(s, g, n, t_begin / kTile, (t_end + kTile - 1) / kTile, sink);
+  range(s, g, sp.lo, sp.n, sp.t0 + t_begin, sp.t0 + t_end, sink);
 }
 
 }  // namespace pa

@@ -29,9 +29,10 @@
 //    tile (one vector load per 64 tiles); readlane moves it to an SGPR, so
 //    the K/V address is an SGPR base plus a per-lane offset.
 //  * Every block id read from the table is clamped into [0, NB), and rows at
-//    or past the context length are masked (score -inf, V zeroed), so the
-//    kernel never reads outside the pool and never lets unused rows — even
-//    NaN ones — reach the output.
+//    or past the context length — or before a sliding window's first key
+//    ([KV2P] §7.2) — are masked (score -inf, V zeroed), so the kernel never
+//    reads outside the pool and never lets unused rows — even NaN ones —
+//    reach the output.
 #include "device_common.h"
 #include "decode_epilogue.h"
 #include "decode_schedule.h"
@@ -41,11 +42,11 @@ namespace pa {
 namespace {
 
 // One range: tiles [tile_begin, tile_end) of (sequence s, KV head g), whose
-// context holds n tokens; the result goes to `sink`.
+// keys are tokens [lo, n); the result goes to `sink`.
 template <typename T, int D, int BS, int G, int NW, bool NT>
 __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, D, NW>& sm, int s,
-                                             int g, int n, int tile_begin, int tile_end,
-                                             const Sink& sink) {
+                                             int g, int lo, int n, int tile_begin,
+                                             int tile_end, const Sink& sink) {
   constexpr int E = DType<T>::kBytes;
   constexpr int EPL = 16 / E;        // elements per 16-byte chunk
   constexpr int LPT = D / EPL;       // lanes per token row
@@ -149,11 +150,11 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
         y[i][h] = group_sum<LPT>(d) * cs;
       }
     }
-    if ((tile + 1) * kTile > n) {  // partial tile: mask rows at or past n
+    if ((tile + 1) * kTile > n || tile * kTile < lo) {  // partial tile: mask non-keys
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int tok = tile * kTile + i * RPI + r;
-        if (tok >= n) {
+        if (tok >= n || tok < lo) {
 #pragma unroll
           for (int h = 0; h < G; ++h) y[i][h] = -INFINITY;
           vr[i] = u32x4_t{0u, 0u, 0u, 0u};
@@ -250,8 +251,9 @@ template <typename T, int D, int BS, int G, int NW, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G, D, NW> sm;
   __shared__ int prefix[kBalancedMaxSeqs];
-  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int n, int ta, int tb, const Sink& sink) {
-    decode_range<T, D, BS, G, NW, NT>(a, sm, s, g, n, ta, tb, sink);
+  run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int lo, int n, int ta, int tb,
+                                         const Sink& sink) {
+    decode_range<T, D, BS, G, NW, NT>(a, sm, s, g, lo, n, ta, tb, sink);
   });
 }
 

@@ -41,6 +41,7 @@ struct DecodeArgs {
   float scale_log2;         // scale * log2(e)
   int variant;              // MFMA: 1 = one tile in flight per wave, 0 = two
   int cached_kv;            // 1: plain K/V loads; 0: non-temporal (streaming) loads
+  int window;               // > 0: attend to the last `window` tokens only; 0: all
 };
 
 // Each returns 0 on success, 1 if the (dtype, D, BS, G) combination has no

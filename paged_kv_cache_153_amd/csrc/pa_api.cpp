@@ -246,8 +246,9 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
 int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t* block_tables,
               const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
               int head_dim, int block_size, int max_blocks_per_seq, int max_context_len,
-              int64_t num_blocks, float scale, int partition_size, int kernel, void* workspace,
-              size_t workspace_bytes, size_t* workspace_needed, int dtype, void* stream_) {
+              int64_t num_blocks, float scale, int sliding_window, int partition_size, int kernel,
+              void* workspace, size_t workspace_bytes, size_t* workspace_needed, int dtype,
+              void* stream_) {
   pa::clear_error();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   if (workspace_needed) *workspace_needed = 0;
@@ -256,6 +257,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
       block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes out of range");
   if (num_q_heads % num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_q_heads % num_kv_heads");
+  if (sliding_window < 0) return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0");
   const int group = num_q_heads / num_kv_heads;
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim");
   if (block_size != 8 && block_size != 16 && block_size != 32)
@@ -275,7 +277,14 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
   if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   const int max_tokens = (int)max_tokens_ll;
-  const int ctx = max_context_len < max_tokens ? max_context_len : max_tokens;
+  int ctx = max_context_len < max_tokens ? max_context_len : max_tokens;
+  // under a sliding window of W tokens a sequence's keys lie in at most
+  // ceil(W/16) + 1 tiles: partitions and the schedule are sized for that span
+  if (sliding_window > 0) {
+    const long long span = ((long long)sliding_window + pa::kTile - 1) / pa::kTile * pa::kTile +
+                           pa::kTile;
+    if (span < ctx) ctx = (int)span;
+  }
   int part = partition_size;
   if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx, cached_kv);
   // the balanced schedule keeps an int32 tile prefix of all sequences in LDS
@@ -336,6 +345,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
     if (forced == 0 || forced == 1) a.variant = forced;
   }
   a.cached_kv = cached_kv;
+  a.window = sliding_window;
 
   int use = kernel;
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);

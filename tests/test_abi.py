@@ -50,13 +50,14 @@ def test_strerror_and_version():
 
 def _decode_status(**kw):
     args = dict(out=None, query=None, kv=None, bt=None, cl=None, S=2, Hq=8, Hkv=2, D=128, bs=16,
-                MB=4, maxlen=64, NB=16, scale=0.1, part=0, kernel=0, ws=None, wsb=0, need=None,
-                dtype=1)
+                MB=4, maxlen=64, NB=16, scale=0.1, window=0, part=0, kernel=0, ws=None, wsb=0,
+                need=None, dtype=1)
     args.update(kw)
     need = args["need"]
     return pa.lib().pa_decode(args["out"], args["query"], args["kv"], args["bt"], args["cl"],
                               args["S"], args["Hq"], args["Hkv"], args["D"], args["bs"],
-                              args["MB"], args["maxlen"], args["NB"], args["scale"], args["part"],
+                              args["MB"], args["maxlen"], args["NB"], args["scale"],
+                              args["window"], args["part"],
                               args["kernel"], args["ws"], args["wsb"],
                               ctypes.byref(need) if need is not None else None, args["dtype"],
                               None)
@@ -67,6 +68,7 @@ def _decode_status(**kw):
     (dict(dtype=5), -2), (dict(kernel=2, dtype=0), -2), (dict(kernel=2, Hq=2), -2),
     (dict(part=24), -1), (dict(part=8, bs=16), -1), (dict(part=-3), -1), (dict(MB=0), -1),
     (dict(kernel=7), -1), (dict(NB=0), -1), (dict(kernel=0x200), -1), (dict(kernel=0x103), -1),
+    (dict(window=-1), -1),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert _decode_status(**kw) == status
@@ -92,6 +94,13 @@ def test_workspace_size_closed_form():
     got = pa.decode_workspace_size(s, hq, 8, d, 16, 2048, maxlen, part)
     assert got == want
     assert pa.decode_workspace_size(s, hq, 8, d, 16, 2048, maxlen, -1) == 0
+    # a sliding window of W tokens needs partitions over ceil(W/16)*16 + 16 tokens only
+    for w, span in [(4096, 4112), (1000, 1024), (1, 32)]:
+        np_ = -(-span // part)
+        rows = s * hq * np_
+        want = rnd(rows * d * 4) + 2 * rnd(rows * 4)
+        assert pa.decode_workspace_size(s, hq, 8, d, 16, 2048, maxlen, part,
+                                        sliding_window=w) == want
 
 
 def test_cache_write_rejects_bad_arguments():

@@ -45,11 +45,21 @@ bool check_mode() {
 //  * otherwise the balanced schedule (-2): equal tile slices per workgroup
 //    whatever the length mix (it needs S <= kBalancedMaxSeqs);
 //  * fixed partitions are 512 tokens up to 4K contexts, 1024 up to 16K and
-//    2048 beyond.
-int choose_partition(int num_seqs, int num_kv_heads, int max_context_len, int cached_kv) {
+//    2048 beyond;
+//  * under a sliding window that shortens the longest context, fixed
+//    partitions of about a quarter of the window's span (256 to 2048).
+int choose_partition(int num_seqs, int num_kv_heads, int max_context_len, int cached_kv,
+                     bool windowed) {
   const long pairs = (long)num_seqs * num_kv_heads;
   if (max_context_len <= 512) return -1;
   if (pairs >= 1024 && max_context_len <= 8192) return -1;
+  if (windowed) {
+    // spans cut by a window are nearly equal: about four fixed partitions
+    // per span (no straddling slices) measured faster than balanced slices
+    int p = 256;
+    while (p < 2048 && 2 * p <= max_context_len / 4) p *= 2;
+    return p;
+  }
   if (!cached_kv && num_seqs <= kBalancedMaxSeqs) return -2;
   if (max_context_len <= 4096) return 512;
   if (max_context_len <= 16384) return 1024;
@@ -280,13 +290,17 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   int ctx = max_context_len < max_tokens ? max_context_len : max_tokens;
   // under a sliding window of W tokens a sequence's keys lie in at most
   // ceil(W/16) + 1 tiles: partitions and the schedule are sized for that span
+  bool windowed = false;
   if (sliding_window > 0) {
     const long long span = ((long long)sliding_window + pa::kTile - 1) / pa::kTile * pa::kTile +
                            pa::kTile;
-    if (span < ctx) ctx = (int)span;
+    if (span < ctx) {
+      ctx = (int)span;
+      windowed = true;
+    }
   }
   int part = partition_size;
-  if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx, cached_kv);
+  if (part == 0) part = pa::choose_partition(num_seqs, num_kv_heads, ctx, cached_kv, windowed);
   // the balanced schedule keeps an int32 tile prefix of all sequences in LDS
   if (part == -2 && (num_seqs > pa::kBalancedMaxSeqs ||
                      (long long)num_seqs * ((max_tokens + pa::kTile - 1) / pa::kTile) >= (1LL << 31)))

@@ -257,3 +257,145 @@ def window_one_is_last_value(decode):
     bt = np.array([[3, 1], [4, 0]])
     out = decode(q, kv, bt, np.array([12, 8]), 0.5, window=1)
     return bool(np.array_equal(out[0, 2], kv[1, 1, 1, 3]) and np.array_equal(out[1, 0], kv[4, 1, 0, 7]))
+
+
+# --------------------------------------------------------------------------
+# INT8 group-wise quantisation pins ([KV2P] §5.2)
+# --------------------------------------------------------------------------
+def quant_integers_exact(quantize):
+    """A row of integers whose largest magnitude is 127 has scale exactly 1,
+    so its codes are the integers themselves."""
+    row = np.array([127, -3, 0, 45, -127, 1, 99, -64], dtype=np.float16)
+    codes, scales = quantize(row[None])
+    return bool(scales[0] == np.float32(1.0) and np.array_equal(codes[0], row.astype(np.int8)))
+
+
+def quant_rounds_half_to_even(quantize):
+    """At scale 1 the ties x.5 go to the even neighbour."""
+    row = np.array([127, 2.5, -2.5, 3.5, 0.5, -0.5, 1.5, -1.5], dtype=np.float16)
+    codes, _ = quantize(row[None])
+    return bool(np.array_equal(codes[0], np.array([127, 2, -2, 4, 0, 0, 2, -2], dtype=np.int8)))
+
+
+def quant_scale_is_amax_over_127(quantize):
+    """scale * 127 equals the row's largest magnitude to float32 rounding, and
+    that element's code is +-127; a zero row has scale 0 and codes 0."""
+    rng = np.random.default_rng(5)
+    rows = (rng.standard_normal((64, 128)) * rng.uniform(0.01, 50, (64, 1))).astype(np.float16)
+    rows[7] = 0
+    codes, scales = quantize(rows)
+    amax = np.abs(rows.astype(np.float64)).max(axis=1)
+    ok = np.all(np.abs(scales.astype(np.float64) * 127 - amax) <= amax * 2.0 ** -22)
+    arg = np.abs(rows.astype(np.float64)).argmax(axis=1)
+    live = amax > 0
+    ok &= np.all(np.abs(codes[np.arange(64), arg][live].astype(int)) == 127)
+    ok &= scales[7] == 0 and not codes[7].any()
+    return bool(ok)
+
+
+def quant_error_within_half_step(quantize, dequantize):
+    """Every dequantised value is within half a step of its input, and the
+    steps are per row: an outlier in one row leaves the others' steps alone."""
+    rng = np.random.default_rng(6)
+    rows = rng.standard_normal((32, 64)).astype(np.float16)
+    rows[3, 10] = 900.0
+    codes, scales = quantize(rows)
+    back = dequantize(codes, scales)
+    err = np.abs(back - rows.astype(np.float64))
+    bound = scales.astype(np.float64)[:, None] * (0.5 + 2.0 ** -20)
+    amax = np.abs(rows.astype(np.float64)).max(axis=1)
+    return bool(np.all(err <= bound) and np.all(scales[np.arange(32) != 3] < 0.05)
+                and abs(scales[3] * 127 - 900) < 1e-3
+                and np.all(np.abs(back) <= amax[:, None] * (1 + 2.0 ** -22)))
+
+
+QUANT_PINS = [quant_integers_exact, quant_rounds_half_to_even, quant_scale_is_amax_over_127]
+
+
+def quant_failing(quantize, dequantize):
+    bad = [p.__name__ for p in QUANT_PINS if not p(quantize)]
+    if not quant_error_within_half_step(quantize, dequantize):
+        bad.append("quant_error_within_half_step")
+    return bad
+
+
+def i8_cache_round_trip(cache_write_i8, quantize, dequantize):
+    """Rows written at the slots of the page's printed ranges come back, through
+    the page's table, as their own quantisation (codes and per-row scales in
+    [block, K|V, head, row]); untouched rows and scales stay."""
+    ex = page_example()
+    bs, n = ex["block_size"], ex["num_tokens"]
+    rng = np.random.default_rng(2)
+    hkv, d = 3, 16
+    codes = rng.integers(-127, 128, (10, 2, hkv, bs, d)).astype(np.int8)
+    scales = rng.uniform(0.1, 1, (10, 2, hkv, bs)).astype(np.float32)
+    key = (rng.standard_normal((n, hkv, d)) * 3).astype(np.float16)
+    value = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    slots = np.empty(n, dtype=np.int64)
+    for r in ex["ranges"]:
+        lo, hi = r["tokens"]
+        slots[lo:hi + 1] = r["physical"] * bs + np.arange(hi - lo + 1)
+    c2, s2 = cache_write_i8(codes, scales, key, value, slots)
+    kq, ks = quantize(key)
+    vq, vs = quantize(value)
+    table = ex["block_table"]
+    ok = True
+    for t in range(n):
+        b, r = table[t // bs], t % bs
+        ok &= np.array_equal(c2[b, 0, :, r], kq[t]) and np.array_equal(c2[b, 1, :, r], vq[t])
+        ok &= np.array_equal(s2[b, 0, :, r], ks[t]) and np.array_equal(s2[b, 1, :, r], vs[t])
+    # block 3 holds tokens 96..99 in rows 0..3 only; blocks 0 and 4 are not in the table
+    ok &= np.array_equal(c2[3, :, :, 4:], codes[3, :, :, 4:])
+    ok &= np.array_equal(s2[3, :, :, 4:], scales[3, :, :, 4:])
+    ok &= np.array_equal(c2[0], codes[0]) and np.array_equal(s2[4], scales[4])
+    # dequantised keys are within half a step of the written ones
+    back = dequantize(c2[table[0], 0, :, :16].transpose(1, 0, 2), s2[table[0], 0, :, :16].T)
+    ok &= np.all(np.abs(back - key[:16].astype(np.float64)) <= ks[:16, :, None] * 0.5001)
+    return bool(ok)
+
+
+def i8_cow_before_scatter(cache_write_i8):
+    """Copies go first and carry codes and scales; the source stays intact."""
+    rng = np.random.default_rng(3)
+    codes = rng.integers(-127, 128, (4, 2, 2, 8, 16)).astype(np.int8)
+    scales = rng.uniform(0.1, 1, (4, 2, 2, 8)).astype(np.float32)
+    key = np.full((1, 2, 16), 2.0, dtype=np.float16)
+    value = np.full((1, 2, 16), -4.0, dtype=np.float16)
+    c2, s2 = cache_write_i8(codes, scales, key, value, np.array([2 * 8 + 5]), [(1, 2)])
+    ok = np.array_equal(c2[1], codes[1]) and np.array_equal(s2[1], scales[1])
+    ok &= np.array_equal(np.delete(c2[2], 5, axis=2), np.delete(codes[1], 5, axis=2))
+    ok &= np.array_equal(np.delete(s2[2], 5, axis=2), np.delete(scales[1], 5, axis=2))
+    ok &= np.all(c2[2, 0, :, 5] == 127) and np.all(c2[2, 1, :, 5] == -127)
+    ok &= np.allclose(s2[2, 0, :, 5], 2 / 127) and np.allclose(s2[2, 1, :, 5], 4 / 127)
+    return bool(ok)
+
+
+def i8_decode_is_sdpa_on_dequantised(decode_i8, dequantize):
+    """Decode over the INT8 pool equals SDPA over the dequantised contiguous
+    K/V of each sequence (scattered through a random table)."""
+    rng = np.random.default_rng(8)
+    lens, hq, hkv, d, bs = (40, 3, 17), 8, 2, 16, 8
+    nbs = [-(-n // bs) for n in lens]
+    nb = sum(nbs) + 2
+    codes = rng.integers(-127, 128, (nb, 2, hkv, bs, d)).astype(np.int8)
+    scales = rng.uniform(0.001, 0.05, (nb, 2, hkv, bs)).astype(np.float32)
+    perm = rng.permutation(nb)
+    tables = np.full((len(lens), max(nbs)), -1)
+    pos = 0
+    for s, k in enumerate(nbs):
+        tables[s, :k] = perm[pos:pos + k]
+        pos += k
+    q = rng.standard_normal((len(lens), hq, d))
+    out = decode_i8(q, codes, scales, tables, np.array(lens), 0.3)
+    for s, n in enumerate(lens):
+        t = np.arange(n)
+        blk = tables[s][t // bs]
+        kk = codes[blk, 0, :, t % bs, :].astype(np.float64) * scales[blk, 0, :, t % bs][..., None]
+        vv = codes[blk, 1, :, t % bs, :].astype(np.float64) * scales[blk, 1, :, t % bs][..., None]
+        kt = torch.from_numpy(kk).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[s])[:, None, :], kt, vt, scale=0.3)[:, 0, :]
+        if not np.allclose(out[s], ref.numpy(), rtol=0, atol=1e-12):
+            return False
+    return True

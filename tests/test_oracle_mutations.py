@@ -156,3 +156,73 @@ def test_block_manager_pins_catch_planted_mistake(cls):
         except (BlockManagerError, KeyError, IndexError, AssertionError):
             return False
     assert not (passes(pins.bm_fork_cow_example) and passes(pins.bm_scripted_lifecycle))
+
+
+# --------------------------------------------------------------------------
+# INT8 quantisation mutants
+# --------------------------------------------------------------------------
+def quantize_mutant(mistake):
+    def quantize(x):
+        xf = np.asarray(x).astype(np.float32)
+        if mistake == "per_tensor":
+            amax = np.broadcast_to(np.abs(xf).max(), xf.shape[:-1])
+        else:
+            amax = np.abs(xf).max(axis=-1)
+        q = np.float32(128 if mistake == "divide_by_128" else 127)
+        scales = (amax / q).astype(np.float32)
+        codes = np.zeros(xf.shape, dtype=np.int8)
+        live = scales > 0
+        r = xf[live] / scales[live][..., None]
+        if mistake == "truncate":
+            r = np.trunc(r)
+        elif mistake == "half_away":
+            r = np.sign(r) * np.floor(np.abs(r) + 0.5)
+        else:
+            r = np.rint(r)
+        codes[live] = np.clip(r, -127, 127).astype(np.int8)
+        return codes, scales
+    return quantize
+
+
+@pytest.mark.parametrize("mistake", ["per_tensor", "divide_by_128", "truncate", "half_away"])
+def test_quant_pins_catch(mistake):
+    assert pins.quant_failing(quantize_mutant(mistake), oracle.dequantize_ref)
+
+
+def test_quant_pins_pass_oracle_and_clean_copy():
+    assert not pins.quant_failing(oracle.quantize_rows_ref, oracle.dequantize_ref)
+    assert not pins.quant_failing(quantize_mutant(None), oracle.dequantize_ref)
+
+
+def i8_write_mutant(mistake):
+    def write(codes, scales, key, value, slots, cow_pairs=()):
+        codes, scales = np.array(codes, copy=True), np.array(scales, copy=True)
+        bs = codes.shape[3]
+        for src, dst in cow_pairs:
+            codes[dst] = codes[src]
+            if mistake != "cow_skips_scales":
+                scales[dst] = scales[src]
+        kq, ks = oracle.quantize_rows_ref(key)
+        vq, vs = oracle.quantize_rows_ref(value)
+        if mistake == "scales_swapped":
+            ks, vs = vs, ks
+        for i, slot in enumerate(np.asarray(slots).tolist()):
+            if slot < 0:
+                continue
+            b, r = divmod(int(slot), bs)
+            rs = 0 if mistake == "scale_row_zero" else r
+            codes[b, 0, :, r], codes[b, 1, :, r] = kq[i], vq[i]
+            scales[b, 0, :, rs], scales[b, 1, :, rs] = ks[i], vs[i]
+        return codes, scales
+    return write
+
+
+@pytest.mark.parametrize("mistake", ["cow_skips_scales", "scales_swapped", "scale_row_zero"])
+def test_i8_write_pins_catch(mistake):
+    w = i8_write_mutant(mistake)
+    ok = (pins.i8_cache_round_trip(w, oracle.quantize_rows_ref, oracle.dequantize_ref)
+          and pins.i8_cow_before_scatter(w))
+    assert not ok
+    c = i8_write_mutant(None)
+    assert pins.i8_cache_round_trip(c, oracle.quantize_rows_ref, oracle.dequantize_ref)
+    assert pins.i8_cow_before_scatter(c)

@@ -102,7 +102,7 @@ class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
     def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
-                 window=0):
+                 window=0, kv_dtype="f16"):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -112,13 +112,19 @@ class Step:
             w["bs"] = bs
         self.w, self.name, self.kernel, self.partition = w, name, kernel, partition
         self.window = window
+        self.int8 = kv_dtype == "i8"
+        if self.int8 and w["dtype"] != "f16":
+            raise SystemExit("--kv-dtype i8 needs a float16 workload")
         # a pool whose prefix blocks every sequence shares is read with cached
         # loads (the block manager knows it shares); streaming loads otherwise
         self.cached_kv = name == "shared_prefix"
         S, Hq, Hkv, D, bs = w["S"], w["Hq"], w["Hkv"], w["D"], w["bs"]
         self.S, self.Hq, self.Hkv, self.D, self.bs = S, Hq, Hkv, D, bs
         tdt = synth.DTYPES[w["dtype"]]
-        self.elem = torch.tensor([], dtype=tdt).element_size()
+        self.elem = 1 if self.int8 else torch.tensor([], dtype=tdt).element_size()
+        # HBM bytes one (token, KV head) costs the decode: K and V rows, plus
+        # their two float32 scales in an INT8 pool
+        self.row_bytes = 2 * D * self.elem + (2 * 4 if self.int8 else 0)
         g_cpu = torch.Generator().manual_seed(seed)
 
         # ---- context lengths at the first decoded step ----
@@ -177,15 +183,24 @@ class Step:
         g = torch.Generator(device=dev).manual_seed(seed + 2)
         log(f"[bench] {name}: pool {nb} blocks x {2 * Hkv * bs * D * self.elem} B = "
             f"{nb * 2 * Hkv * bs * D * self.elem / 2**30:.2f} GiB, generating on {dev}")
-        self.pool = synth.normal((nb, 2, Hkv, bs, D), tdt, g, dev, w["std"],
-                                 chunk_rows=max(1, (1 << 26) // (2 * Hkv * bs * D)))
+        if self.int8:
+            self.pool = synth.int8_codes((nb, 2, Hkv, bs, D), g, dev,
+                                         chunk_rows=max(1, (1 << 26) // (2 * Hkv * bs * D)))
+            self.kv_scales = (torch.rand((nb, 2, Hkv, bs), generator=g, device=dev) * 0.02
+                              + 0.01) * w["std"]
+        else:
+            self.pool = synth.normal((nb, 2, Hkv, bs, D), tdt, g, dev, w["std"],
+                                     chunk_rows=max(1, (1 << 26) // (2 * Hkv * bs * D)))
+            self.kv_scales = None
         self.q = synth.normal((S, Hq, D), tdt, g, dev, w["std"])
         self.new_k = synth.normal((S, Hkv, D), tdt, g, dev, w["std"])
         self.new_v = synth.normal((S, Hkv, D), tdt, g, dev, w["std"])
         self.scale = 1.0 / math.sqrt(D)
         self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
         ws = pa.decode_workspace_size(S, Hq, Hkv, D, bs, self.mb, self.mb * bs, partition,
-                                      pa.F32 if w["dtype"] == "f32" else pa.F16, kernel)
+                                      pa.I8 if self.int8 else
+                                      pa.F32 if w["dtype"] == "f32" else pa.F16, kernel,
+                                      sliding_window=window)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         # one packed host->device transfer per step: slots | pairs | lens | tables
         self.n_i32 = 2 * S + 2 * S + S + S * self.mb
@@ -229,7 +244,7 @@ class Step:
         self.bm.block_tables_into(self.seqs, buf["tables"], buf["lens"])
         tokens = self.key_tokens(buf["lens"])
         self.ctx_tokens.append(tokens)
-        self.kv_bytes.append(tokens * 2 * self.Hkv * self.D * self.elem)
+        self.kv_bytes.append(tokens * self.Hkv * self.row_bytes)
         self.ncow.append(ncow)
         return ncow
 
@@ -249,17 +264,25 @@ class Step:
         self.d_pack.copy_(buf["pack"], non_blocking=True)
         buf["event"].record()
         pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
-                       cow_pairs=self.d_pairs[:ncow] if ncow else None)
+                       cow_pairs=self.d_pairs[:ncow] if ncow else None, kv_scales=self.kv_scales)
         if timed_events is not None:
             timed_events[0].record()
         pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
                   max_context_len=maxlen, partition_size=self.partition, kernel=self.kernel,
                   out=self.out, workspace=self.ws, cached_kv=self.cached_kv,
-                  sliding_window=self.window)
+                  sliding_window=self.window, kv_scales=self.kv_scales)
         if timed_events is not None:
             timed_events[1].record()
         self.k += 1
         return buf
+
+    def oracle_decode(self, q, pool, bt, lens):
+        """The fp64 oracle on host copies from ``host_inputs``."""
+        import oracle
+        if self.int8:
+            return oracle.decode_i8_ref(q, pool[0], pool[1], bt, lens, self.scale,
+                                        window=self.window)
+        return oracle.decode_ref(q, pool, bt, lens, self.scale, window=self.window)
 
     def host_inputs(self, positions):
         """Host copies of the last step's inputs for some table rows: only those
@@ -272,11 +295,17 @@ class Step:
             n = int(lens[pos])
             nblk = -(-n // self.bs)
             ids = tables[pos, :nblk].long().to(self.pool.device)
-            blocks.append(self.pool[ids].cpu().numpy())
+            if self.int8:
+                blocks.append((self.pool[ids].cpu().numpy(), self.kv_scales[ids].cpu().numpy()))
+            else:
+                blocks.append(self.pool[ids].cpu().numpy())
             rows.append(np.arange(off, off + nblk))
             off += nblk
             lns.append(n)
-        pool = np.concatenate(blocks)
+        if self.int8:
+            pool = (np.concatenate([b[0] for b in blocks]), np.concatenate([b[1] for b in blocks]))
+        else:
+            pool = np.concatenate(blocks)
         bt = np.full((len(rows), max(1, max(len(r) for r in rows))), -1, dtype=np.int64)
         for i, r in enumerate(rows):
             bt[i, :len(r)] = r
@@ -290,16 +319,15 @@ def cpu_baseline(st, budget_s=10.0, cap_s=30.0):
     through them until about ``budget_s`` of CPU time has been spent."""
     from threadpoolctl import threadpool_limits
     import numpy as np
-    import oracle
     runs, t_used, nbytes, toks = 0, 0.0, 0, 0
     with threadpool_limits(1):
         while (runs < st.S and t_used < cap_s) or t_used < budget_s:
             q, pool, bt, lens, _ = st.host_inputs([runs % st.S])
             t0 = time.perf_counter()
-            oracle.decode_ref(q, pool, bt, lens, st.scale, window=st.window)
+            st.oracle_decode(q, pool, bt, lens)
             t_used += time.perf_counter() - t0
             keys = int(np.minimum(lens, st.window).sum()) if st.window > 0 else int(lens.sum())
-            nbytes += keys * 2 * st.Hkv * st.D * st.elem
+            nbytes += keys * st.Hkv * st.row_bytes
             toks += keys
             runs += 1
     return dict(value=round(nbytes / t_used / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
@@ -374,10 +402,9 @@ def calibrate_copy(dev, nbytes=1 << 30, reps=5):
 def parity_sample(st, samples=3):
     """Max-abs error of the last step's output vs the oracle on a few sequences."""
     import numpy as np
-    import oracle
     picks = sorted({0, st.S - 1, st.S // 2})[:samples]
     q, pool, bt, lens, pos = st.host_inputs(picks)
-    want = oracle.decode_ref(q, pool, bt, lens, st.scale, window=st.window)
+    want = st.oracle_decode(q, pool, bt, lens)
     got = st.out[pos].cpu().numpy().astype(np.float64)
     return float(np.abs(got - want).max())
 
@@ -396,6 +423,8 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--context", type=int, default=0,
                     help="override: every sequence at this context length (not shared_prefix)")
+    ap.add_argument("--kv-dtype", default="f16", choices=["f16", "i8"],
+                    help="i8: INT8 pool with one float32 scale per (token, head) row")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -420,7 +449,8 @@ def main():
         print(json.dumps(calibrate_copy(dev)), flush=True)
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
-              args.partition, dev, context=args.context, window=args.window)
+              args.partition, dev, context=args.context, window=args.window,
+              kv_dtype=args.kv_dtype)
     step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -463,7 +493,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w["dtype"],
+        "dtype": "i8" if st.int8 else w["dtype"],
         "data": "synthetic (seeded N(0, std^2) K/V/Q; fragmented pool; no weights)",
         "config": {
             "workload": w["desc"] + (f" (block {st.bs})" if args.workload == "shared_prefix" else ""),
@@ -473,6 +503,7 @@ def main():
             "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
             "context_override": args.context or None,
             "sliding_window": args.window or None,
+            "kv_cache": "int8 codes + f32 row scales" if st.int8 else w["dtype"],
             "kv_loads": "cached" if st.cached_kv else "streaming (non-temporal)",
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
@@ -491,8 +522,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload + (f"_w{args.window}" if args.window
-                                                         else ""))
+            "traffic": measured_traffic(args.workload + ("_i8" if st.int8 else "")
+                                        + (f"_w{args.window}" if args.window else ""))
             if (args.kernel, args.partition, args.context) == ("auto", 0, 0) else None,
         },
         "cpu_baseline": cpu,

@@ -54,7 +54,15 @@ typedef enum pa_status {
 
 typedef enum pa_dtype {
   PA_F32 = 0, /* IEEE binary32 */
-  PA_F16 = 1  /* IEEE binary16 */
+  PA_F16 = 1, /* IEEE binary16 */
+  /* INT8 KV cache ([KV2P] §5.2: INT8 halves the cache; one scale per group
+   * of 128 elements).  kv_cache holds int8 codes, and a separate kv_scales
+   * array [num_blocks, 2, num_kv_heads, block_size] float32 holds one scale
+   * per (token, KV head) row of K and of V (the row of head_dim values is
+   * the group).  Value = code * scale.  pa_cache_write takes binary16 key
+   * and value rows and quantises them; pa_decode takes a binary16 query.
+   * head_dim 64 or 128. */
+  PA_I8 = 2
 } pa_dtype;
 
 /* Kernel family for pa_decode.  PA_KERNEL_AUTO picks per shape. */
@@ -79,12 +87,22 @@ typedef enum pa_kernel {
  * copies the whole physical block src onto dst (K and V, every head, every
  * row): the copy-on-write a sequence needs before writing into a block it
  * shares ([NANO] §2.3, §5.5).  Both steps are enqueued on `stream`, copies
- * first.  The result is a byte copy (bit-exact).
+ * first.  For f32 / f16 pools the result is a byte copy (bit-exact).
  *
- *   key, value   device, [num_tokens, num_kv_heads, head_dim], dtype,
- *                contiguous, 16-byte aligned
+ * INT8 pools (PA_I8): each row x of head_dim values (one token, one KV head,
+ * K or V) is stored as scale s = amax|x| / 127 and codes
+ * clamp(rint(x / s), -127, 127), rint rounding ties to even, both divisions
+ * IEEE binary32 on the binary16 inputs widened to binary32; a row of zeros
+ * gets s = 0 and zero codes.  Copy-on-write copies move codes and scales.
+ * Inputs must be finite.
+ *
+ *   key, value   device, [num_tokens, num_kv_heads, head_dim], dtype
+ *                (binary16 for PA_I8), contiguous, 16-byte aligned
  *   kv_cache     device, [num_blocks, 2, num_kv_heads, block_size, head_dim],
  *                dtype, contiguous, 16-byte aligned; index 1 of dim 1 is V
+ *   kv_scales    PA_I8: device, [num_blocks, 2, num_kv_heads, block_size]
+ *                float32, 16-byte aligned (num_kv_heads * block_size even);
+ *                otherwise NULL
  *   slot_mapping device, [num_tokens] int64; slot < 0 skips the row; slots
  *                must lie in [0, num_blocks*block_size) and be distinct
  *   cow_pairs    device, [num_cow, 2] int32 (src, dst) block ids, or NULL
@@ -93,7 +111,7 @@ typedef enum pa_kernel {
  *   head_dim * element size must be a multiple of 16 bytes.
  * ------------------------------------------------------------------------- */
 int pa_cache_write(const void* key, const void* value, void* kv_cache,
-                   const int64_t* slot_mapping, int64_t num_tokens,
+                   float* kv_scales, const int64_t* slot_mapping, int64_t num_tokens,
                    const int32_t* cow_pairs, int64_t num_cow,
                    int64_t num_blocks, int num_kv_heads, int head_dim,
                    int block_size, int dtype, void* stream);
@@ -114,8 +132,12 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  * Accumulation is float32; the output is float32.
  *
  *   out            device, [num_seqs, num_q_heads, head_dim] float32
- *   query          device, [num_seqs, num_q_heads, head_dim] dtype, 16B aligned
+ *   query          device, [num_seqs, num_q_heads, head_dim] dtype (binary16
+ *                  for PA_I8), 16B aligned
  *   kv_cache       device, as for pa_cache_write
+ *   kv_scales      PA_I8: the row scales written by pa_cache_write; K_t and
+ *                  V_t above are then code * scale of their rows.  NULL
+ *                  otherwise.
  *   block_tables   device, [num_seqs, max_blocks_per_seq] int32 (row stride =
  *                  max_blocks_per_seq); entries past ceil(n/block_size) unused
  *   context_lens   device, [num_seqs] int32, 0 <= n <= max_context_len and
@@ -136,13 +158,13 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  *                  NULL when *workspace_needed is 0
  *   workspace_needed  out (may be NULL): bytes this call needs.  Calling with
  *                  out == NULL only computes it and returns PA_OK.
- * Supported: dtype f32 or f16; head_dim 64 or 128; block_size 8, 16 or 32;
- * G in {1, 2, 4, 8}.  MFMA needs f16 and G >= 2.  Anything else returns
- * PA_ERR_UNSUPPORTED.
+ * Supported: dtype f32, f16 or PA_I8; head_dim 64 or 128; block_size 8, 16
+ * or 32; G in {1, 2, 4, 8}.  MFMA needs f16 or PA_I8 and G >= 2.  Anything
+ * else returns PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 int pa_decode(float* out, const void* query, const void* kv_cache,
-              const int32_t* block_tables, const int32_t* context_lens,
-              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              const float* kv_scales, const int32_t* block_tables,
+              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
               int block_size, int max_blocks_per_seq, int max_context_len,
               int64_t num_blocks, float scale, int sliding_window,
               int partition_size, int kernel, void* workspace,

@@ -19,14 +19,14 @@ from typing import Optional
 
 __all__ = [
     "PAError", "lib", "library_path", "cache_write", "decode", "decode_workspace_size",
-    "BlockManager", "KERNELS", "F32", "F16",
+    "BlockManager", "KERNELS", "F32", "F16", "I8", "kv_scales_like",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 _lib = None
 
-F32, F16 = 0, 1
+F32, F16, I8 = 0, 1, 2
 KERNELS = {"auto": 0, "valu": 1, "mfma": 2}
 KV_CACHED = 0x100   # flag: plain cached K/V loads instead of streaming loads
 
@@ -52,9 +52,9 @@ _I32P = _c.POINTER(_c.c_int32)
 _I64P = _c.POINTER(_c.c_int64)
 
 _SIGNATURES = {
-    "pa_cache_write": (_c.c_int, [_P, _P, _P, _P, _c.c_int64, _P, _c.c_int64, _c.c_int64,
+    "pa_cache_write": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int64, _P, _c.c_int64, _c.c_int64,
                                   _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P]),
-    "pa_decode": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+    "pa_decode": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                              _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float, _c.c_int,
                              _c.c_int, _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t),
                              _c.c_int, _P]),
@@ -115,7 +115,31 @@ def _dtype_code(t):
         return F32
     if t.dtype == torch.float16:
         return F16
+    if t.dtype == torch.int8:
+        return I8
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def kv_scales_like(kv_cache):
+    """A zeroed float32 scale array [NB, 2, Hkv, bs] for an INT8 pool."""
+    torch = _torch()
+    nb, two, hkv, bs, _ = kv_cache.shape
+    return torch.zeros((nb, two, hkv, bs), dtype=torch.float32, device=kv_cache.device)
+
+
+def _scales_ptr(kv_cache, kv_scales):
+    """Pointer of the row-scale array an INT8 pool needs (None otherwise)."""
+    torch = _torch()
+    if kv_cache.dtype != torch.int8:
+        if kv_scales is not None:
+            raise TypeError("kv_scales is only for INT8 pools")
+        return None
+    nb, two, hkv, bs, _ = kv_cache.shape
+    if kv_scales is None or kv_scales.dtype != torch.float32 or \
+            tuple(kv_scales.shape) != (nb, two, hkv, bs):
+        raise TypeError("an INT8 pool needs kv_scales float32 [NB, 2, Hkv, bs]")
+    _need_cuda(kv_scales)
+    return kv_scales.data_ptr()
 
 
 def _stream(device, stream):
@@ -133,17 +157,22 @@ def _need_cuda(*tensors):
             raise ValueError("tensors must be contiguous")
 
 
-def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None):
+def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None,
+                kv_scales=None):
     """Copy-on-write block copies (``cow_pairs`` [k, 2] int32 on device), then
     scatter ``key``/``value`` [T, Hkv, D] into ``kv_cache`` [NB, 2, Hkv, bs, D]
-    at ``slot_mapping`` [T] int64 (negative = skip).  Enqueued on ``stream``."""
+    at ``slot_mapping`` [T] int64 (negative = skip).  Enqueued on ``stream``.
+    An int8 ``kv_cache`` takes float16 key/value rows, quantised per row into
+    codes plus ``kv_scales`` [NB, 2, Hkv, bs] float32."""
     torch = _torch()
     _need_cuda(key, value, kv_cache, slot_mapping, cow_pairs)
     nb, two, hkv, bs, d = kv_cache.shape
     if two != 2 or key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
         raise ValueError("shape mismatch between key/value and kv_cache")
-    if key.dtype != kv_cache.dtype or value.dtype != kv_cache.dtype:
-        raise TypeError("key, value and kv_cache must share a dtype")
+    in_dtype = torch.float16 if kv_cache.dtype == torch.int8 else kv_cache.dtype
+    if key.dtype != in_dtype or value.dtype != in_dtype:
+        raise TypeError("key and value must have the pool's dtype (float16 for an int8 pool)")
+    sp = _scales_ptr(kv_cache, kv_scales)
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
         raise TypeError("slot_mapping must be int64 [T]")
     ncow = 0
@@ -151,7 +180,7 @@ def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None)
         if cow_pairs.dtype != torch.int32 or cow_pairs.dim() != 2 or cow_pairs.shape[1] != 2:
             raise TypeError("cow_pairs must be int32 [k, 2]")
         ncow = cow_pairs.shape[0]
-    _check(lib().pa_cache_write(key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(),
+    _check(lib().pa_cache_write(key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(), sp,
                                 slot_mapping.data_ptr(), key.shape[0],
                                 cow_pairs.data_ptr() if ncow else None, ncow, nb, hkv, d, bs,
                                 _dtype_code(kv_cache), _stream(kv_cache.device, stream)))
@@ -162,8 +191,8 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
                           dtype=F16, kernel="auto", sliding_window=0):
     """Bytes of split-context workspace ``decode`` needs for this shape."""
     need = ctypes.c_size_t(0)
-    _check(lib().pa_decode(None, None, None, None, None, num_seqs, num_q_heads, num_kv_heads,
-                           head_dim, block_size, max_blocks_per_seq, max_context_len, 1, 1.0,
+    _check(lib().pa_decode(None, None, None, None, None, None, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len, 1, 1.0,
                            int(sliding_window), partition_size, KERNELS[kernel], None, 0,
                            ctypes.byref(need), dtype, None))
     return need.value
@@ -171,7 +200,7 @@ def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_s
 
 def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_len=None,
            partition_size=0, kernel="auto", out=None, workspace=None, stream=None,
-           cached_kv=False, sliding_window=0):
+           cached_kv=False, sliding_window=0, kv_scales=None):
     """Paged decode attention.
 
     query [S, Hq, D] (kv dtype), kv_cache [NB, 2, Hkv, bs, D], block_tables
@@ -181,7 +210,8 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     ``cached_kv``: read K/V with cached loads (for pools whose blocks many
     sequences share); default streams them with non-temporal loads.
     ``sliding_window`` W > 0: each query attends to its sequence's last W
-    tokens only; 0 = the whole context.
+    tokens only; 0 = the whole context.  An int8 ``kv_cache`` needs its row
+    scales ``kv_scales`` (written by ``cache_write``) and a float16 query.
     """
     torch = _torch()
     _need_cuda(query, kv_cache, block_tables, context_lens, out, workspace)
@@ -189,8 +219,10 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     s, hq, dq = query.shape
     if two != 2 or dq != d:
         raise ValueError("query/kv_cache shape mismatch")
-    if query.dtype != kv_cache.dtype:
-        raise TypeError("query and kv_cache must share a dtype")
+    q_dtype = torch.float16 if kv_cache.dtype == torch.int8 else kv_cache.dtype
+    if query.dtype != q_dtype:
+        raise TypeError("query must have the pool's dtype (float16 for an int8 pool)")
+    sp = _scales_ptr(kv_cache, kv_scales)
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != s:
         raise TypeError("block_tables must be int32 [S, MB]")
     if context_lens.dtype != torch.int32 or context_lens.shape != (s,):
@@ -210,7 +242,7 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().pa_decode(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
+    _check(lib().pa_decode(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(), sp,
                            block_tables.data_ptr(), context_lens.data_ptr(), s, hq, hkv, d, bs,
                            mb, int(max_context_len), nb, float(scale), int(sliding_window),
                            int(partition_size),

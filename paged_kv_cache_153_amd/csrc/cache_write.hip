@@ -8,11 +8,20 @@
 // it shares first gets a whole-block copy ([NANO] zwxr.cn walkthrough §2.3,
 // §5.5: copy-on-write); the copies are enqueued before the scatter.
 //
-// Both kernels are pure 16-byte copies (bit-exact).  One thread moves one
-// 16-byte chunk; consecutive threads take consecutive chunks of a row, so
-// each wave reads and writes contiguous 1 KiB runs.  Slots and block ids are
-// range-checked on the device: an out-of-range entry is skipped, never
-// written through.
+// For f32 / f16 pools both kernels are pure 16-byte copies (bit-exact).  One
+// thread moves one 16-byte chunk; consecutive threads take consecutive chunks
+// of a row, so each wave reads and writes contiguous 1 KiB runs.  Slots and
+// block ids are range-checked on the device: an out-of-range entry is
+// skipped, never written through.
+//
+// INT8 pools ([KV2P] "KV Cache从原理到实战" §5.2: INT8 halves the cache, one
+// scale per 128-element group): each (token, KV head) row of K and of V is
+// quantised on its way in, symmetric, with its own float32 scale
+// s = amax / 127 and codes rint(x / s) clamped to [-127, 127] (ties to even;
+// an all-zero row gets s = 0 and zero codes).  Both divisions are IEEE
+// float32 divisions, so the codes are exactly determined by the f16 inputs.
+// A group of D/8 threads takes one row (8 values each) and finds amax with a
+// butterfly over the group; copy-on-write copies move the scales too.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -62,25 +71,106 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
     to[k] = from[k];
 }
 
+// One row = (token i, head h, K|V); TPR threads per row, 8 f16 values each.
+// Grid-stride over num_tokens * Hkv * 2 * TPR threads; TPR divides the
+// stride, so a row's threads always run the same iteration together.
+template <int TPR>
+__global__ __launch_bounds__(256) void cache_write_i8_kernel(const u32x4_t* __restrict__ key,
+                                                             const u32x4_t* __restrict__ value,
+                                                             u32x2_t* __restrict__ codes,
+                                                             float* __restrict__ scales,
+                                                             const int64_t* __restrict__ slots,
+                                                             int64_t num_tokens,
+                                                             int num_kv_heads, int block_size,
+                                                             int64_t num_blocks) {
+  const int64_t total = num_tokens * num_kv_heads * 2 * TPR;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(idx % TPR);
+    const int64_t row = idx / TPR;  // (i * Hkv + h) * 2 + kv
+    const int kv = (int)(row & 1);
+    const int64_t ih = row >> 1;    // i * Hkv + h
+    const int64_t i = ih / num_kv_heads;
+    const int64_t h = ih - i * num_kv_heads;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_blocks * block_size) continue;  // uniform per row
+    const half8_t x = __builtin_bit_cast(half8_t, (kv ? value : key)[ih * TPR + c]);
+    float f[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] = (float)x[e];
+      amax = fmaxf(amax, fabsf(f[e]));
+    }
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float sc = amax / 127.f;
+    uint32_t w[2] = {0u, 0u};
+    if (sc > 0.f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float q = rintf(f[e] / sc);
+        q = fminf(fmaxf(q, -127.f), 127.f);
+        w[e / 4] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (e % 4));
+      }
+    }
+    const int64_t b = slot / block_size;
+    const int64_t r = slot - b * block_size;
+    const int64_t srow = ((b * 2 + kv) * num_kv_heads + h) * block_size + r;  // scale index
+    codes[srow * TPR + c] = u32x2_t{w[0], w[1]};
+    if (c == 0) scales[srow] = sc;
+  }
+}
+
+void copy_blocks(void* buf, const int32_t* cow_pairs, int64_t num_cow, int64_t block_chunks,
+                 int64_t num_blocks, hipStream_t stream, int* rc) {
+  const int64_t per_pair = (block_chunks + 255) / 256;
+  const unsigned gx = (unsigned)(per_pair < 64 ? per_pair : 64);
+  for (int64_t p0 = 0; p0 < num_cow && *rc == 0; p0 += 65535) {
+    const unsigned gy = (unsigned)(num_cow - p0 < 65535 ? num_cow - p0 : 65535);
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream,
+                       reinterpret_cast<u32x4_t*>(buf), cow_pairs + 2 * p0, block_chunks,
+                       num_blocks);
+    if (hipGetLastError() != hipSuccess) *rc = 2;
+  }
+}
+
 }  // namespace
 
-int launch_cache_write(const void* key, const void* value, void* kv, const int64_t* slots,
-                       int64_t num_tokens, const int32_t* cow_pairs, int64_t num_cow,
-                       int64_t num_blocks, int num_kv_heads, int head_dim, int block_size,
-                       int elem_bytes, hipStream_t stream) {
-  const int cpr = head_dim * elem_bytes / 16;
+int launch_cache_write(const void* key, const void* value, void* kv, float* scales,
+                       const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,
+                       int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                       int block_size, int elem_bytes, hipStream_t stream) {
+  int rc = 0;
   if (num_cow > 0) {
-    const int64_t block_chunks = 2LL * num_kv_heads * block_size * cpr;
-    const int64_t per_pair = (block_chunks + 255) / 256;
-    const unsigned gx = (unsigned)(per_pair < 64 ? per_pair : 64);
-    for (int64_t p0 = 0; p0 < num_cow; p0 += 65535) {
-      const unsigned gy = (unsigned)(num_cow - p0 < 65535 ? num_cow - p0 : 65535);
-      hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, stream,
-                         reinterpret_cast<u32x4_t*>(kv), cow_pairs + 2 * p0, block_chunks,
-                         num_blocks);
-      if (hipGetLastError() != hipSuccess) return 2;
-    }
+    copy_blocks(kv, cow_pairs, num_cow, 2LL * num_kv_heads * block_size * head_dim * elem_bytes / 16,
+                num_blocks, stream, &rc);
+    if (elem_bytes == 1)  // scale rows: 2 * Hkv * BS floats per block (a multiple of 16 bytes)
+      copy_blocks(scales, cow_pairs, num_cow, 2LL * num_kv_heads * block_size * 4 / 16,
+                  num_blocks, stream, &rc);
+    if (rc) return rc;
   }
+  if (num_tokens > 0 && elem_bytes == 1) {
+    const int tpr = head_dim / 8;
+    const int64_t total = num_tokens * num_kv_heads * 2 * tpr;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    const auto* k = reinterpret_cast<const u32x4_t*>(key);
+    const auto* v = reinterpret_cast<const u32x4_t*>(value);
+    auto* c = reinterpret_cast<u32x2_t*>(kv);
+    if (tpr == 16)
+      hipLaunchKernelGGL(cache_write_i8_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         k, v, c, scales, slots, num_tokens, num_kv_heads, block_size,
+                         num_blocks);
+    else if (tpr == 8)
+      hipLaunchKernelGGL(cache_write_i8_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         k, v, c, scales, slots, num_tokens, num_kv_heads, block_size,
+                         num_blocks);
+    else
+      return 1;
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+  }
+  const int cpr = head_dim * elem_bytes / 16;
   if (num_tokens > 0) {
     const int64_t total = num_tokens * num_kv_heads * cpr;
     int64_t blocks = (total + 255) / 256;

@@ -26,6 +26,7 @@ struct DecodeArgs {
   float* ws_l;              // [S, Hq, NP] partition sum of exp2(y - m)
   const void* q;            // [S, Hq, D]
   const void* kv;           // [NB, 2, Hkv, BS, D]
+  const float* kv_scales;   // INT8 pool: [NB, 2, Hkv, BS] row scales; else null
   const int32_t* bt;        // [S, MB]
   const int32_t* cl;        // [S]
   int64_t num_blocks;       // NB
@@ -50,6 +51,11 @@ int launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int block_s
                        int waves, hipStream_t stream);
 int launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,
                        int waves, hipStream_t stream);
+// INT8 pool (codes + row scales; query in f16).
+int launch_decode_valu_i8(const DecodeArgs& a, int head_dim, int block_size, int group,
+                          hipStream_t stream);
+int launch_decode_mfma_i8(const DecodeArgs& a, int head_dim, int block_size, int group,
+                          hipStream_t stream);
 int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream);
 int launch_merge_balanced(const DecodeArgs& a, int head_dim, hipStream_t stream);
 // Resident workgroups per compute unit of the kernel a launch would pick
@@ -57,9 +63,13 @@ int launch_merge_balanced(const DecodeArgs& a, int head_dim, hipStream_t stream)
 int decode_valu_occupancy(const DecodeArgs& a, int dtype, int head_dim, int block_size,
                           int group);
 int decode_mfma_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
-int launch_cache_write(const void* key, const void* value, void* kv, const int64_t* slots,
-                       int64_t num_tokens, const int32_t* cow_pairs, int64_t num_cow,
-                       int64_t num_blocks, int num_kv_heads, int head_dim, int block_size,
-                       int elem_bytes, hipStream_t stream);
+int decode_valu_i8_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
+int decode_mfma_i8_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
+// elem_bytes 4 / 2: byte copies; 1: INT8 pool, f16 inputs quantised per
+// row with their scales written to `scales` ([NB, 2, Hkv, BS] floats).
+int launch_cache_write(const void* key, const void* value, void* kv, float* scales,
+                       const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,
+                       int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                       int block_size, int elem_bytes, hipStream_t stream);
 
 }  // namespace pa

@@ -71,7 +71,7 @@ int choose_partition(int num_seqs, int num_kv_heads, int max_context_len, int ca
 // (G >= 4 measured faster: its VALU work per tile does not grow with G); the
 // vector kernel for MHA / G = 2, where MFMA rows would be mostly padding.
 int choose_kernel(int dtype, int group) {
-  return (dtype == PA_F16 && group >= 4) ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
+  return (dtype != PA_F32 && group >= 4) ? PA_KERNEL_MFMA : PA_KERNEL_VALU;
 }
 
 struct Plan {
@@ -224,18 +224,28 @@ const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
 
 const char* pa_version(void) { return "pa 0.1 gfx950"; }
 
-int pa_cache_write(const void* key, const void* value, void* kv_cache,
+int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv_scales,
                    const int64_t* slot_mapping, int64_t num_tokens, const int32_t* cow_pairs,
                    int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
                    int block_size, int dtype, void* stream_) {
   pa::clear_error();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype");
-  const int eb = dtype == PA_F32 ? 4 : 2;
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "dtype");
+  const int eb = dtype == PA_F32 ? 4 : dtype == PA_F16 ? 2 : 1;
   if (num_tokens < 0 || num_cow < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
   if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
   if ((head_dim * eb) % 16) return fail(PA_ERR_UNSUPPORTED, "head_dim * element size % 16 != 0");
+  if (dtype == PA_I8) {
+    if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 head_dim");
+    if ((2LL * num_kv_heads * block_size * 4) % 16)
+      return fail(PA_ERR_UNSUPPORTED, "INT8: num_kv_heads * block_size must be even");
+    if (!kv_scales || !aligned16(kv_scales))
+      return fail(PA_ERR_INVALID_ARG, "INT8 pool needs 16-byte aligned kv_scales");
+  } else if (kv_scales) {
+    return fail(PA_ERR_INVALID_ARG, "kv_scales is only for INT8 pools");
+  }
   if (!kv_cache || !aligned16(kv_cache)) return fail(PA_ERR_INVALID_ARG, "kv_cache null/unaligned");
   if (num_tokens > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
     return fail(PA_ERR_INVALID_ARG, "key/value/slot_mapping null or unaligned");
@@ -246,15 +256,15 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
                                         block_size, stream))
       return st;
   }
-  const int rc = pa::launch_cache_write(key, value, kv_cache, slot_mapping, num_tokens, cow_pairs,
-                                        num_cow, num_blocks, num_kv_heads, head_dim, block_size,
-                                        eb, stream);
+  const int rc = pa::launch_cache_write(key, value, kv_cache, kv_scales, slot_mapping, num_tokens,
+                                        cow_pairs, num_cow, num_blocks, num_kv_heads, head_dim,
+                                        block_size, eb, stream);
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
   return rc ? fail(PA_ERR_UNSUPPORTED, "cache write") : PA_OK;
 }
 
-int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t* block_tables,
-              const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+int pa_decode(float* out, const void* query, const void* kv_cache, const float* kv_scales,
+              const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
               int head_dim, int block_size, int max_blocks_per_seq, int max_context_len,
               int64_t num_blocks, float scale, int sliding_window, int partition_size, int kernel,
               void* workspace, size_t workspace_bytes, size_t* workspace_needed, int dtype,
@@ -262,7 +272,8 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   pa::clear_error();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   if (workspace_needed) *workspace_needed = 0;
-  if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype");
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "dtype");
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes out of range");
@@ -278,8 +289,8 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   if (kernel & ~(0xFF | PA_KV_CACHED)) return fail(PA_ERR_INVALID_ARG, "kernel flags");
   kernel &= 0xFF;
   if (kernel < PA_KERNEL_AUTO || kernel > PA_KERNEL_MFMA) return fail(PA_ERR_INVALID_ARG, "kernel");
-  if (kernel == PA_KERNEL_MFMA && (dtype != PA_F16 || group < 2))
-    return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs f16 and a query group of 2 or more");
+  if (kernel == PA_KERNEL_MFMA && (dtype == PA_F32 || group < 2))
+    return fail(PA_ERR_UNSUPPORTED, "MFMA kernel needs f16 or INT8 and a query group of 2 or more");
   if (partition_size < -2 ||
       (partition_size > 0 && (partition_size % pa::kTile || partition_size % block_size)))
     return fail(PA_ERR_INVALID_ARG, "partition_size must be -2, -1, 0 or a multiple of 16 and "
@@ -319,6 +330,8 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
     return fail(PA_ERR_INVALID_ARG, "null device pointer");
   if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache))
     return fail(PA_ERR_INVALID_ARG, "out/query/kv_cache must be 16-byte aligned");
+  if (dtype == PA_I8 ? (!kv_scales || !aligned16(kv_scales)) : kv_scales != nullptr)
+    return fail(PA_ERR_INVALID_ARG, "kv_scales: 16-byte aligned for INT8 pools, NULL otherwise");
   if (plan.ws_bytes && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
     return fail(PA_ERR_WORKSPACE, "workspace of " + std::to_string(plan.ws_bytes) +
                                       " bytes (16-byte aligned) needed");
@@ -335,6 +348,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
   a.q = query;
   a.kv = kv_cache;
+  a.kv_scales = kv_scales;
   a.bt = block_tables;
   a.cl = context_lens;
   a.num_blocks = num_blocks;
@@ -365,15 +379,25 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const int32_t
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);
   if (plan.schedule == pa::kScheduleBalanced) {
     // as many workgroups as are resident at once: one wave of the grid
-    const int occ = use == PA_KERNEL_MFMA
-                        ? pa::decode_mfma_occupancy(a, head_dim, block_size, group)
-                        : pa::decode_valu_occupancy(a, dtype, head_dim, block_size, group);
+    int occ;
+    if (dtype == PA_I8)
+      occ = use == PA_KERNEL_MFMA ? pa::decode_mfma_i8_occupancy(a, head_dim, block_size, group)
+                                  : pa::decode_valu_i8_occupancy(a, head_dim, block_size, group);
+    else
+      occ = use == PA_KERNEL_MFMA
+                ? pa::decode_mfma_occupancy(a, head_dim, block_size, group)
+                : pa::decode_valu_occupancy(a, dtype, head_dim, block_size, group);
     if (occ <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
     a.num_workgroups = std::min(plan.workgroups, cus * std::min(occ, pa::kMaxWorkgroupsPerCU));
   }
-  int rc = use == PA_KERNEL_MFMA
-               ? pa::launch_decode_mfma(a, dtype, head_dim, block_size, group, 4, stream)
-               : pa::launch_decode_valu(a, dtype, head_dim, block_size, group, 4, stream);
+  int rc;
+  if (dtype == PA_I8)
+    rc = use == PA_KERNEL_MFMA ? pa::launch_decode_mfma_i8(a, head_dim, block_size, group, stream)
+                               : pa::launch_decode_valu_i8(a, head_dim, block_size, group, stream);
+  else
+    rc = use == PA_KERNEL_MFMA
+             ? pa::launch_decode_mfma(a, dtype, head_dim, block_size, group, 4, stream)
+             : pa::launch_decode_valu(a, dtype, head_dim, block_size, group, 4, stream);
   if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no kernel for this shape");
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
   if (plan.schedule != pa::kScheduleSingle) {

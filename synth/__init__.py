@@ -29,6 +29,12 @@ examples; no weights are involved):
 
 Pools whose size the workload does not fix hold 1.1x the blocks the tables
 use (rounded up), the same slack as 9000 blocks for 8192 used.
+
+INT8 pools (``int8_pool``) keep a workload's queries, tables and lengths and
+draw the pool itself as int8 codes plus one float32 scale per (block, K|V,
+head, row): codes are rounded N(0, 42^2) draws clipped to [-127, 127] (about
+the spread of rows whose largest value maps to 127), scales are uniform on
+[0.01, 0.03] times the workload's standard deviation.
 """
 
 from __future__ import annotations
@@ -51,6 +57,7 @@ class DecodeInputs:
     scale: float
     seed: int
     meta: dict = field(default_factory=dict)
+    kv_scales: torch.Tensor = None   # INT8 pools: [NB, 2, Hkv, bs] float32
 
     @property
     def num_seqs(self):
@@ -75,7 +82,8 @@ class DecodeInputs:
     def to(self, device):
         return DecodeInputs(self.name, self.q.to(device), self.kv_cache.to(device),
                             self.block_tables.to(device), self.context_lens.to(device),
-                            self.scale, self.seed, dict(self.meta))
+                            self.scale, self.seed, dict(self.meta),
+                            None if self.kv_scales is None else self.kv_scales.to(device))
 
 
 def _gen(seed, device):
@@ -150,6 +158,42 @@ def make_decode_inputs(context_lens, num_q_heads, num_kv_heads, head_dim, block_
                         torch.tensor(lens, dtype=torch.int32, device=device),
                         float(scale), seed,
                         {"num_blocks": num_blocks, "dtype": dtype, "std": std})
+
+
+def int8_codes(shape, gen, device, code_std=42.0, chunk_rows=None):
+    """Rounded N(0, code_std^2) draws clipped to [-127, 127], as int8."""
+    out = torch.empty(shape, dtype=torch.int8, device=device)
+    step = shape[0] if not chunk_rows else chunk_rows
+    for lo in range(0, shape[0], step):
+        hi = min(shape[0], lo + step)
+        x = torch.randn((hi - lo,) + tuple(shape[1:]), generator=gen, device=device)
+        out[lo:hi] = x.mul_(code_std).round_().clamp_(-127, 127).to(torch.int8)
+    return out
+
+
+def int8_pool(x, seed=None, fill_unused=None):
+    """The same queries, tables and lengths as ``x`` over a freshly drawn INT8
+    pool: codes [NB, 2, Hkv, bs, D] int8 and scales [NB, 2, Hkv, bs] float32.
+    ``fill_unused`` (e.g. NaN) overwrites the scales of rows no context covers."""
+    nb, two, hkv, bs, d = x.kv_cache.shape
+    device = x.kv_cache.device
+    seed = x.seed + 100 if seed is None else seed
+    g = _gen(seed, device)
+    codes = int8_codes((nb, two, hkv, bs, d), g, device,
+                       chunk_rows=max(1, (1 << 26) // (2 * hkv * bs * d)))
+    std = float(x.meta.get("std", 1.0))
+    scales = (torch.rand((nb, two, hkv, bs), generator=g, device=device) * 0.02 + 0.01) * std
+    if fill_unused is not None:
+        covered = torch.zeros((nb, bs), dtype=torch.bool)
+        tables = x.block_tables.cpu()
+        for s, n in enumerate(x.context_lens.tolist()):
+            for i in range(-(-n // bs)):
+                covered[int(tables[s, i]), :min(bs, n - i * bs)] = True
+        mask = (~covered).to(device)
+        scales.permute(0, 3, 1, 2)[mask] = fill_unused
+    q = x.q if x.q.dtype == torch.float16 else x.q.to(torch.float16)
+    return DecodeInputs(x.name + "_i8", q, codes, x.block_tables, x.context_lens, x.scale,
+                        x.seed, dict(x.meta, dtype="i8"), scales)
 
 
 def tiny(seed=0, device="cpu", fill_unused=None):

@@ -49,12 +49,13 @@ def test_strerror_and_version():
 
 
 def _decode_status(**kw):
-    args = dict(out=None, query=None, kv=None, bt=None, cl=None, S=2, Hq=8, Hkv=2, D=128, bs=16,
+    args = dict(out=None, query=None, kv=None, scales=None, bt=None, cl=None, S=2, Hq=8, Hkv=2, D=128, bs=16,
                 MB=4, maxlen=64, NB=16, scale=0.1, window=0, part=0, kernel=0, ws=None, wsb=0,
                 need=None, dtype=1)
     args.update(kw)
     need = args["need"]
-    return pa.lib().pa_decode(args["out"], args["query"], args["kv"], args["bt"], args["cl"],
+    return pa.lib().pa_decode(args["out"], args["query"], args["kv"], args["scales"], args["bt"],
+                              args["cl"],
                               args["S"], args["Hq"], args["Hkv"], args["D"], args["bs"],
                               args["MB"], args["maxlen"], args["NB"], args["scale"],
                               args["window"], args["part"],
@@ -68,7 +69,7 @@ def _decode_status(**kw):
     (dict(dtype=5), -2), (dict(kernel=2, dtype=0), -2), (dict(kernel=2, Hq=2), -2),
     (dict(part=24), -1), (dict(part=8, bs=16), -1), (dict(part=-3), -1), (dict(MB=0), -1),
     (dict(kernel=7), -1), (dict(NB=0), -1), (dict(kernel=0x200), -1), (dict(kernel=0x103), -1),
-    (dict(window=-1), -1),
+    (dict(window=-1), -1), (dict(dtype=2, D=96), -2), (dict(dtype=2, kernel=2, Hq=2, Hkv=2), -2),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert _decode_status(**kw) == status
@@ -82,6 +83,11 @@ def test_decode_reports_null_pointers_and_missing_workspace():
     assert st == -3
     st = _decode_status(out=ctypes.c_void_p((1 << 20) + 4), query=fake, kv=fake, bt=fake, cl=fake)
     assert st == -1   # misaligned output
+    # INT8 pools need their scales; other pools must not get any
+    st = _decode_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, dtype=2, part=-1)
+    assert st == -1
+    st = _decode_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, scales=fake, part=-1)
+    assert st == -1
 
 
 def test_workspace_size_closed_form():
@@ -107,11 +113,19 @@ def test_cache_write_rejects_bad_arguments():
     L = pa.lib()
     fake = ctypes.c_void_p(1 << 20)
     # head_dim*2 bytes not a multiple of 16
-    assert L.pa_cache_write(fake, fake, fake, fake, 1, None, 0, 4, 1, 4, 16, 1, None) == -2
-    assert L.pa_cache_write(fake, fake, fake, fake, -1, None, 0, 4, 1, 64, 16, 1, None) == -1
-    assert L.pa_cache_write(fake, fake, None, fake, 1, None, 0, 4, 1, 64, 16, 1, None) == -1
-    assert L.pa_cache_write(fake, fake, fake, fake, 0, None, 1, 4, 1, 64, 16, 1, None) == -1
-    assert L.pa_cache_write(fake, fake, fake, fake, 0, None, 0, 4, 1, 64, 16, 1, None) == 0
+    assert L.pa_cache_write(fake, fake, fake, None, fake, 1, None, 0, 4, 1, 4, 16, 1, None) == -2
+    assert L.pa_cache_write(fake, fake, fake, None, fake, -1, None, 0, 4, 1, 64, 16, 1, None) == -1
+    assert L.pa_cache_write(fake, fake, None, None, fake, 1, None, 0, 4, 1, 64, 16, 1, None) == -1
+    assert L.pa_cache_write(fake, fake, fake, None, fake, 0, None, 1, 4, 1, 64, 16, 1, None) == -1
+    assert L.pa_cache_write(fake, fake, fake, None, fake, 0, None, 0, 4, 1, 64, 16, 1, None) == 0
+    # INT8: scales required (and 16-byte aligned), head_dim 64 or 128 only
+    assert L.pa_cache_write(fake, fake, fake, None, fake, 1, None, 0, 4, 1, 64, 16, 2, None) == -1
+    assert L.pa_cache_write(fake, fake, fake, fake, fake, 1, None, 0, 4, 1, 32, 16, 2, None) == -2
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert L.pa_cache_write(fake, fake, fake, odd, fake, 1, None, 0, 4, 1, 64, 16, 2, None) == -1
+    assert L.pa_cache_write(fake, fake, fake, fake, fake, 0, None, 0, 4, 1, 64, 16, 2, None) == 0
+    # scales given for an f16 pool
+    assert L.pa_cache_write(fake, fake, fake, fake, fake, 0, None, 0, 4, 1, 64, 16, 1, None) == -1
 
 
 # --------------------------------------------------------------------------

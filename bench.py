@@ -102,14 +102,15 @@ class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
     def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
-                 window=0, kv_dtype="f16"):
+                 window=0, kv_dtype="f16", kv_loads="auto"):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
         self.torch, self.pa = torch, pa
         w = dict(WORKLOADS[name])
-        if name == "shared_prefix":
+        if bs and bs != w["bs"]:
             w["bs"] = bs
+            w["pool"] = None  # fixed pool sizes are in blocks of the default size
         self.w, self.name, self.kernel, self.partition = w, name, kernel, partition
         self.window = window
         self.int8 = kv_dtype == "i8"
@@ -117,7 +118,7 @@ class Step:
             raise SystemExit("--kv-dtype i8 needs a float16 workload")
         # a pool whose prefix blocks every sequence shares is read with cached
         # loads (the block manager knows it shares); streaming loads otherwise
-        self.cached_kv = name == "shared_prefix"
+        self.cached_kv = name == "shared_prefix" if kv_loads == "auto" else kv_loads == "cached"
         S, Hq, Hkv, D, bs = w["S"], w["Hq"], w["Hkv"], w["D"], w["bs"]
         self.S, self.Hq, self.Hkv, self.D, self.bs = S, Hq, Hkv, D, bs
         tdt = synth.DTYPES[w["dtype"]]
@@ -337,24 +338,22 @@ def cpu_baseline(st, budget_s=10.0, cap_s=30.0):
                        f"{toks / t_used:.4g} seq*ctx tokens/s")
 
 
-def stream_ceiling(dev, nbytes=4 << 30, reps=5):
+def stream_ceiling(dev, tile_bytes=4096, nbytes=4 << 30, reps=5):
     """Measured HBM read ceiling on this GPU (libpa_probe.so): a linear
-    grid-stride read and a read of 4 KiB tiles in random order — the access
-    pattern of paged K/V tiles.  GB/s, best over launch shapes and over
-    plain / non-temporal loads."""
+    grid-stride read and reads of 4 KiB (and, when the decode's K/V tiles
+    are 2 KiB, 2 KiB) tiles in random order — the access pattern of paged K/V
+    tiles.  GB/s, best over launch shapes and over plain / non-temporal
+    loads."""
     import ctypes
     import torch
     probe = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_153_amd", "libpa_probe.so"))
     probe.pa_probe_read_linear.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    probe.pa_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                          ctypes.c_void_p, ctypes.c_void_p]
+    probe.pa_probe_read_tiles_sized.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     buf = torch.ones(nbytes // 2, dtype=torch.float16, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    ntiles = nbytes // 4096
-    order = torch.randperm(ntiles, generator=torch.Generator().manual_seed(5)).to(torch.int32)
-    order = order.to(dev)
     st = torch.cuda.current_stream(dev).cuda_stream
 
     def timed(fn):
@@ -372,12 +371,19 @@ def stream_ceiling(dev, nbytes=4 << 30, reps=5):
     lin = max(timed(lambda: probe.pa_probe_read_linear(buf.data_ptr(), nbytes, w, nt,
                                                        sink.data_ptr(), st))
               for w in (1024, 2048, 4096) for nt in (0, 1))
-    til = max(timed(lambda: probe.pa_probe_read_tiles(buf.data_ptr(), ntiles, order.data_ptr(),
-                                                      ntiles, per, nt, sink.data_ptr(), st))
-              for per in (16, 64) for nt in (0, 1))
-    del buf, order
+    res = {"linear_read_GBps": round(lin, 1)}
+    for tb in sorted({4096, tile_bytes}):
+        ntiles = nbytes // tb
+        order = torch.randperm(ntiles, generator=torch.Generator().manual_seed(5))
+        order = order.to(torch.int32).to(dev)
+        til = max(timed(lambda: probe.pa_probe_read_tiles_sized(
+            buf.data_ptr(), ntiles, order.data_ptr(), ntiles, per, tb, nt, sink.data_ptr(), st))
+            for per in (16, 64) for nt in (0, 1))
+        res[f"random_{tb // 1024}KiB_tile_read_GBps"] = round(til, 1)
+        del order
+    del buf
     torch.cuda.empty_cache()
-    return {"linear_read_GBps": round(lin, 1), "random_4KiB_tile_read_GBps": round(til, 1)}
+    return res
 
 
 def calibrate_copy(dev, nbytes=1 << 30, reps=5):
@@ -415,7 +421,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b_mha", choices=sorted(WORKLOADS))
-    ap.add_argument("--block-size", type=int, default=16, help="shared_prefix: 8, 16 or 32")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the workload's block size (8, 16 or 32)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=0, help="0 auto, -1 single pass, or tokens")
     ap.add_argument("--seed", type=int, default=0)
@@ -425,6 +432,8 @@ def main():
                     help="override: every sequence at this context length (not shared_prefix)")
     ap.add_argument("--kv-dtype", default="f16", choices=["f16", "i8"],
                     help="i8: INT8 pool with one float32 scale per (token, head) row")
+    ap.add_argument("--kv-loads", default="auto", choices=["auto", "cached", "streaming"],
+                    help="K/V load policy (auto: cached for shared_prefix, else streaming)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -450,7 +459,7 @@ def main():
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
               args.partition, dev, context=args.context, window=args.window,
-              kv_dtype=args.kv_dtype)
+              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads)
     step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -479,7 +488,9 @@ def main():
         f"{achieved:.1f} GB/s decode, {value:.1f} GB/s whole step")
 
     parity = None if args.no_parity else parity_sample(st)
-    ceiling = None if args.no_ceiling else stream_ceiling(dev)
+    # bytes of one K (or V) tile of one KV head: the unit the decode reads
+    tile_bytes = 2048 if st.bs * st.D * st.elem <= 2048 else 4096
+    ceiling = None if args.no_ceiling else stream_ceiling(dev, tile_bytes)
     cpu = None if args.no_cpu_baseline else cpu_baseline(st)
     w = st.w
     res = {
@@ -496,7 +507,7 @@ def main():
         "dtype": "i8" if st.int8 else w["dtype"],
         "data": "synthetic (seeded N(0, std^2) K/V/Q; fragmented pool; no weights)",
         "config": {
-            "workload": w["desc"] + (f" (block {st.bs})" if args.workload == "shared_prefix" else ""),
+            "workload": w["desc"] + (f" (block {st.bs})" if args.block_size else ""),
             "num_seqs": st.S, "num_q_heads": st.Hq, "num_kv_heads": st.Hkv, "head_dim": st.D,
             "block_size": st.bs, "pool_blocks": st.num_blocks,
             "mean_key_tokens": round(total_tokens / args.steps / st.S, 1),
@@ -514,8 +525,9 @@ def main():
         "cow_pairs_per_step": round(sum(st.ncow) / args.steps, 3),
         "parity_max_abs_err": parity,
         "measured_read_ceiling": ceiling,
-        "decode_frac_of_tile_ceiling": (round(achieved / ceiling["random_4KiB_tile_read_GBps"], 4)
-                                        if ceiling else None),
+        "decode_frac_of_tile_ceiling": (
+            round(achieved / ceiling[f"random_{tile_bytes // 1024}KiB_tile_read_GBps"], 4)
+            if ceiling else None),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

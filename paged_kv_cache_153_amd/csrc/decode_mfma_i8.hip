@@ -112,7 +112,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   using vchunk_t = typename VChunk<D>::type;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // the wave index is uniform: keeping it scalar keeps tile indices and
+  // block-table reads scalar
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int quad = lane >> 4;
   const int col = lane & 15;
   const int Hq = a.num_q_heads;
@@ -139,18 +141,17 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   const float* sch = a.kv_scales + (size_t)g * BS;
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
 
-  int ids[BPT];
-  auto load_ids = [&](int k0) {
-    const int tile = tile_begin + w + (k0 + lane) * NW;
+  // Block ids are read with scalar loads one step before the tile's loads
+  // are issued.  Look-ahead loads past the range re-read its last tile, so
+  // every step issues the same vector loads and the compiler's wait counts
+  // stay exact (a conditional load would force it to wait for all of them).
+  auto fetch_ids = [&](int tile, int (&out)[BPT]) {
+    if (tile >= tile_end) tile = tile_end - 1;
 #pragma unroll
     for (int jj = 0; jj < BPT; ++jj) {
       const int lb = BS >= kTile ? tile * kTile / BS : tile * BPT + jj;
-      int v = 0;
-      if (lb < a.max_blocks) {
-        v = bt_row[lb];
-        if (v < 0 || v >= a.num_blocks) v = 0;
-      }
-      ids[jj] = v;
+      const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
+      out[jj] = (v < 0 || v >= a.num_blocks) ? 0 : v;
     }
   };
 
@@ -164,15 +165,12 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   struct Buf {
     u32x4_t k[KL];     // codes of K row `col`, bytes quad*D/4 ..
     vchunk_t v[4];     // codes of V rows 4*quad + i, bytes col*VB ..
-    u32x4_t sk, sv;    // scales of tokens 4*quad .. 4*quad + 3
+    float sk, sv;      // scales of token 4*quad + (col & 3)
   };
-  Buf bA, bB;
+  Buf buf[DEPTH];
 
-  auto issue = [&](int tile, int k_it, Buf& b) {
-    const int sel = k_it & 63;
-    int blk[BPT];
-#pragma unroll
-    for (int jj = 0; jj < BPT; ++jj) blk[jj] = readlane(ids[jj], sel);
+  auto issue = [&](int tile, const int (&blk)[BPT], Buf& b) {
+    if (tile >= tile_end) tile = tile_end - 1;  // look-ahead past the range
     const int row0 = BS > kTile ? (tile % (BS / kTile)) * kTile : 0;
     // K row `col`; V rows and scales of tokens 4*quad ..; blocks per lane
     // when a tile spans two 8-row blocks
@@ -189,8 +187,10 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       b.v[i] = VChunk<D>::template load<NT>(vb, (uint32_t)((vrow + i) * D + col * VB));
-    b.sk = kv_load16<NT>(sb, (uint32_t)vrow * 4u);
-    b.sv = kv_load16<NT>(sb + sv_offset, (uint32_t)vrow * 4u);
+    // one scale per lane: lanes 4k .. 4k+3 of a quad hold its four tokens
+    const uint32_t soff = (uint32_t)(vrow + (col & 3)) * 4u;
+    b.sk = __builtin_bit_cast(float, kv_load4<NT>(sb, soff));
+    b.sv = __builtin_bit_cast(float, kv_load4<NT>(sb + sv_offset, soff));
   };
 
   auto compute = [&](int tile, Buf& b) {
@@ -206,23 +206,24 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
         sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[2 * x + jj], sc, 0, 0, 0);
       }
     }
-    // whole-vector casts: this compiler miscompiles a bit_cast of a single
-    // vector element (it reads element 0)
-    const float4_t skf = __builtin_bit_cast(float4_t, b.sk);
-    const float4_t svf = __builtin_bit_cast(float4_t, b.sv);
+    // token 4*quad + i's scales come from lane i of each group of four
+    // (quad_perm broadcast, fused into the multiply where it can be)
+    const float skc = b.sk * cs;
     float y[4], svt[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[i] = sc[i] * (skf[i] * cs);
-      svt[i] = svf[i];
-    }
+    y[0] = sc[0] * quad_bcast<0>(skc);
+    y[1] = sc[1] * quad_bcast<1>(skc);
+    y[2] = sc[2] * quad_bcast<2>(skc);
+    y[3] = sc[3] * quad_bcast<3>(skc);
+    svt[0] = quad_bcast<0>(b.sv);
+    svt[1] = quad_bcast<1>(b.sv);
+    svt[2] = quad_bcast<2>(b.sv);
+    svt[3] = quad_bcast<3>(b.sv);
     if ((tile + 1) * kTile > n || tile * kTile < lo) {  // partial tile: non-keys
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = tile * kTile + 4 * quad + i;
-        if (tok >= n || tok < lo) {
+        if (tok >= n || tok < lo) {  // codes are finite: a zero weight suffices
           y[i] = -INFINITY;
-          b.v[i] = VChunk<D>::zero();
           svt[i] = 0.f;
         }
       }
@@ -277,35 +278,31 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
     m = m_new;
   };
 
+  // ---- main loop: DEPTH - 1 tiles in flight ahead of the one computed ------
+  // buf[k] of an unrolled round of DEPTH steps holds the tile computed at
+  // step k; each step first refills the buffer the previous step freed.
   int tile = tile_begin + w;
-  int k_it = 0;
-  load_ids(0);
-  if constexpr (DEPTH == 1) {
-    for (; tile < tile_end; tile += NW, ++k_it) {
-      if (k_it > 0 && (k_it & 63) == 0) load_ids(k_it);
-      issue(tile, k_it, bA);
-      compute(tile, bA);
+  if (tile < tile_end) {
+    int nb[BPT];
+#pragma unroll
+    for (int k = 0; k < DEPTH - 1; ++k) {
+      fetch_ids(tile + k * NW, nb);
+      issue(tile + k * NW, nb, buf[k]);
     }
-  } else {
-    if (tile < tile_end) issue(tile, 0, bA);
+    fetch_ids(tile + (DEPTH - 1) * NW, nb);
     while (tile < tile_end) {
-      int nxt = tile + NW;
-      if (nxt < tile_end) {
-        if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-        issue(nxt, k_it + 1, bB);
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) {
+        const int ahead = tile + (DEPTH - 1) * NW;
+        int cur[BPT];
+#pragma unroll
+        for (int jj = 0; jj < BPT; ++jj) cur[jj] = nb[jj];
+        issue(ahead, cur, buf[(k + DEPTH - 1) % DEPTH]);
+        fetch_ids(ahead + NW, nb);  // for the next step
+        compute(tile, buf[k]);
+        tile += NW;
+        if (tile >= tile_end) break;
       }
-      compute(tile, bA);
-      tile = nxt;
-      ++k_it;
-      if (tile >= tile_end) break;
-      nxt = tile + NW;
-      if (nxt < tile_end) {
-        if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-        issue(nxt, k_it + 1, bA);
-      }
-      compute(tile, bB);
-      tile = nxt;
-      ++k_it;
     }
   }
 
@@ -328,9 +325,8 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   finish_range<G, D, NW>(sm, sink);
 }
 
-template <int D, int BS, int G, int NW, int DEPTH, bool NT>
-__global__ __launch_bounds__(NW * 64, DEPTH == 1 ? 4 : 2) void decode_mfma_i8_kernel(
-    DecodeArgs a) {
+template <int D, int BS, int G, int NW, int DEPTH, int OCC, bool NT>
+__global__ __launch_bounds__(NW * 64, OCC) void decode_mfma_i8_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G, D, NW> sm;
   __shared__ int prefix[kBalancedMaxSeqs];
   run_schedule<G, D, NW>(a, prefix, [&](int s, int g, int lo, int n, int ta, int tb,
@@ -344,30 +340,41 @@ unsigned grid_of(const DecodeArgs& a) {
   return (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
 }
 
-template <int D, int BS, int G, int NW>
-int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
+// Pipeline depth and waves per SIMD of each variant: 0 = one tile in flight
+// ahead of the computed one at four waves per SIMD (streaming K/V; measured
+// best: 70B-shaped layer 202 us, ragged GQA batch 118 us, against 203 / 128
+// for two tiles ahead at three waves); 1 = no look-ahead at four waves
+// (cached K/V); 2 = two tiles ahead at three waves (kept for tuning runs).
+template <int D, int BS, int G, int NW, int DEPTH, int OCC>
+int launch_variant(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
   if (mode == 1) {
     int n = 0;
-    const void* fn =
-        a.variant == 1
-            ? reinterpret_cast<const void*>(&decode_mfma_i8_kernel<D, BS, G, NW, 1, true>)
-            : reinterpret_cast<const void*>(&decode_mfma_i8_kernel<D, BS, G, NW, 2, true>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 2;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(&decode_mfma_i8_kernel<D, BS, G, NW, DEPTH, OCC, true>),
+            NW * 64, 0) != hipSuccess)
+      return 2;
     *occ = n;
     return 0;
   }
   const unsigned grid = grid_of(a);
   if (grid == 0) return 0;
-  const dim3 g(grid), b(NW * 64);
-  if (a.variant == 1 && a.cached_kv)
-    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, 1, false>), g, b, 0, stream, a);
-  else if (a.variant == 1)
-    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, 1, true>), g, b, 0, stream, a);
-  else if (a.cached_kv)
-    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, 2, false>), g, b, 0, stream, a);
+  if (a.cached_kv)
+    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, DEPTH, OCC, false>), dim3(grid),
+                       dim3(NW * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, 2, true>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_i8_kernel<D, BS, G, NW, DEPTH, OCC, true>), dim3(grid),
+                       dim3(NW * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+template <int D, int BS, int G, int NW>
+int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
+  switch (a.variant) {
+    case 1: return launch_variant<D, BS, G, NW, 1, 4>(a, stream, mode, occ);
+    case 2: return launch_variant<D, BS, G, NW, 3, 3>(a, stream, mode, occ);
+    // 8-row blocks need per-lane block addresses: more registers, three waves
+    default: return launch_variant<D, BS, G, NW, 2, BS == 8 ? 3 : 4>(a, stream, mode, occ);
+  }
 }
 
 template <int D, int BS, int NW>

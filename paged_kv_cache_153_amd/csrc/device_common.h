@@ -118,6 +118,28 @@ __device__ __forceinline__ u32x2_t kv_load8(const void* base, uint32_t byte_off)
   else return load8_at(base, byte_off);
 }
 
+template <bool NT>
+__device__ __forceinline__ uint32_t kv_load4(const void* base, uint32_t byte_off) {
+  const uint32_t* p =
+      reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_off);
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Lane I of every group of four lanes, broadcast to the group (DPP quad_perm).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return dpp_mov<I | (I << 2) | (I << 4) | (I << 6)>(x);
+}
+
+// A wave-uniform int32 read through the scalar data cache (s_load_dword): for
+// read-only data such as block tables.  Scalar loads complete on their own
+// counter, so they never make the wave wait for its in-flight vector loads.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *(const_i32*)(p);
+}
+
 // True when any lane of the wave has `pred` set (wave-uniform).
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;

@@ -365,12 +365,12 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   // tile per wave in flight at twice the occupancy when they are read through
   // the caches (shared blocks): measured faster in each case.
   a.variant = cached_kv ? 1 : 0;
-  {  // PA_TUNE_VARIANT=0|1 overrides the choice (tuning experiments only)
+  {  // PA_TUNE_VARIANT=0..2 overrides the choice (tuning experiments only)
     static const int forced = [] {
       const char* e = std::getenv("PA_TUNE_VARIANT");
       return e ? std::atoi(e) : -1;
     }();
-    if (forced == 0 || forced == 1) a.variant = forced;
+    if (forced >= 0 && forced <= 2) a.variant = forced;
   }
   a.cached_kv = cached_kv;
   a.window = sliding_window;

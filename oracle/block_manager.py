@@ -38,9 +38,60 @@ sequence, a block table mapping logical block ``i`` to a physical block
 
 Readings: an unknown or already-freed sequence is an error with no state
 change ([NANO] §4.2 would raise ``KeyError``; [KV2P] §6.2 silently ignores).
+
+Prefix cache (optional, ``enable_prefix_cache``)
+-----------------------------------------------
+Requests that start with the same tokens reuse the blocks that hold them
+([KVPA] §8.1-§8.2: hash the prefix, look it up in a global cache, add a
+reference to each reused block; [KV2P] §4.2: one hash per block from its
+content and position, match block by block for the longest prefix, keep
+reference counts, evict with LRU but never a referenced block; [NANO] §3.2:
+hash fixed-size chunks so that partial matches count, §4.3: a dict from the
+chunk hash to the block, reuse only full blocks).
+
+* Block hash: ``h_i = FNV-1a-64(le64(h_{i-1}) || le32(t) for the bs token ids
+  of block i)`` with ``h_{-1} = 0``, so a block's hash depends on its tokens
+  and on everything before it (its position).  A match also compares the
+  stored parent hash and token ids, so a hash collision is never a hit.
+* ``allocate_prompt(seq, tokens)``: walk the prompt's full blocks from the
+  start while their hashes are in the cache; every matched block gains a
+  reference (and a hit); the rest of the prompt gets fresh blocks.  Returns
+  the number of leading tokens whose K/V the matched blocks already hold.
+* ``register(seq)``: after the caller wrote the K/V of the sequence's full
+  blocks, put those not yet cached into the cache (a hash already present
+  keeps its block; the sequence's copy stays private).  ``record_tokens``
+  appends the ids of decoded tokens so that their blocks can be registered.
+* A cached block whose count drops to 0 is not returned to the free pool: it
+  becomes evictable, stamped with a release clock.  Fresh blocks come from
+  the free pool first; only when it is empty is an evictable block evicted
+  (removed from the cache): the least recently released one, taking blocks
+  with at least ``protect_hits`` hits last ([KV2P] §4.3: protect frequently
+  reused prefixes against one-off requests; 0 = plain LRU).
+* With the cache on, ``free`` counts free plus evictable blocks.
 """
 
 from __future__ import annotations
+
+FNV_OFFSET = 0xCBF29CE484222325
+FNV_PRIME = 0x100000001B3
+MASK64 = (1 << 64) - 1
+
+
+def fnv1a64(data, h=FNV_OFFSET):
+    """64-bit FNV-1a over ``data`` (bytes), from its published definition:
+    for each octet, xor it into the hash, then multiply by the FNV prime."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV_PRIME) & MASK64
+    return h
+
+
+def block_hash(parent, tokens):
+    """Hash of one full block: its parent's hash (8 bytes, little endian)
+    followed by its token ids (4 bytes each, little endian, two's complement)."""
+    data = int(parent).to_bytes(8, "little") + b"".join(
+        (int(t) & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
 
 
 class BlockManagerError(Exception):
@@ -61,21 +112,48 @@ class BlockManagerModel:
         self.ref_counts = [0] * self.num_blocks
         self.tables = {}       # seq -> list of physical block ids
         self.num_tokens = {}   # seq -> tokens held
+        # prefix cache
+        self.cache_on = False
+        self.protect_hits = 0
+        self.cache = {}        # hash -> block
+        self.block_key = {}    # cached block -> (hash, parent hash, tokens)
+        self.hits = [0] * self.num_blocks
+        self.evictable = {}    # block -> (protected, release clock)
+        self.clock = 0
+        self.tokens = {}       # seq -> known token ids (a prefix of its tokens)
+        self.registered = {}   # seq -> leading blocks already in the cache chain
+        self.counters = {"lookups": 0, "hit_blocks": 0, "miss_blocks": 0, "evictions": 0}
 
     # -- helpers -----------------------------------------------------------
     def _need(self, seq):
         if seq not in self.tables:
             raise BlockManagerError("not_found", f"unknown sequence {seq}")
 
+    def _available(self):
+        return len(self.free_blocks) + len(self.evictable)
+
     def _take(self):
-        block = self.free_blocks.pop()
+        if self.free_blocks:
+            block = self.free_blocks.pop()
+        else:  # evict the least recently released, unprotected first
+            block = min(self.evictable, key=lambda b: self.evictable[b])
+            del self.evictable[block]
+            h = self.block_key.pop(block)[0]
+            del self.cache[h]
+            self.hits[block] = 0
+            self.counters["evictions"] += 1
         self.ref_counts[block] = 1
         return block
 
     def _release(self, block):
         self.ref_counts[block] -= 1
         if self.ref_counts[block] == 0:
-            self.free_blocks.append(block)
+            if block in self.block_key:
+                prot = self.protect_hits > 0 and self.hits[block] >= self.protect_hits
+                self.evictable[block] = (prot, self.clock)
+                self.clock += 1
+            else:
+                self.free_blocks.append(block)
 
     # -- operations --------------------------------------------------------
     def allocate(self, seq, num_tokens):
@@ -84,10 +162,12 @@ class BlockManagerModel:
         if num_tokens < 0:
             raise BlockManagerError("invalid", "negative token count")
         needed = -(-num_tokens // self.block_size)
-        if len(self.free_blocks) < needed:
+        if self._available() < needed:
             raise BlockManagerError("oom", "out of KV cache blocks")
         self.tables[seq] = [self._take() for _ in range(needed)]
         self.num_tokens[seq] = num_tokens
+        self.tokens[seq] = []
+        self.registered[seq] = 0
         return list(self.tables[seq])
 
     def share(self, seq, blocks, num_tokens):
@@ -101,6 +181,8 @@ class BlockManagerModel:
             raise BlockManagerError("invalid", "sequence ends inside a block")
         table = self.tables.setdefault(seq, [])
         self.num_tokens.setdefault(seq, 0)
+        self.tokens.setdefault(seq, [])
+        self.registered.setdefault(seq, 0)
         for b in blocks:
             self.ref_counts[b] += 1
             table.append(b)
@@ -112,6 +194,8 @@ class BlockManagerModel:
             raise BlockManagerError("invalid", f"sequence {child} already exists")
         self.tables[child] = list(self.tables[parent])
         self.num_tokens[child] = self.num_tokens[parent]
+        self.tokens[child] = list(self.tokens[parent])
+        self.registered[child] = self.registered[parent]
         for b in self.tables[child]:
             self.ref_counts[b] += 1
 
@@ -123,11 +207,11 @@ class BlockManagerModel:
         offset = t % self.block_size
         cow_src = cow_dst = -1
         if offset == 0:
-            if not self.free_blocks:
+            if not self._available():
                 raise BlockManagerError("oom", "out of KV cache blocks")
             table.append(self._take())
         elif self.ref_counts[table[-1]] > 1:
-            if not self.free_blocks:
+            if not self._available():
                 raise BlockManagerError("oom", "out of KV cache blocks")
             old = table[-1]
             new = self._take()
@@ -142,6 +226,92 @@ class BlockManagerModel:
         for b in self.tables.pop(seq):
             self._release(b)
         del self.num_tokens[seq]
+        del self.tokens[seq]
+        del self.registered[seq]
+
+    # -- prefix cache ------------------------------------------------------
+    def enable_prefix_cache(self, protect_hits=0):
+        if self.tables or protect_hits < 0:
+            raise BlockManagerError("invalid", "enable the prefix cache on an empty manager")
+        self.cache_on = True
+        self.protect_hits = int(protect_hits)
+
+    def _chain(self, seq, upto):
+        """Hashes of the sequence's first ``upto`` full blocks."""
+        toks, bs, h, out = self.tokens[seq], self.block_size, 0, []
+        for i in range(upto):
+            h = block_hash(h, toks[i * bs:(i + 1) * bs])
+            out.append(h)
+        return out
+
+    def allocate_prompt(self, seq, tokens):
+        """Returns (table, cached_tokens)."""
+        if not self.cache_on:
+            raise BlockManagerError("invalid", "prefix cache is off")
+        if seq in self.tables:
+            raise BlockManagerError("invalid", f"sequence {seq} already exists")
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        matched, parent = [], 0
+        for i in range(len(tokens) // bs):
+            blk = tokens[i * bs:(i + 1) * bs]
+            h = block_hash(parent, blk)
+            b = self.cache.get(h)
+            if b is None or self.block_key[b][1:] != (parent, blk):
+                break
+            matched.append(b)
+            parent = h
+        needed = -(-len(tokens) // bs) - len(matched)
+        if self._available() - sum(1 for b in matched if b in self.evictable) < needed:
+            raise BlockManagerError("oom", "out of KV cache blocks")
+        self.counters["lookups"] += 1
+        self.counters["hit_blocks"] += len(matched)
+        self.counters["miss_blocks"] += len(tokens) // bs - len(matched)
+        for b in matched:
+            if self.ref_counts[b] == 0:
+                del self.evictable[b]
+            self.ref_counts[b] += 1
+            self.hits[b] += 1
+        table = matched + [self._take() for _ in range(needed)]
+        self.tables[seq] = table
+        self.num_tokens[seq] = len(tokens)
+        self.tokens[seq] = tokens
+        self.registered[seq] = len(matched)
+        return list(table), len(matched) * bs
+
+    def record_tokens(self, seq, ids):
+        self._need(seq)
+        ids = [int(t) for t in ids]
+        if len(self.tokens[seq]) + len(ids) > self.num_tokens[seq]:
+            raise BlockManagerError("invalid", "more token ids than the sequence holds")
+        self.tokens[seq].extend(ids)
+
+    def register(self, seq):
+        """Put the sequence's known full blocks into the cache; returns how
+        many blocks were newly cached."""
+        self._need(seq)
+        if not self.cache_on:
+            raise BlockManagerError("invalid", "prefix cache is off")
+        full = len(self.tokens[seq]) // self.block_size
+        hashes = self._chain(seq, full)
+        added = 0
+        for i in range(self.registered[seq], full):
+            b = self.tables[seq][i]
+            h = hashes[i]
+            if h not in self.cache and b not in self.block_key:
+                parent = hashes[i - 1] if i else 0
+                toks = self.tokens[seq][i * self.block_size:(i + 1) * self.block_size]
+                self.cache[h] = b
+                self.block_key[b] = (h, parent, toks)
+                added += 1
+        self.registered[seq] = full
+        return added
+
+    def prefix_stats(self):
+        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions)."""
+        c = self.counters
+        return (len(self.block_key), len(self.evictable), c["lookups"], c["hit_blocks"],
+                c["miss_blocks"], c["evictions"])
 
     # -- queries -----------------------------------------------------------
     def block_table(self, seq):
@@ -154,7 +324,8 @@ class BlockManagerModel:
         return self.ref_counts[block]
 
     def stats(self):
-        """(free, used, shared): used = count >= 1, shared = count >= 2."""
+        """(free, used, shared): free counts evictable cached blocks too;
+        used = count >= 1, shared = count >= 2."""
         used = sum(1 for c in self.ref_counts if c >= 1)
         shared = sum(1 for c in self.ref_counts if c >= 2)
-        return len(self.free_blocks), used, shared
+        return self._available(), used, shared

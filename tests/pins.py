@@ -178,8 +178,10 @@ def invariants_hold(bm):
             refs[b] += 1
     free = set(bm.free_blocks)
     held = {b for b in range(bm.num_blocks) if refs[b] > 0}
+    idle = set(getattr(bm, "evictable", ()))   # cached, unreferenced (prefix cache)
     return (refs == list(bm.ref_counts) and len(free) == len(bm.free_blocks)
-            and free.isdisjoint(held) and free | held == set(range(bm.num_blocks)))
+            and free.isdisjoint(held) and idle.isdisjoint(held) and free.isdisjoint(idle)
+            and free | held | idle == set(range(bm.num_blocks)))
 
 
 def bm_fork_cow_example(model_cls):
@@ -399,3 +401,129 @@ def i8_decode_is_sdpa_on_dequantised(decode_i8, dequantize):
         if not np.allclose(out[s], ref.numpy(), rtol=0, atol=1e-12):
             return False
     return True
+
+
+# --------------------------------------------------------------------------
+# prefix-cache pins ([KVPA] §8.1-§8.2; [KV2P] §4.2-§4.3; [NANO] §3.2, §4.3)
+# --------------------------------------------------------------------------
+def fnv_vectors(fnv):
+    """Published FNV-1a 64-bit test values."""
+    return (fnv(b"") == 0xCBF29CE484222325 and fnv(b"a") == 0xAF63DC4C8601EC8C
+            and fnv(b"foobar") == 0x85944171F73967E8)
+
+
+def _toks(seed, n, lo=0, hi=32000):
+    return np.random.default_rng(seed).integers(lo, hi, n).tolist()
+
+
+def system_prompt_stored_once(model_cls):
+    """100 requests with the same 512-token system prompt keep one copy of its
+    32 blocks: every request after the first reuses all of them."""
+    bs, sys_prompt = 16, _toks(1, 512)
+    m = model_cls(4096, bs)
+    m.enable_prefix_cache()
+    got = []
+    for r in range(100):
+        table, cached = m.allocate_prompt(r, sys_prompt + _toks(100 + r, 20))
+        m.register(r)
+        got.append((table, cached))
+    shared = got[0][0][:32]
+    ok = got[0][1] == 0 and all(c == 512 and t[:32] == shared for t, c in got[1:])
+    ok &= all(m.ref_count(b) == 100 for b in shared)
+    ok &= m.stats()[1] == 32 + 100 * 2
+    return bool(ok)
+
+
+def position_matters(model_cls):
+    """A block's hash covers its position: the same 16 tokens after a
+    different prefix do not match."""
+    bs = 16
+    a, b, c = _toks(2, 16), _toks(3, 16), _toks(4, 16)
+    m = model_cls(64, bs)
+    m.enable_prefix_cache()
+    m.allocate_prompt(0, a + b)
+    m.register(0)
+    _, c1 = m.allocate_prompt(1, b + a)
+    _, c2 = m.allocate_prompt(2, a + c)
+    _, c3 = m.allocate_prompt(3, c + b)
+    _, c4 = m.allocate_prompt(4, a + b + c)
+    return (c1, c2, c3, c4) == (0, 16, 0, 32)
+
+
+def multi_turn_reuses_full_blocks(model_cls):
+    """Turn 2 repeats turn 1 and extends it: the full blocks of turn 1 are
+    reused, its partial last block is not."""
+    bs = 16
+    t1 = _toks(5, 40)                      # 2 full blocks + 8 tokens
+    m = model_cls(64, bs)
+    m.enable_prefix_cache()
+    table1, c1 = m.allocate_prompt(0, t1)
+    n_reg = m.register(0)
+    m.free(0)
+    table2, c2 = m.allocate_prompt(1, t1 + _toks(6, 50))
+    # (the freed partial block may come back as a fresh block: ids are policy)
+    return c1 == 0 and n_reg == 2 and c2 == 32 and table2[:2] == table1[:2] \
+        and m.prefix_stats()[3] == 2
+
+
+def lru_spares_referenced_blocks(model_cls):
+    """Eviction takes the least recently released cached block and never one
+    that a live sequence holds."""
+    bs = 4
+    A, B, C = _toks(7, 8), _toks(8, 8), _toks(9, 8)
+    m = model_cls(8, bs)
+    m.enable_prefix_cache()
+    m.allocate_prompt("A", A)
+    m.register("A")                        # A stays alive
+    for s, t in (("B", B), ("C", C)):
+        m.allocate_prompt(s, t)
+        m.register(s)
+    m.free("B")                            # released first
+    m.free("C")
+    m.allocate("big", 10)                  # 3 blocks: 2 free + 1 evicted
+    evicted_first_b = m.prefix_stats()[5] == 1
+    _, cc = m.allocate_prompt("C2", C)     # C and A still match whole
+    _, ca = m.allocate_prompt("A2", A)
+    m.free("big")
+    _, cb = m.allocate_prompt("B2", B)     # B lost its first block: no match
+    return bool(evicted_first_b and cb == 0 and cc == 8 and ca == 8)
+
+
+def protection_keeps_hot_prefix(model_cls):
+    """With protect_hits = 2 a block hit twice outlives a once-hit block that
+    was released later (plain LRU would evict the hot one first)."""
+    bs = 4
+    hot, cold = _toks(10, 4), _toks(11, 4)
+    m = model_cls(4, bs)
+    m.enable_prefix_cache(protect_hits=2)
+    for s in ("h0", "h1", "h2"):          # hot block: cached, then hit twice
+        m.allocate_prompt(s, hot)
+        m.register(s)
+    m.allocate_prompt("c0", cold)
+    m.register("c0")
+    m.allocate_prompt("c1", cold)          # cold: one hit
+    for s in ("h0", "h1", "h2"):
+        m.free(s)                          # hot released first
+    m.free("c0")
+    m.free("c1")
+    m.allocate("big", 12)                  # 3 blocks: 2 free + 1 evicted
+    _, ch = m.allocate_prompt("h3", hot)
+    m.free("big")
+    _, cc = m.allocate_prompt("c2", cold)
+    return ch == 4 and cc == 0
+
+
+def prefix_invariants(m):
+    """Cache bookkeeping: evictable = cached with count 0, free blocks are not
+    cached, free + evictable + held partition the pool, the hash map and the
+    per-block keys agree."""
+    n = m.num_blocks
+    held = {b for b in range(n) if m.ref_counts[b] > 0}
+    free = set(m.free_blocks)
+    ev = set(m.evictable)
+    cached = set(m.block_key)
+    ok = ev == {b for b in cached if m.ref_counts[b] == 0}
+    ok &= not (free & cached) and len(free) == len(m.free_blocks)
+    ok &= (free | ev | held) == set(range(n)) and not (free & held) and not (ev & held)
+    ok &= all(m.cache[k[0]] == b for b, k in m.block_key.items()) and len(m.cache) == len(cached)
+    return bool(ok)

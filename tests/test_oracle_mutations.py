@@ -226,3 +226,91 @@ def test_i8_write_pins_catch(mistake):
     c = i8_write_mutant(None)
     assert pins.i8_cache_round_trip(c, oracle.quantize_rows_ref, oracle.dequantize_ref)
     assert pins.i8_cow_before_scatter(c)
+
+
+# --------------------------------------------------------------------------
+# prefix-cache mutants
+# --------------------------------------------------------------------------
+import oracle.block_manager as obm
+
+
+class PositionFreeMatch(BlockManagerModel):
+    """Matches a prompt block with any cached block holding the same tokens,
+    wherever it stood."""
+
+    def allocate_prompt(self, seq, tokens):
+        by_tokens = {tuple(k[2]): b for b, k in self.block_key.items()}
+        bs = self.block_size
+        first = tokens[:bs]
+        b = by_tokens.get(tuple(int(t) for t in first))
+        if b is not None and len(tokens) >= bs:
+            # pretend the block was cached under the chain that leads here
+            h, _, toks = self.block_key[b]
+            del self.cache[h]
+            nh = obm.block_hash(0, toks)
+            self.cache[nh] = b
+            self.block_key[b] = (nh, 0, toks)
+        return super().allocate_prompt(seq, tokens)
+
+
+class MostRecentEviction(BlockManagerModel):
+    def _take(self):
+        if not self.free_blocks and self.evictable:
+            newest = max(self.evictable, key=lambda b: self.evictable[b][1])
+            self.evictable[newest] = (False, -1)          # make it the victim
+        return super()._take()
+
+
+class NoProtection(BlockManagerModel):
+    def enable_prefix_cache(self, protect_hits=0):
+        super().enable_prefix_cache(0)
+
+
+class CachesPartialBlocks(BlockManagerModel):
+    def register(self, seq):
+        added = super().register(seq)
+        n = len(self.tokens[seq])
+        if n % self.block_size and len(self.tables[seq]) > n // self.block_size:
+            b = self.tables[seq][n // self.block_size]
+            if b not in self.block_key:
+                h = obm.block_hash(0, self.tokens[seq][-(n % self.block_size):] + [seq])
+                self.cache[h] = b
+                self.block_key[b] = (h, 0, [])
+                added += 1
+        return added
+
+
+class NoReferenceOnHit(BlockManagerModel):
+    def allocate_prompt(self, seq, tokens):
+        table, cached = super().allocate_prompt(seq, tokens)
+        for b in table[:cached // self.block_size]:
+            if self.ref_counts[b] > 1:
+                self.ref_counts[b] -= 1
+        return table, cached
+
+
+PREFIX_PINS = [pins.system_prompt_stored_once, pins.position_matters,
+               pins.multi_turn_reuses_full_blocks, pins.lru_spares_referenced_blocks,
+               pins.protection_keeps_hot_prefix]
+
+
+def _prefix_pins_fail(cls):
+    bad = []
+    for p in PREFIX_PINS:
+        try:
+            ok = p(cls)
+        except BlockManagerError:
+            ok = False
+        if not ok:
+            bad.append(p.__name__)
+    return bad
+
+
+@pytest.mark.parametrize("cls", [PositionFreeMatch, MostRecentEviction, NoProtection,
+                                 CachesPartialBlocks, NoReferenceOnHit])
+def test_prefix_pins_catch(cls):
+    assert _prefix_pins_fail(cls), cls.__name__
+
+
+def test_prefix_pins_pass_the_model():
+    assert not _prefix_pins_fail(BlockManagerModel)

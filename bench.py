@@ -102,7 +102,7 @@ class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
     def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
-                 window=0, kv_dtype="f16", kv_loads="auto"):
+                 window=0, kv_dtype="f16", kv_loads="auto", prefix_cache=False):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -156,7 +156,29 @@ class Step:
         for i in torch.randperm(nb, generator=g_cpu).tolist():
             bm.free(tmp + i)
         self.bm = bm
-        if name == "shared_prefix":
+        self.prefix_info = None
+        if name == "shared_prefix" and prefix_cache:
+            # requests admitted through the prefix cache: the first one's
+            # system-prompt blocks are registered, the others find them by
+            # block-hash lookup (token ids are synthetic)
+            bm.enable_prefix_cache()
+            gen = torch.Generator().manual_seed(seed + 3)
+            sys_ids = torch.randint(0, 32000, (self.prefix,), generator=gen).tolist()
+            prompts = [sys_ids + torch.randint(0, 32000, (n - self.prefix,), generator=gen).tolist()
+                       for n in lens0]
+            t0 = time.perf_counter()
+            for s_, toks in enumerate(prompts):
+                bm.allocate_prompt(s_, toks)
+                bm.register(s_)
+            admit = time.perf_counter() - t0
+            st_ = bm.prefix_stats()
+            self.prefix_info = {"admitted_prompts": len(prompts),
+                                "admit_us_per_prompt": round(admit / len(prompts) * 1e6, 2),
+                                "cached_blocks": st_[0], "hit_blocks": st_[3],
+                                "missed_full_blocks": st_[4]}
+            self.fork_child = S - 1
+            self.rng = torch.Generator().manual_seed(seed + 1)
+        elif name == "shared_prefix":
             self.prefix_seq = 1 << 41
             bm.allocate(self.prefix_seq, self.prefix)
             pblocks, _ = bm.block_table(self.prefix_seq)
@@ -434,6 +456,9 @@ def main():
                     help="i8: INT8 pool with one float32 scale per (token, head) row")
     ap.add_argument("--kv-loads", default="auto", choices=["auto", "cached", "streaming"],
                     help="K/V load policy (auto: cached for shared_prefix, else streaming)")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="shared_prefix: admit the requests through the block manager's prefix "
+                         "cache (block-hash lookup) instead of sharing the prefix by hand")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -459,7 +484,7 @@ def main():
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
               args.partition, dev, context=args.context, window=args.window,
-              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads)
+              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads, prefix_cache=args.prefix_cache)
     step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -523,6 +548,7 @@ def main():
         "decode_us": round(dec_avg_s * 1e6, 2),
         "decode_seq_ctx_tokens_per_s": round(total_tokens / args.steps / dec_avg_s, 1),
         "cow_pairs_per_step": round(sum(st.ncow) / args.steps, 3),
+        "prefix_cache": st.prefix_info,
         "parity_max_abs_err": parity,
         "measured_read_ceiling": ceiling,
         "decode_frac_of_tile_ceiling": (

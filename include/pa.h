@@ -233,12 +233,58 @@ int pa_bm_block_table(const pa_bm* bm, int64_t seq, int32_t* out, int cap,
 int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int n,
                        int32_t* tables, int max_blocks, int32_t* context_lens);
 
-/* Pool counts: free blocks, blocks with count >= 1, blocks with count >= 2. */
+/* Pool counts: free blocks (plus evictable cached blocks when the prefix
+ * cache is on), blocks with count >= 1, blocks with count >= 2. */
 int pa_bm_stats(const pa_bm* bm, int64_t* num_free, int64_t* num_used,
                 int64_t* num_shared);
 
 /* Reference count of one block (>= 0), or PA_ERR_INVALID_ARG. */
 int pa_bm_ref_count(const pa_bm* bm, int32_t block);
+
+/* -------------------------------------------------------------------------
+ * 3b. Prefix cache ([KVPA] §8.1-§8.2; [KV2P] §4.2-§4.3; [NANO] §3.2, §4.3)
+ *
+ * Requests that start with the same tokens share the blocks holding them.
+ * Every full block is keyed by a chain hash of its token ids and position:
+ * h_i = FNV-1a-64 over (h_{i-1} as 8 little-endian bytes, then the block's
+ * token ids as 4 little-endian bytes each), h_{-1} = 0.  A lookup also
+ * compares the stored parent hash and token ids, so a collision never hits.
+ * Only full blocks are cached.  A cached block whose count reaches 0 stays
+ * cached and becomes evictable; fresh blocks come from the free pool first,
+ * then from evicting the least recently released evictable block, blocks
+ * with at least protect_hits hits after all others (0 = plain LRU).  A
+ * referenced block is never evicted.  With the cache on, pa_bm_stats'
+ * num_free counts free plus evictable blocks.
+ * ------------------------------------------------------------------------- */
+
+/* Turn the prefix cache on; only on a manager that holds no sequence.
+ * protect_hits >= 0. */
+int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits);
+
+/* Admit a new sequence with prompt `tokens` [n] (host int32): its leading
+ * full blocks that are cached are reused (one more reference each), the rest
+ * of the prompt gets fresh blocks.  *cached_tokens (may be NULL) receives the
+ * number of leading tokens whose K/V the reused blocks already hold; the
+ * caller writes the others.  Errors: PA_ERR_INVALID_ARG (cache off, sequence
+ * exists), PA_ERR_OOM (state unchanged). */
+int pa_bm_allocate_prompt(pa_bm* bm, int64_t seq, const int32_t* tokens,
+                          int64_t n, int64_t* cached_tokens);
+
+/* Append the ids of the tokens appended since the known ids ended (decoded
+ * tokens), so that their blocks can be registered; afterwards the known ids
+ * must cover every token the sequence holds (else PA_ERR_INVALID_ARG). */
+int pa_bm_record_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens,
+                        int64_t n);
+
+/* Cache the sequence's full blocks whose token ids are known and whose K/V
+ * the caller has written (call after the write).  A block whose key is
+ * already cached under another block stays private.  *newly_cached (may be
+ * NULL) receives the number of blocks added. */
+int pa_bm_register(pa_bm* bm, int64_t seq, int64_t* newly_cached);
+
+/* out[6]: cached blocks, evictable blocks, lookups, reused (hit) blocks,
+ * missed full blocks, evictions. */
+int pa_bm_prefix_stats(const pa_bm* bm, int64_t* out);
 
 /* ------------------------------------------------------------------------- */
 const char* pa_strerror(int status);

@@ -60,7 +60,9 @@ chunk hash to the block, reuse only full blocks).
 * ``register(seq)``: after the caller wrote the K/V of the sequence's full
   blocks, put those not yet cached into the cache (a hash already present
   keeps its block; the sequence's copy stays private).  ``record_tokens``
-  appends the ids of decoded tokens so that their blocks can be registered.
+  appends the ids of the tokens appended since the known ids ended (they
+  must bring the known ids up to the tokens held), so that decoded blocks can
+  be registered too.
 * A cached block whose count drops to 0 is not returned to the free pool: it
   becomes evictable, stamped with a release clock.  Fresh blocks come from
   the free pool first; only when it is empty is an evictable block evicted
@@ -282,8 +284,8 @@ class BlockManagerModel:
     def record_tokens(self, seq, ids):
         self._need(seq)
         ids = [int(t) for t in ids]
-        if len(self.tokens[seq]) + len(ids) > self.num_tokens[seq]:
-            raise BlockManagerError("invalid", "more token ids than the sequence holds")
+        if len(self.tokens[seq]) + len(ids) != self.num_tokens[seq]:
+            raise BlockManagerError("invalid", "token ids must complete the known prefix")
         self.tokens[seq].extend(ids)
 
     def register(self, seq):

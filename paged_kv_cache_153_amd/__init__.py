@@ -67,6 +67,11 @@ _SIGNATURES = {
     "pa_bm_append_slots": (_c.c_int, [_P, _I64P, _c.c_int, _I64P, _I32P,
                                       _c.POINTER(_c.c_int)]),
     "pa_bm_free": (_c.c_int, [_P, _c.c_int64]),
+    "pa_bm_enable_prefix_cache": (_c.c_int, [_P, _c.c_int]),
+    "pa_bm_allocate_prompt": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int64, _I64P]),
+    "pa_bm_record_tokens": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int64]),
+    "pa_bm_register": (_c.c_int, [_P, _c.c_int64, _I64P]),
+    "pa_bm_prefix_stats": (_c.c_int, [_P, _I64P]),
     "pa_bm_block_table": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int, _c.POINTER(_c.c_int),
                                      _I64P]),
     "pa_bm_block_tables": (_c.c_int, [_P, _I64P, _c.c_int, _I32P, _c.c_int, _I32P]),
@@ -359,3 +364,31 @@ class BlockManager:
         if r < 0:
             _check(r)
         return r
+
+    # -- prefix cache --------------------------------------------------------
+    def enable_prefix_cache(self, protect_hits=0):
+        _check(lib().pa_bm_enable_prefix_cache(self._h, int(protect_hits)))
+
+    def allocate_prompt(self, seq, tokens):
+        """Admit a prompt (token ids); returns (block table, cached_tokens)."""
+        n = len(tokens)
+        arr = (ctypes.c_int32 * max(1, n))(*[int(t) for t in tokens])
+        cached = ctypes.c_int64(0)
+        _check(lib().pa_bm_allocate_prompt(self._h, int(seq), arr, n, ctypes.byref(cached)))
+        return self.block_table(seq)[0], cached.value
+
+    def record_tokens(self, seq, tokens):
+        n = len(tokens)
+        arr = (ctypes.c_int32 * max(1, n))(*[int(t) for t in tokens])
+        _check(lib().pa_bm_record_tokens(self._h, int(seq), arr, n))
+
+    def register(self, seq):
+        added = ctypes.c_int64(0)
+        _check(lib().pa_bm_register(self._h, int(seq), ctypes.byref(added)))
+        return added.value
+
+    def prefix_stats(self):
+        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions)."""
+        out = (ctypes.c_int64 * 6)()
+        _check(lib().pa_bm_prefix_stats(self._h, out))
+        return tuple(out)

@@ -16,9 +16,22 @@
 // so a failing call leaves the manager as it was.  With PA_LOG=1 in the
 // environment every allocation and release is logged to stderr with the
 // sequence, block, count and free-pool size ([NANO] §4.5 logging advice).
+//
+// Prefix cache (pa_bm_enable_prefix_cache; [KVPA] §8.1-§8.2, [KV2P] §4.2-§4.3,
+// [NANO] §3.2 and §4.3): every full block that a sequence registers is keyed
+// by a chain hash of its token ids and position, h_i = FNV-1a-64(le64(h_{i-1})
+// || le32 token ids), h_{-1} = 0.  A new prompt walks its full blocks from the
+// start while they are cached (hash, parent hash and token ids all equal) and
+// takes a reference on each; the rest gets fresh blocks.  A cached block whose
+// count reaches 0 stays cached but evictable; fresh blocks come from the free
+// pool first, then by evicting the least recently released evictable block,
+// blocks with at least protect_hits hits last.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <new>
+#include <set>
+#include <tuple>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -30,6 +43,13 @@ struct pa_bm {
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t num_tokens = 0;
+    std::vector<int32_t> tokens;  // known token ids (a prefix of the sequence)
+    int64_t registered = 0;       // leading blocks already in the cache chain
+  };
+  struct Key {  // a cached block's identity
+    bool cached = false;
+    uint64_t hash = 0, parent = 0;
+    std::vector<int32_t> tokens;
   };
   int64_t num_blocks = 0;
   int block_size = 0;
@@ -37,10 +57,33 @@ struct pa_bm {
   std::vector<int32_t> refs;
   std::unordered_map<int64_t, Seq> seqs;
   bool log = false;
+  // prefix cache
+  bool cache_on = false;
+  int protect_hits = 0;
+  std::unordered_map<uint64_t, int32_t> cache;
+  std::vector<Key> keys;
+  std::vector<int64_t> hits;
+  std::set<std::tuple<int, uint64_t, int32_t>> evictable;  // (protected, clock, block)
+  std::vector<uint64_t> ev_clock;
+  std::vector<int> ev_prot;
+  uint64_t clock = 0;
+  int64_t lookups = 0, hit_blocks = 0, miss_blocks = 0, evictions = 0;
+
+  int64_t available() const { return (int64_t)free_list.size() + (int64_t)evictable.size(); }
 
   int32_t take(int64_t seq) {
-    const int32_t b = free_list.back();
-    free_list.pop_back();
+    int32_t b;
+    if (!free_list.empty()) {
+      b = free_list.back();
+      free_list.pop_back();
+    } else {  // evict the least recently released block, unprotected first
+      b = std::get<2>(*evictable.begin());
+      evictable.erase(evictable.begin());
+      cache.erase(keys[b].hash);
+      keys[b] = Key();
+      hits[b] = 0;
+      ++evictions;
+    }
     refs[b] = 1;
     if (log)
       std::fprintf(stderr, "[pa_bm] take seq=%lld block=%d ref=1 free=%zu\n", (long long)seq, b,
@@ -49,10 +92,26 @@ struct pa_bm {
   }
   void release(int64_t seq, int32_t b) {
     refs[b] -= 1;
-    if (refs[b] == 0) free_list.push_back(b);
+    if (refs[b] == 0) {
+      if (keys[b].cached) {
+        const int prot = protect_hits > 0 && hits[b] >= protect_hits;
+        evictable.insert({prot, clock, b});
+        ev_clock[b] = clock;
+        ev_prot[b] = prot;
+        ++clock;
+      } else {
+        free_list.push_back(b);
+      }
+    }
     if (log)
       std::fprintf(stderr, "[pa_bm] drop seq=%lld block=%d ref=%d free=%zu\n", (long long)seq, b,
                    refs[b], free_list.size());
+  }
+  // a reference on a cached block (a prefix hit)
+  void hold(int32_t b) {
+    if (refs[b] == 0) evictable.erase({ev_prot[b], ev_clock[b], b});
+    refs[b] += 1;
+    hits[b] += 1;
   }
   int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
 };
@@ -60,6 +119,23 @@ struct pa_bm {
 namespace {
 
 using pa::fail;
+
+// 64-bit FNV-1a (published definition: per octet, xor then multiply by the
+// prime) over the parent hash (8 bytes, little endian) and the block's token
+// ids (4 bytes each, little endian).
+uint64_t block_hash(uint64_t parent, const int32_t* tokens, int n) {
+  uint64_t h = 0xCBF29CE484222325ull;
+  auto octet = [&](uint8_t x) {
+    h ^= x;
+    h *= 0x100000001B3ull;
+  };
+  for (int i = 0; i < 8; ++i) octet((uint8_t)(parent >> (8 * i)));
+  for (int k = 0; k < n; ++k) {
+    const uint32_t t = (uint32_t)tokens[k];
+    for (int i = 0; i < 4; ++i) octet((uint8_t)(t >> (8 * i)));
+  }
+  return h;
+}
 
 int need_seq(const pa_bm* bm, int64_t seq) {
   if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
@@ -120,6 +196,10 @@ pa_bm* pa_bm_create(int64_t num_blocks, int block_size) {
     bm->free_list.resize(num_blocks);
     for (int64_t i = 0; i < num_blocks; ++i) bm->free_list[i] = (int32_t)i;
     bm->refs.assign(num_blocks, 0);
+    bm->keys.resize(num_blocks);
+    bm->hits.assign(num_blocks, 0);
+    bm->ev_clock.assign(num_blocks, 0);
+    bm->ev_prot.assign(num_blocks, 0);
     const char* env = std::getenv("PA_LOG");
     bm->log = env && env[0] == '1';
   } catch (...) {
@@ -138,7 +218,7 @@ int pa_bm_allocate(pa_bm* bm, int64_t seq, int64_t num_tokens) {
   if (bm->seqs.count(seq))
     return fail(PA_ERR_INVALID_ARG, "sequence " + std::to_string(seq) + " already exists");
   const int64_t needed = bm->blocks_for(num_tokens);
-  if ((int64_t)bm->free_list.size() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
+  if (bm->available() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
   try {
     pa_bm::Seq s;
     s.blocks.reserve(needed);
@@ -200,7 +280,7 @@ int pa_bm_append_slot(pa_bm* bm, int64_t seq, int64_t* slot, int32_t* cow_src,
   if (int st = need_seq(bm, seq)) return st;
   pa_bm::Seq& s = bm->seqs.at(seq);
   std::unordered_map<int32_t, int> dropped;
-  if ((int64_t)bm->free_list.size() < plan_append(bm, s, dropped))
+  if (bm->available() < plan_append(bm, s, dropped))
     return fail(PA_ERR_OOM, "out of KV cache blocks");
   do_append(bm, seq, s, slot, cow_src, cow_dst);
   return PA_OK;
@@ -223,7 +303,7 @@ int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int64_t* slots,
       return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seqs[i]));
     // fail at the first sequence that would not fit, as a sequential run would
     needed += plan_append(bm, it->second, dropped);
-    if ((int64_t)bm->free_list.size() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
+    if (bm->available() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
   }
   int k = 0;
   for (int i = 0; i < n; ++i) {
@@ -294,9 +374,131 @@ int pa_bm_stats(const pa_bm* bm, int64_t* num_free, int64_t* num_used, int64_t* 
     used += c >= 1;
     shared += c >= 2;
   }
-  if (num_free) *num_free = (int64_t)bm->free_list.size();
+  if (num_free) *num_free = bm->available();
   if (num_used) *num_used = used;
   if (num_shared) *num_shared = shared;
+  return PA_OK;
+}
+
+int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (!bm->seqs.empty() || protect_hits < 0)
+    return fail(PA_ERR_INVALID_ARG, "enable the prefix cache on an empty manager");
+  bm->cache_on = true;
+  bm->protect_hits = protect_hits;
+  return PA_OK;
+}
+
+int pa_bm_allocate_prompt(pa_bm* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                          int64_t* cached_tokens) {
+  pa::clear_error();
+  if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
+  if (!bm->cache_on) return fail(PA_ERR_INVALID_ARG, "prefix cache is off");
+  if (n < 0 || (n > 0 && !tokens)) return fail(PA_ERR_INVALID_ARG, "bad token array");
+  if (bm->seqs.count(seq))
+    return fail(PA_ERR_INVALID_ARG, "sequence " + std::to_string(seq) + " already exists");
+  const int bs = bm->block_size;
+  std::vector<int32_t> matched;
+  uint64_t parent = 0;
+  int64_t evictable_hits = 0;
+  for (int64_t i = 0; i < n / bs; ++i) {
+    const int32_t* blk = tokens + i * bs;
+    const uint64_t h = block_hash(parent, blk, bs);
+    auto it = bm->cache.find(h);
+    if (it == bm->cache.end()) break;
+    const pa_bm::Key& k = bm->keys[it->second];
+    if (k.parent != parent || !std::equal(k.tokens.begin(), k.tokens.end(), blk)) break;
+    matched.push_back(it->second);
+    evictable_hits += bm->refs[it->second] == 0;
+    parent = h;
+  }
+  const int64_t needed = bm->blocks_for(n) - (int64_t)matched.size();
+  if (bm->available() - evictable_hits < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
+  try {
+    pa_bm::Seq s;
+    s.blocks.reserve(bm->blocks_for(n));
+    s.tokens.assign(tokens, tokens + n);
+    bm->seqs.reserve(bm->seqs.size() + 1);
+    bm->lookups += 1;
+    bm->hit_blocks += (int64_t)matched.size();
+    bm->miss_blocks += n / bs - (int64_t)matched.size();
+    for (int32_t b : matched) {
+      bm->hold(b);
+      s.blocks.push_back(b);
+    }
+    for (int64_t i = 0; i < needed; ++i) s.blocks.push_back(bm->take(seq));
+    s.num_tokens = n;
+    s.registered = (int64_t)matched.size();
+    bm->seqs.emplace(seq, std::move(s));
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  if (cached_tokens) *cached_tokens = (int64_t)matched.size() * bs;
+  return PA_OK;
+}
+
+int pa_bm_record_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens, int64_t n) {
+  pa::clear_error();
+  if (int st = need_seq(bm, seq)) return st;
+  if (n < 0 || (n > 0 && !tokens)) return fail(PA_ERR_INVALID_ARG, "bad token array");
+  pa_bm::Seq& s = bm->seqs.at(seq);
+  if ((int64_t)s.tokens.size() + n != s.num_tokens)
+    return fail(PA_ERR_INVALID_ARG, "token ids must complete the known prefix");
+  try {
+    s.tokens.insert(s.tokens.end(), tokens, tokens + n);
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  return PA_OK;
+}
+
+int pa_bm_register(pa_bm* bm, int64_t seq, int64_t* newly_cached) {
+  pa::clear_error();
+  if (int st = need_seq(bm, seq)) return st;
+  if (!bm->cache_on) return fail(PA_ERR_INVALID_ARG, "prefix cache is off");
+  pa_bm::Seq& s = bm->seqs.at(seq);
+  const int bs = bm->block_size;
+  const int64_t full = (int64_t)s.tokens.size() / bs;
+  int64_t added = 0;
+  try {
+    uint64_t parent = 0;
+    for (int64_t i = 0; i < full; ++i) {
+      const int32_t* blk = s.tokens.data() + i * bs;
+      const uint64_t h = block_hash(parent, blk, bs);
+      if (i >= s.registered) {
+        const int32_t b = s.blocks[i];
+        if (!bm->cache.count(h) && !bm->keys[b].cached) {
+          pa_bm::Key& k = bm->keys[b];
+          k.tokens.assign(blk, blk + bs);
+          k.hash = h;
+          k.parent = parent;
+          k.cached = true;
+          bm->cache.emplace(h, b);
+          ++added;
+        }
+      }
+      parent = h;
+    }
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  s.registered = full;
+  if (newly_cached) *newly_cached = added;
+  return PA_OK;
+}
+
+int pa_bm_prefix_stats(const pa_bm* bm, int64_t* out) {
+  pa::clear_error();
+  if (!bm || !out) return fail(PA_ERR_INVALID_ARG, "null argument");
+  int64_t cached = 0;
+  for (const auto& k : bm->keys) cached += k.cached;
+  out[0] = cached;
+  out[1] = (int64_t)bm->evictable.size();
+  out[2] = bm->lookups;
+  out[3] = bm->hit_blocks;
+  out[4] = bm->miss_blocks;
+  out[5] = bm->evictions;
   return PA_OK;
 }
 

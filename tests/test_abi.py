@@ -221,3 +221,107 @@ def test_native_block_manager_matches_model(ops, bs, nb):
             t, ntok = ref.block_table(s_)
             assert row == t + [-1] * (mb - len(t)) and ln == ntok
     bm.close()
+
+
+# --------------------------------------------------------------------------
+# native prefix cache == oracle model
+# --------------------------------------------------------------------------
+def _prompts(seed):
+    """Prompts with shared prefixes: a system part, then one of two topics,
+    then a private tail (token ids from a small vocabulary)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    sys_ = rng.integers(0, 50, 24).tolist()
+    topics = [rng.integers(0, 50, 10).tolist() for _ in range(2)]
+    out = []
+    for k in range(6):
+        tail = rng.integers(0, 50, int(rng.integers(0, 12))).tolist()
+        out.append(sys_ + topics[k % 2] + tail if k < 5 else tail)
+    return out
+
+
+PREFIX_OPS = st.lists(st.tuples(st.sampled_from(["prompt", "register", "decode", "free",
+                                                 "fork", "alloc", "batch"]),
+                                st.integers(0, 5), st.integers(0, 5), st.integers(0, 40)),
+                      max_size=50)
+
+
+@settings(max_examples=120, deadline=None)
+@given(ops=PREFIX_OPS, bs=st.sampled_from([2, 4, 8]), nb=st.integers(4, 40),
+       protect=st.integers(0, 2), seed=st.integers(0, 3))
+def test_native_prefix_cache_matches_model(ops, bs, nb, protect, seed):
+    ref, bm = BlockManagerModel(nb, bs), pa.BlockManager(nb, bs)
+    ref.enable_prefix_cache(protect)
+    bm.enable_prefix_cache(protect)
+    prompts = _prompts(seed)
+    for op, a, b, n in ops:
+        if op == "prompt":
+            w, g = _run_both(lambda: ref.allocate_prompt(a, prompts[b]),
+                             lambda: bm.allocate_prompt(a, prompts[b]))
+            assert w == g
+        elif op == "register":
+            w, g = _run_both(lambda: ref.register(a), lambda: bm.register(a))
+            assert w == g
+        elif op == "decode":
+            w, g = _run_both(lambda: ref.append_slot(a), lambda: bm.append_slot(a))
+            assert w == g
+            if w is not None:
+                _run_both(lambda: ref.record_tokens(a, [n]), lambda: bm.record_tokens(a, [n]))
+        elif op == "free":
+            _run_both(lambda: ref.free(a), lambda: bm.free(a))
+        elif op == "fork":
+            _run_both(lambda: ref.fork(a, b), lambda: bm.fork(a, b))
+        elif op == "alloc":
+            _run_both(lambda: ref.allocate(a, n), lambda: bm.allocate(a, n))
+        elif op == "batch":
+            import copy
+            seqs = sorted({a, b})
+            trial = copy.deepcopy(ref)
+            try:
+                want = [trial.append_slot(x) for x in seqs]
+                werr = None
+            except BlockManagerError as e:
+                want, werr = None, KIND[e.kind]
+            try:
+                slots, pairs = bm.append_slots(seqs)
+                gerr = None
+            except pa.PAError as e:
+                gerr = e.status
+            assert werr == gerr
+            if werr is None:
+                ref = trial
+                assert slots == [x[0] for x in want]
+        assert bm.stats() == ref.stats()
+        assert bm.prefix_stats() == ref.prefix_stats()
+        for blk in range(nb):
+            assert bm.ref_count(blk) == ref.ref_count(blk)
+        for seq in ref.tables:
+            assert bm.block_table(seq) == ref.block_table(seq)
+    bm.close()
+
+
+def test_native_prefix_cache_rejects_bad_use():
+    bm = pa.BlockManager(8, 4)
+    with pytest.raises(pa.PAError) as e:
+        bm.allocate_prompt(0, [1, 2, 3])
+    assert e.value.status == -1            # cache off
+    bm.allocate(5, 3)
+    with pytest.raises(pa.PAError) as e:
+        bm.enable_prefix_cache()
+    assert e.value.status == -1            # not empty
+    bm.free(5)
+    bm.enable_prefix_cache()
+    bm.allocate_prompt(0, [1, 2, 3, 4, 5])
+    with pytest.raises(pa.PAError) as e:
+        bm.record_tokens(0, [9])           # more ids than tokens held
+    assert e.value.status == -1
+    bm.append_slot(0)
+    bm.append_slot(0)
+    with pytest.raises(pa.PAError) as e:
+        bm.record_tokens(0, [9])           # two appended, one id
+    assert e.value.status == -1
+    bm.record_tokens(0, [9, 10])
+    with pytest.raises(pa.PAError) as e:
+        bm.allocate_prompt(0, [1])         # exists
+    assert e.value.status == -1
+    bm.close()

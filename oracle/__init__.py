@@ -22,7 +22,8 @@ Sources cited in the modules (page title, then the section on that page):
 Modules:
 
 * ``attention``      — decode attention over a paged cache (definition),
-                       the split-context partials and their log-sum-exp merge.
+                       causal multi-token (chunked prefill) attention, the
+                       split-context partials and their log-sum-exp merge.
 * ``cache``          — the slot-mapped K/V scatter and block copy-on-write.
 * ``block_manager``  — a dict/list model of the host block manager.
 * ``kv_size``        — closed forms for KV-cache sizes and block counts.
@@ -35,7 +36,7 @@ pages, library routines on contiguous data, invariants).  No function is
 "parity unpinned".
 """
 
-from .attention import decode_ref, gather_sequence, split_ref, merge_ref
+from .attention import decode_ref, gather_sequence, split_ref, merge_ref, prefill_ref
 from .cache import cache_write_ref
 from .block_manager import BlockManagerModel, BlockManagerError
 from .quant import (quantize_rows_ref, dequantize_ref, cache_write_i8_ref, decode_i8_ref)
@@ -43,6 +44,7 @@ from . import kv_size
 
 __all__ = [
     "decode_ref",
+    "prefill_ref",
     "gather_sequence",
     "split_ref",
     "merge_ref",

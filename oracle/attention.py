@@ -39,6 +39,17 @@ contexts: each new token attends only to the last W tokens.  With
 ``window = W > 0`` the keys are tokens ``t`` with ``max(0, n - W) <= t < n``;
 ``window = 0`` means the whole context.
 
+Multi-token queries (chunked prefill)
+-------------------------------------
+A prefill chunk brings T > 1 new tokens per sequence at once ([KV2P] §5.4:
+a long prompt's prefill is split into chunks; [INFRA] §2: with T > 1 the
+scores need a causal mask).  The chunk's K/V are written to the cache first;
+query ``i`` of the chunk sits at position ``p = n - T + i`` and attends to the
+keys ``t <= p``.  Reading: the page's mask is square (``tril(T, T)``) while
+its scores span past + T keys; the plain reading is the mask aligned to the
+end (each query sees all past tokens and the chunk tokens up to itself),
+which for T = 1 is the decode case and for n = T is the square mask.
+
 Split-context partials
 ----------------------
 The pages merge block results with decay factors ([KVPA] §7.2 running max /
@@ -110,6 +121,41 @@ def decode_ref(q, kv_cache, block_tables, context_lens, scale, window=0):
         for h in range(num_q_heads):
             g = h // group
             out[s, h] = _attend(q[s, h].astype(np.float64), k[:, g, :], v[:, g, :], scale)
+    return out
+
+
+def prefill_ref(q, kv_cache, block_tables, context_lens, query_start, scale):
+    """Causal attention of multi-token queries over a paged cache.
+
+    q:            [total_q, Hq, D], the queries of sequence s are rows
+                  ``query_start[s] .. query_start[s+1]-1`` (T_s of them)
+    context_lens: [S], n_s, counting the chunk (n_s >= T_s)
+    query_start:  [S+1] increasing, query_start[0] = 0
+    returns       [total_q, Hq, D] float64: row ``query_start[s] + i`` is the
+                  attention of query i over keys t <= n_s - T_s + i
+    """
+    q = np.asarray(q)
+    total, num_q_heads, head_dim = q.shape
+    num_kv_heads = kv_cache.shape[2]
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(len(context_lens)):
+        n = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        T = q1 - q0
+        if T == 0:
+            continue
+        if T > n:
+            raise ValueError("a chunk cannot be longer than its context")
+        k, v = gather_sequence(kv_cache, block_tables[s], n)
+        k = k.astype(np.float64)
+        v = v.astype(np.float64)
+        for i in range(T):
+            p = n - T + i
+            for h in range(num_q_heads):
+                g = h // group
+                out[q0 + i, h] = _attend(q[q0 + i, h].astype(np.float64), k[:p + 1, g, :],
+                                         v[:p + 1, g, :], scale)
     return out
 
 

@@ -527,3 +527,79 @@ def prefix_invariants(m):
     ok &= (free | ev | held) == set(range(n)) and not (free & held) and not (ev & held)
     ok &= all(m.cache[k[0]] == b for b, k in m.block_key.items()) and len(m.cache) == len(cached)
     return bool(ok)
+
+
+# --------------------------------------------------------------------------
+# multi-token (chunked prefill) pins ([KV2P] §5.4; [INFRA] §2)
+# --------------------------------------------------------------------------
+def _scatter(ks, vs, bs, seed):
+    rng = np.random.default_rng(seed)
+    hkv, d = ks[0].shape[1], ks[0].shape[2]
+    nbs = [-(-k.shape[0] // bs) for k in ks]
+    nb = sum(nbs) + 3
+    pool = rng.standard_normal((nb, 2, hkv, bs, d))
+    perm = rng.permutation(nb)
+    tables = np.full((len(ks), max(nbs)), -1, dtype=np.int64)
+    pos = 0
+    for s, (k, v) in enumerate(zip(ks, vs)):
+        for i in range(nbs[s]):
+            b = perm[pos]
+            pos += 1
+            tables[s, i] = b
+            pool[b, 0, :, :k[i * bs:(i + 1) * bs].shape[0]] = k[i * bs:(i + 1) * bs].transpose(1, 0, 2)
+            pool[b, 1, :, :v[i * bs:(i + 1) * bs].shape[0]] = v[i * bs:(i + 1) * bs].transpose(1, 0, 2)
+    return pool, tables
+
+
+def prefill_is_masked_sdpa(prefill, seed=11):
+    """Each sequence's chunk equals SDPA on its contiguous K/V with a causal
+    mask aligned to the end of the context (is_causal when n = T)."""
+    rng = np.random.default_rng(seed)
+    lens, chunks, hq, hkv, d, bs = (40, 17, 64, 9), (40, 5, 20, 1), 8, 2, 16, 8
+    ks = [rng.standard_normal((n, hkv, d)) for n in lens]
+    vs = [rng.standard_normal((n, hkv, d)) for n in lens]
+    pool, tables = _scatter(ks, vs, bs, seed)
+    qstart = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((int(qstart[-1]), hq, d))
+    out = prefill(q, pool, tables, np.array(lens), qstart, 0.3)
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        kt = torch.from_numpy(ks[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vs[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        qt = torch.from_numpy(q[qstart[s]:qstart[s + 1]]).permute(1, 0, 2)      # [Hq, T, D]
+        if n == T:
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True,
+                                                                   scale=0.3)
+        else:
+            allowed = torch.arange(n)[None, :] <= (n - T + torch.arange(T))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed,
+                                                                   scale=0.3)
+        if not np.allclose(out[qstart[s]:qstart[s + 1]], ref.permute(1, 0, 2).numpy(),
+                           rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def prefill_single_token_is_decode(prefill, decode):
+    """T = 1 for every sequence is the decode case, exactly."""
+    rng = np.random.default_rng(12)
+    kv = rng.standard_normal((12, 2, 2, 8, 16))
+    bt = np.array([[3, 1, 7], [4, 0, 11]])
+    lens = np.array([20, 9])
+    q = rng.standard_normal((2, 4, 16))
+    return bool(np.array_equal(prefill(q, kv, bt, lens, np.array([0, 1, 2]), 0.5),
+                               decode(q, kv, bt, lens, 0.5)))
+
+
+def chunked_equals_whole(prefill, seed=13):
+    """Prefilling a prompt in two chunks (the second with the first as its
+    past) gives the rows of prefilling it at once."""
+    rng = np.random.default_rng(seed)
+    n, t1, hq, hkv, d, bs = 37, 15, 4, 4, 8, 4
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    pool, tables = _scatter([k], [v], bs, seed)
+    q = rng.standard_normal((n, hq, d))
+    whole = prefill(q, pool, tables, np.array([n]), np.array([0, n]), 0.2)
+    a = prefill(q[:t1], pool, tables, np.array([t1]), np.array([0, t1]), 0.2)
+    b = prefill(q[t1:], pool, tables, np.array([n]), np.array([0, n - t1]), 0.2)
+    return bool(np.allclose(np.concatenate([a, b]), whole, rtol=0, atol=1e-12))

@@ -314,3 +314,50 @@ def test_prefix_pins_catch(cls):
 
 def test_prefix_pins_pass_the_model():
     assert not _prefix_pins_fail(BlockManagerModel)
+
+
+# --------------------------------------------------------------------------
+# multi-token (causal) mutants
+# --------------------------------------------------------------------------
+def prefill_mutant(mistake):
+    def prefill(q, kv, bt, cl, qstart, scale):
+        q = np.asarray(q, dtype=np.float64)
+        total, hq, d = q.shape
+        hkv, bs = kv.shape[2], kv.shape[3]
+        G = hq // hkv
+        out = np.zeros((total, hq, d))
+        for s in range(len(cl)):
+            n, q0, q1 = int(cl[s]), int(qstart[s]), int(qstart[s + 1])
+            T = q1 - q0
+            t = np.arange(n)
+            blk = np.asarray(bt[s])[t // bs]
+            k = kv[blk, 0, :, t % bs, :].astype(np.float64)
+            v = kv[blk, 1, :, t % bs, :].astype(np.float64)
+            for i in range(T):
+                p = n - T + i
+                if mistake == "top_left":       # the square mask applied to the first keys
+                    p = i
+                if mistake == "strict":
+                    p -= 1
+                p = max(p, 0)
+                for h in range(hq):
+                    z = scale * (k[:p + 1, h // G] @ q[q0 + i, h])
+                    w = np.exp(z - z.max())
+                    out[q0 + i, h] = (w @ v[:p + 1, h // G]) / w.sum()
+        return out
+    return prefill
+
+
+def _prefill_pins_fail(f):
+    return not (pins.prefill_is_masked_sdpa(f) and pins.chunked_equals_whole(f)
+                and pins.prefill_single_token_is_decode(f, oracle.decode_ref))
+
+
+@pytest.mark.parametrize("mistake", ["top_left", "strict"])
+def test_prefill_pins_catch(mistake):
+    assert _prefill_pins_fail(prefill_mutant(mistake))
+
+
+def test_prefill_pins_pass_clean_copy():
+    assert not _prefill_pins_fail(prefill_mutant(None))
+    assert not _prefill_pins_fail(oracle.prefill_ref)

@@ -296,3 +296,27 @@ def test_window_larger_than_context_is_full_attention():
             x.scale)
     assert np.array_equal(oracle.decode_ref(*args, window=300), oracle.decode_ref(*args))
     assert not np.allclose(oracle.decode_ref(*args, window=299), oracle.decode_ref(*args))
+
+
+# --------------------------------------------------------------------------
+# multi-token queries with a causal mask ([KV2P] §5.4; [INFRA] §2)
+# --------------------------------------------------------------------------
+def test_prefill_is_end_aligned_causal_sdpa():
+    assert _pins.prefill_is_masked_sdpa(oracle.prefill_ref)
+
+
+def test_prefill_single_token_is_decode():
+    assert _pins.prefill_single_token_is_decode(oracle.prefill_ref, oracle.decode_ref)
+
+
+def test_prefill_in_chunks_equals_at_once():
+    assert _pins.chunked_equals_whole(oracle.prefill_ref)
+
+
+def test_prefill_first_query_of_fresh_prompt_is_its_value_row():
+    """n = T: query 0 sees only key 0, whose V row it returns."""
+    rng = np.random.default_rng(14)
+    kv = rng.standard_normal((4, 2, 1, 8, 8))
+    q = rng.standard_normal((5, 2, 8))
+    out = oracle.prefill_ref(q, kv, np.array([[2, 0]]), np.array([5]), np.array([0, 5]), 1.0)
+    assert np.array_equal(out[0, 0], kv[2, 1, 0, 0]) and np.array_equal(out[0, 1], kv[2, 1, 0, 0])

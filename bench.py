@@ -437,6 +437,100 @@ def parity_sample(st, samples=3):
     return float(np.abs(got - want).max())
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, AMD specification
+
+
+def prefill_bench(args, dev):
+    """Chunked-prefill attention: each step writes a chunk of new K/V rows per
+    sequence (pa_cache_write) and runs causal multi-token attention over the
+    paged cache (pa_prefill).  Flops counted: 4 * D per (query, head, key
+    attended), the q.K and P.V products."""
+    import torch
+    import numpy as np
+    import paged_kv_cache_153_amd as pa
+    import synth
+    w = WORKLOADS[args.workload]
+    S, Hq, Hkv, D = args.seqs or 8, w["Hq"], w["Hkv"], w["D"]
+    bs = args.block_size or w["bs"]
+    n, T = args.context or 4096, args.chunk
+    if w["dtype"] != "f16" or T > n:
+        raise SystemExit("prefill needs a float16 workload and chunk <= context")
+    x = synth.make_decode_inputs([n] * S, Hq, Hkv, D, bs, dtype="f16", seed=args.seed,
+                                 device=dev, std=w["std"])
+    g = synth._gen(args.seed + 7, dev)
+    q = synth.normal((S * T, Hq, D), torch.float16, g, dev, w["std"])
+    new_k = synth.normal((S * T, Hkv, D), torch.float16, g, dev, w["std"])
+    new_v = synth.normal((S * T, Hkv, D), torch.float16, g, dev, w["std"])
+    bt = x.block_tables.cpu().numpy()
+    pos = np.arange(n - T, n)
+    slots = torch.tensor(np.concatenate([bt[s_, pos // bs] * bs + pos % bs for s_ in range(S)]),
+                         dtype=torch.int64, device=dev)
+    qstart = torch.arange(0, S * T + 1, T, dtype=torch.int32, device=dev)
+    out = torch.empty((S * T, Hq, D), dtype=torch.float32, device=dev)
+    keys = S * (T * (n - T) + T * (T + 1) // 2)
+    flops = 4.0 * D * Hq * keys
+
+    def step(ev=None):
+        pa.cache_write(new_k, new_v, x.kv_cache, slots)
+        if ev:
+            ev[0].record()
+        pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens, qstart, scale=x.scale,
+                   max_query_len=T, out=out)
+        if ev:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    att_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
+    tflops = flops / att_s / 1e12
+    parity = None
+    if not args.no_parity:
+        import oracle
+        rng = np.random.default_rng(0)
+        errs = []
+        for s_ in (0, S - 1):
+            ids = x.block_tables[s_, :-(-n // bs)].long()
+            blocks = x.kv_cache[ids].cpu().numpy()
+            for i in (0, T - 1, int(rng.integers(T))):
+                row = s_ * T + i
+                want = oracle.prefill_ref(q[row:row + 1].cpu().numpy(), blocks,
+                                          np.arange(blocks.shape[0])[None],
+                                          np.array([n - T + i + 1]), np.array([0, 1]), x.scale)
+                errs.append(float(np.abs(out[row].cpu().numpy() - want[0]).max()))
+        parity = max(errs)
+    log(f"[bench] prefill step {wall / args.steps * 1e6:.1f} us, attention {att_s * 1e6:.1f} us, "
+        f"{tflops:.1f} TFLOP/s")
+    res = {
+        "metric": "chunked-prefill attention TFLOP/s (q.K and P.V, useful flops)",
+        "value": round(flops * args.steps / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded N(0, std^2) K/V/Q; no weights)",
+        "config": {"workload": f"{w['desc']}: {S} seqs, chunk {T} at context {n} (past {n - T})",
+                   "num_seqs": S, "chunk": T, "context": n, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
+                   "step": "pa_cache_write (chunk rows) + pa_prefill"},
+        "attention_us": round(att_s * 1e6, 2),
+        "query_tokens_per_s": round(S * T / att_s, 1),
+        "parity_max_abs_err": parity,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,6 +553,10 @@ def main():
     ap.add_argument("--prefix-cache", action="store_true",
                     help="shared_prefix: admit the requests through the block manager's prefix "
                          "cache (block-hash lookup) instead of sharing the prefix by hand")
+    ap.add_argument("--mode", default="decode", choices=["decode", "prefill"],
+                    help="prefill: chunked-prefill attention (pa_prefill) instead of decode")
+    ap.add_argument("--chunk", type=int, default=512, help="prefill: new tokens per sequence")
+    ap.add_argument("--seqs", type=int, default=0, help="prefill: sequences (default 8)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -479,6 +577,9 @@ def main():
         sys.exit(1)
     pa.lib()
     dev = torch.device("cuda:0")
+    if args.mode == "prefill":
+        prefill_bench(args, dev)
+        return
     if args.calibrate_copy:
         print(json.dumps(calibrate_copy(dev)), flush=True)
         return

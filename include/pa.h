@@ -172,6 +172,39 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
               void* stream);
 
 /* -------------------------------------------------------------------------
+ * 2b. Multi-token queries: causal attention of a prefill chunk ([KV2P] §5.4
+ *     chunked prefill; [INFRA] §2 causal mask for T > 1; [KVPA] §4.3
+ *     block-table addressing)
+ *
+ * Sequence s brings T_s = query_start[s+1] - query_start[s] new tokens whose
+ * K/V are already in the cache (pa_cache_write first); n_s = context_lens[s]
+ * counts them.  Query i of sequence s (row query_start[s] + i) sits at
+ * position p = n_s - T_s + i and attends to keys t <= p:
+ *   out[row, h, :] = sum_{t <= p} softmax_t(scale * q[row,h,:] . K_t) V_t,
+ * with the paging and grouping of pa_decode.  T_s = 1 is the decode case;
+ * T_s = n_s is an ordinary causal prefill.  Accumulation and output float32.
+ *
+ *   out            device, [total_queries, num_q_heads, head_dim] float32
+ *   query          device, [total_queries, num_q_heads, head_dim] binary16
+ *   kv_cache       device, binary16 pool as for pa_cache_write
+ *   block_tables   device, [num_seqs, max_blocks_per_seq] int32
+ *   context_lens   device, [num_seqs] int32, T_s <= n_s <= max_blocks * bs
+ *   query_start    device, [num_seqs + 1] int32, non-decreasing, from 0 to
+ *                  total_queries
+ *   max_query_len  host bound on every T_s (sizes the grid)
+ *   kernel         PA_KERNEL_AUTO or PA_KERNEL_MFMA, optionally | PA_KV_CACHED
+ * Sequences with T_s > n_s produce no output rows.  Supported: dtype
+ * PA_F16; head_dim 64 or 128; block_size 8, 16 or 32; G in {1, 2, 4, 8}.
+ * ------------------------------------------------------------------------- */
+int pa_prefill(float* out, const void* query, const void* kv_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int num_seqs, int total_queries,
+               int num_q_heads, int num_kv_heads, int head_dim,
+               int block_size, int max_blocks_per_seq, int max_query_len,
+               int64_t num_blocks, float scale, int kernel, int dtype,
+               void* stream);
+
+/* -------------------------------------------------------------------------
  * 3. Host block manager ([KVPA] §5.1-§5.3, §8.2; [KV2P] §6.2; [NANO] §2.3,
  *    §4.2)
  *

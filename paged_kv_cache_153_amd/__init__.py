@@ -18,7 +18,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "PAError", "lib", "library_path", "cache_write", "decode", "decode_workspace_size",
+    "PAError", "lib", "library_path", "cache_write", "decode", "decode_workspace_size", "prefill",
     "BlockManager", "KERNELS", "F32", "F16", "I8", "kv_scales_like",
 ]
 
@@ -58,6 +58,9 @@ _SIGNATURES = {
                              _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float, _c.c_int,
                              _c.c_int, _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t),
                              _c.c_int, _P]),
+    "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                              _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
+                              _c.c_int, _c.c_int, _P]),
     "pa_bm_create": (_P, [_c.c_int64, _c.c_int]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_allocate": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
@@ -254,6 +257,47 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
                            KERNELS[kernel] | (KV_CACHED if cached_kv else 0),
                            None if workspace is None else workspace.data_ptr(),
                            wbytes, None, dt, _stream(query.device, stream)))
+    return out
+
+
+def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None,
+            max_query_len=None, out=None, stream=None, cached_kv=False):
+    """Causal attention of multi-token query chunks over the paged cache.
+
+    query [total_q, Hq, D] float16 (the chunks of all sequences, in order),
+    kv_cache [NB, 2, Hkv, bs, D] float16 with the chunks' K/V already written,
+    block_tables [S, MB] int32, context_lens [S] int32 (chunks included),
+    query_start [S + 1] int32.  Query i of sequence s attends to the keys up
+    to its own position n_s - T_s + i.  Returns ``out`` [total_q, Hq, D]
+    float32.  ``max_query_len`` is a host bound on the chunk lengths (default
+    total_q).
+    """
+    torch = _torch()
+    _need_cuda(query, kv_cache, block_tables, context_lens, query_start, out)
+    nb, two, hkv, bs, d = kv_cache.shape
+    total, hq, dq = query.shape
+    s = block_tables.shape[0]
+    if two != 2 or dq != d:
+        raise ValueError("query/kv_cache shape mismatch")
+    if query.dtype != torch.float16 or kv_cache.dtype != torch.float16:
+        raise TypeError("prefill takes float16 query and pool")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
+            query_start.dtype != torch.int32 or context_lens.shape != (s,) or \
+            query_start.shape != (s + 1,):
+        raise TypeError("block_tables [S, MB], context_lens [S] and query_start [S+1] must be int32")
+    if scale is None:
+        scale = d ** -0.5
+    if max_query_len is None:
+        max_query_len = total
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=torch.float32, device=query.device)
+    elif out.dtype != torch.float32 or out.shape != (total, hq, d):
+        raise TypeError("out must be float32 [total_q, Hq, D]")
+    _check(lib().pa_prefill(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
+                            block_tables.data_ptr(), context_lens.data_ptr(),
+                            query_start.data_ptr(), s, total, hq, hkv, d, bs,
+                            block_tables.shape[1], int(max_query_len), nb, float(scale),
+                            KV_CACHED if cached_kv else 0, F16, _stream(query.device, stream)))
     return out
 
 

@@ -45,6 +45,28 @@ struct DecodeArgs {
   int window;               // > 0: attend to the last `window` tokens only; 0: all
 };
 
+// Causal multi-token queries (a prefill chunk per sequence).
+struct PrefillArgs {
+  float* out;               // [total_q, Hq, D]
+  const void* q;            // [total_q, Hq, D] f16
+  const void* kv;           // [NB, 2, Hkv, BS, D] f16
+  const int32_t* bt;        // [S, MB]
+  const int32_t* cl;        // [S] context lengths, chunk included
+  const int32_t* qstart;    // [S + 1] first query row of each sequence
+  int64_t num_blocks;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int max_blocks;
+  int max_tokens;           // MB * BS
+  int qblocks;              // workgroups per (sequence, KV head)
+  float scale_log2;
+  int cached_kv;
+};
+int prefill_columns_per_workgroup();
+int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
+                        hipStream_t stream);
+
 // Each returns 0 on success, 1 if the (dtype, D, BS, G) combination has no
 // instantiation, or 2 if the launch failed (hipGetLastError has the code).
 int launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int block_size, int group,

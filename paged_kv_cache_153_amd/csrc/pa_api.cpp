@@ -409,4 +409,60 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   return PA_OK;
 }
 
+int pa_prefill(float* out, const void* query, const void* kv_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int num_seqs, int total_queries, int num_q_heads,
+               int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+               int max_query_len, int64_t num_blocks, float scale, int kernel, int dtype,
+               void* stream_) {
+  pa::clear_error();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "prefill needs an f16 pool");
+  if (num_seqs < 0 || total_queries < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes out of range");
+  if (num_q_heads % num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_q_heads % num_kv_heads");
+  const int group = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim");
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size");
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "group size");
+  if (kernel & ~(0xFF | PA_KV_CACHED)) return fail(PA_ERR_INVALID_ARG, "kernel flags");
+  if ((kernel & 0xFF) != PA_KERNEL_AUTO && (kernel & 0xFF) != PA_KERNEL_MFMA)
+    return fail(PA_ERR_UNSUPPORTED, "prefill runs on the matrix cores only");
+  const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
+  if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  if (num_seqs == 0 || total_queries == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !kv_cache || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache))
+    return fail(PA_ERR_INVALID_ARG, "out/query/kv_cache must be 16-byte aligned");
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.q = query;
+  a.kv = kv_cache;
+  a.bt = block_tables;
+  a.cl = context_lens;
+  a.qstart = query_start;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_tokens = (int)max_tokens_ll;
+  const long long cols = (long long)max_query_len * group;
+  const int per_wg = pa::prefill_columns_per_workgroup();
+  a.qblocks = (int)((cols + per_wg - 1) / per_wg);
+  if ((long long)num_seqs * a.qblocks * num_kv_heads >= (1LL << 31))
+    return fail(PA_ERR_INVALID_ARG, "grid too large");
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.cached_kv = (kernel & PA_KV_CACHED) != 0;
+  const int rc = pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);
+  if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
+  if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,109 @@
+"""GPU parity for causal multi-token queries (a prefill chunk per sequence,
+[KV2P] §5.4; causal mask for T > 1, [INFRA] §2) against the fp64 oracle,
+max-abs error <= 5e-4: ragged chunk lengths and pasts, every block size,
+head_dim and group size, chunks equal to whole prompts, T = 1 against the
+decode, and a 7B-shaped chunk on sampled outputs.  Pool rows past every
+context hold NaN, so a kernel that weighs one fails."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_153_amd as pa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-4
+
+
+def make(lens, chunks, hq, hkv, d, bs, seed, nan=True):
+    x = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype="f16", seed=seed,
+                                 fill_unused=float("nan") if nan else None)
+    qstart = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    g = synth._gen(seed + 50, "cpu")
+    q = synth.normal((int(qstart[-1]), hq, d), torch.float16, g, "cpu")
+    return x, q, qstart
+
+
+def run(x, q, qstart, device, **kw):
+    out = pa.prefill(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
+                     x.context_lens.to(device), torch.from_numpy(qstart).to(device),
+                     scale=x.scale, max_query_len=int(np.diff(qstart).max()), **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def ref(x, q, qstart):
+    return oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                              x.context_lens.numpy(), qstart, x.scale)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 4), (16, 2)])
+def test_ragged_chunks(device, bs, d, hq, hkv):
+    lens = [1, 17, 40, 100, 33, 300, 64]
+    chunks = [1, 17, 9, 100, 1, 37, 64]       # fresh prompts, pasts, single tokens
+    x, q, qs = make(lens, chunks, hq, hkv, d, bs, seed=bs + d + hq)
+    print(f"  prefill bs={bs} d={d} {hq}/{hkv}", flush=True)
+    got, want = run(x, q, qs, device), ref(x, q, qs)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL
+
+
+def test_single_token_chunks_match_decode(device):
+    x, q, qs = make([50, 7, 129], [1, 1, 1], 32, 8, 128, 16, seed=61)
+    got = run(x, q, qs, device)
+    dec = pa.decode(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
+                    x.context_lens.to(device), scale=x.scale, partition_size=-1)
+    torch.cuda.synchronize()
+    assert np.abs(got - dec.cpu().numpy()).max() <= 1e-5
+    assert np.abs(got - ref(x, q, qs)).max() <= TOL
+
+
+def test_chunked_prefill_equals_one_chunk(device):
+    """Two chunks (the second with the first as its past) give the rows of
+    one chunk over the whole prompt."""
+    n, t1 = 200, 77
+    x, q, _ = make([n], [n], 16, 4, 128, 16, seed=62, nan=False)
+    whole = run(x, q, np.array([0, n], np.int32), device)
+    a = run(synth.DecodeInputs("a", x.q, x.kv_cache, x.block_tables,
+                               torch.tensor([t1], dtype=torch.int32), x.scale, 0),
+            q[:t1], np.array([0, t1], np.int32), device)
+    b = run(x, q[t1:], np.array([0, n - t1], np.int32), device)
+    assert np.abs(np.concatenate([a, b]) - whole).max() <= 1e-5
+
+
+def test_empty_and_overlong_chunks_write_nothing(device):
+    x, q, qs = make([20, 5, 30], [0, 4, 0], 8, 2, 64, 16, seed=63)
+    out = torch.full((int(qs[-1]), 8, 64), 7.0, device=device)
+    pa.prefill(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
+               x.context_lens.to(device), torch.from_numpy(qs).to(device), scale=x.scale,
+               max_query_len=4, out=out)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - ref(x, q, qs)).max() <= TOL
+
+
+def test_llama7b_gqa_chunk_sampled(device):
+    """8 sequences x 512-token chunks at context 4096, 32 q / 8 KV heads."""
+    lens, chunks = [4096] * 8, [512] * 8
+    x = synth.make_decode_inputs(lens, 32, 8, 128, 16, dtype="f16", seed=64, device=device)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = synth.normal((int(qs[-1]), 32, 128), torch.float16, synth._gen(65, device), device)
+    out = pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=512)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(0)
+    for s in (0, 7, int(rng.integers(8))):
+        ids = x.block_tables[s, :256].long()
+        blocks = x.kv_cache[ids].cpu().numpy()
+        rows = [0, 511] + rng.integers(0, 512, 3).tolist()
+        for i in rows:
+            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
+                                      np.arange(256)[None], np.array([4096 - 512 + i + 1]),
+                                      np.array([0, 1]), x.scale)
+            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
+            assert err <= TOL, (s, i, err)

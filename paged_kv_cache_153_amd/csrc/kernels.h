@@ -62,6 +62,7 @@ struct PrefillArgs {
   int qblocks;              // workgroups per (sequence, KV head)
   float scale_log2;
   int cached_kv;
+  int variant;              // look-ahead depth: 0 = two tiles, 1 = one, 2 = three
 };
 int prefill_columns_per_workgroup();
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,

@@ -44,7 +44,7 @@ struct VRow<64> {
   static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
 };
 
-template <int D, int BS, int G, bool NT>
+template <int D, int BS, int G, int DEPTH, bool NT>
 __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KS = D / 32;          // 16x16x32 steps for q.K
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_mfma_kernel(Pre
     u32x4_t k[KS];
     vrow_t v[4];
   };
-  Buf buf[2];
+  Buf buf[DEPTH];
 
   auto issue = [&](int tile, const int (&blk)[BPT], Buf& b) {
     if (tile >= tile_end) tile = tile_end - 1;  // look-ahead past the range
@@ -201,21 +201,24 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_mfma_kernel(Pre
     m = m_new;
   };
 
-  // ---- key tiles 0 .. tile_end - 1, one tile in flight ahead -----------------
+  // ---- key tiles 0 .. tile_end - 1, DEPTH - 1 tiles in flight ahead ---------
   {
     int nb[BPT];
-    fetch_ids(0, nb);
-    issue(0, nb, buf[0]);
-    fetch_ids(1, nb);
+#pragma unroll
+    for (int k = 0; k < DEPTH - 1; ++k) {
+      fetch_ids(k, nb);
+      issue(k, nb, buf[k]);
+    }
+    fetch_ids(DEPTH - 1, nb);
     int tile = 0;
     while (tile < tile_end) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < DEPTH; ++k) {
         int cur[BPT];
 #pragma unroll
         for (int jj = 0; jj < BPT; ++jj) cur[jj] = nb[jj];
-        issue(tile + 1, cur, buf[k ^ 1]);
-        fetch_ids(tile + 2, nb);
+        issue(tile + DEPTH - 1, cur, buf[(k + DEPTH - 1) % DEPTH]);
+        fetch_ids(tile + DEPTH, nb);
         compute(tile, buf[k]);
         ++tile;
         if (tile >= tile_end) break;
@@ -238,17 +241,26 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_mfma_kernel(Pre
   }
 }
 
-template <int D, int BS, int G>
-int launch_one(const PrefillArgs& a, hipStream_t stream) {
+template <int D, int BS, int G, int DEPTH>
+int launch_depth(const PrefillArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.num_seqs * a.qblocks * a.num_kv_heads);
   if (grid == 0) return 0;
   if (a.cached_kv)
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, false>), dim3(grid),
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, DEPTH, false>), dim3(grid),
                        dim3(kPrefillWaves * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, true>), dim3(grid),
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, DEPTH, true>), dim3(grid),
                        dim3(kPrefillWaves * 64), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+template <int D, int BS, int G>
+int launch_one(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.variant) {
+    case 1: return launch_depth<D, BS, G, 2>(a, stream);
+    case 2: return launch_depth<D, BS, G, 4>(a, stream);
+    default: return launch_depth<D, BS, G, 3>(a, stream);
+  }
 }
 
 template <int D, int BS>

@@ -192,7 +192,9 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
  *   query_start    device, [num_seqs + 1] int32, non-decreasing, from 0 to
  *                  total_queries
  *   max_query_len  host bound on every T_s (sizes the grid)
- *   kernel         PA_KERNEL_AUTO or PA_KERNEL_MFMA, optionally | PA_KV_CACHED
+ *   kernel         PA_KERNEL_AUTO or PA_KERNEL_MFMA (PA_KV_CACHED is accepted
+ *                  and has no effect: every K/V row is read by several
+ *                  query blocks, so the prefill always uses cached loads)
  * Sequences with T_s > n_s produce no output rows.  Supported: dtype
  * PA_F16; head_dim 64 or 128; block_size 8, 16 or 32; G in {1, 2, 4, 8}.
  * ------------------------------------------------------------------------- */

@@ -261,7 +261,7 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
 
 
 def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None,
-            max_query_len=None, out=None, stream=None, cached_kv=False):
+            max_query_len=None, out=None, stream=None):
     """Causal attention of multi-token query chunks over the paged cache.
 
     query [total_q, Hq, D] float16 (the chunks of all sequences, in order),
@@ -297,7 +297,7 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
                             block_tables.data_ptr(), context_lens.data_ptr(),
                             query_start.data_ptr(), s, total, hq, hkv, d, bs,
                             block_tables.shape[1], int(max_query_len), nb, float(scale),
-                            KV_CACHED if cached_kv else 0, F16, _stream(query.device, stream)))
+                            0, F16, _stream(query.device, stream)))
     return out
 
 

@@ -61,10 +61,9 @@ struct PrefillArgs {
   int max_tokens;           // MB * BS
   int qblocks;              // workgroups per (sequence, KV head)
   float scale_log2;
-  int cached_kv;
-  int variant;              // look-ahead depth: 0 = two tiles, 1 = one, 2 = three
+  int variant;              // columns per wave: 0 = 32, 1 = 16
 };
-int prefill_columns_per_workgroup();
+int prefill_columns_per_workgroup(int variant);
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream);
 

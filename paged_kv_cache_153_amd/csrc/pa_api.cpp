@@ -452,18 +452,17 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = (int)max_tokens_ll;
+  {  // PA_TUNE_VARIANT=0|1 overrides the columns per wave (tuning experiments only)
+    const char* e = std::getenv("PA_TUNE_VARIANT");
+    const int forced = e ? std::atoi(e) : -1;
+    a.variant = forced >= 0 && forced <= 1 ? forced : 0;
+  }
   const long long cols = (long long)max_query_len * group;
-  const int per_wg = pa::prefill_columns_per_workgroup();
+  const int per_wg = pa::prefill_columns_per_workgroup(a.variant);
   a.qblocks = (int)((cols + per_wg - 1) / per_wg);
   if ((long long)num_seqs * a.qblocks * num_kv_heads >= (1LL << 31))
     return fail(PA_ERR_INVALID_ARG, "grid too large");
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.cached_kv = (kernel & PA_KV_CACHED) != 0;
-  {  // PA_TUNE_VARIANT=0..2 overrides the look-ahead depth (tuning experiments only)
-    const char* e = std::getenv("PA_TUNE_VARIANT");
-    const int forced = e ? std::atoi(e) : -1;
-    a.variant = forced >= 0 && forced <= 2 ? forced : 0;
-  }
   const int rc = pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);
   if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));

@@ -9,19 +9,27 @@
 // PagedAttention深度解析" §4.3): token t is row t % BS of block
 // block_tables[s, t / BS].
 //
-// With T tokens the product q K^T is a real [T*G x D] x [D x 16] contraction
-// per 16-key tile, so the 16 MFMA columns of one wave are 16 (query token,
-// head) pairs of one KV head: column c is token c / G of the wave's block and
-// head c % G of the group.  Each wave owns its columns outright: it walks the
-// key tiles from 0 to the last one its latest token may see, keeps an online
-// softmax per column, and writes its outputs itself (no cross-wave merge).
-// The tile flow is the decode's matrix-core flow (decode_mfma.hip): K rows
-// are the A operand of v_mfma_f32_16x16x32_f16, whose C layout is the B
-// layout of v_mfma_f32_16x16x16f16 for P^T, and the weights go in as fp16
-// hi + lo parts scaled by 2^15.  Block ids are read with scalar loads, and
-// the next tile's loads are issued before the current one is computed, on
-// every step (look-ahead past the end re-reads the last tile), so the
-// compiler's wait counts keep them in flight.
+// Columns are (query token, head) pairs of one KV head, head fastest; a wave
+// owns CB blocks of 16 columns and a workgroup of four waves 64 * CB columns
+// of one (sequence, KV head).  The workgroup walks the keys in steps of 32:
+// each step's K and V rows (32 x 2D bytes each) are loaded once, with plain
+// (cached) 16-byte loads whose block ids come from scalar loads, into a
+// double-buffered LDS tile, and every wave takes its matrix operands from
+// there — the prefill reads each K/V row once per workgroup, not once per
+// wave.  Per step and column block:
+//   S^T = K q^T  two 16-key tiles x D/32 v_mfma_f32_16x16x32_f16 (K rows are
+//                the A operand, q the B operand);
+//   online softmax per column in log2 units, the causal mask only on steps
+//                that cross the diagonal or the end of the context;
+//   O^T += V^T P^T  one v_mfma_f32_16x16x32_f16 per 16 output rows and per
+//                weight part: the C layout of the two S tiles gives each lane
+//                keys 4q..4q+3 of both tiles, which is the B layout of a
+//                32-deep contraction once the contraction index is relabelled
+//                (k = 8q + j  ->  key 4q + j of tile j / 4); V is read with
+//                the same relabelling, and the weights go in as fp16 hi + lo
+//                parts scaled by 2^15, which keeps ~21 bits of each weight.
+// LDS rows are 2D bytes with 16-byte chunks XOR-swizzled by the row, so that
+// the 16 lanes that read one chunk of 16 different K rows hit distinct banks.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,238 +37,292 @@ namespace pa {
 namespace {
 
 constexpr float kPScale = 32768.f;  // 2^15
-constexpr int kPrefillWaves = 4;    // waves (column blocks) per workgroup
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kKeys = 32;           // keys per step: two 16-key MFMA tiles
 
 template <int D>
 struct VRow;  // per-lane share of one V row: 16 bytes (D=128) or 8 bytes (D=64)
 template <>
 struct VRow<128> {
   using type = u32x4_t;
-  static __device__ __forceinline__ type zero() { return type{0u, 0u, 0u, 0u}; }
 };
 template <>
 struct VRow<64> {
   using type = u32x2_t;
-  static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
 };
 
-template <int D, int BS, int G, int DEPTH, bool NT>
-__global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
+// Byte offset of 16-byte chunk c of row r in an LDS step tile.
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int r, int c) {
+  constexpr int CPR = D / 8;  // chunks per row
+  return (uint32_t)(r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
+}
+
+template <int D, int BS, int G, int CB>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
-  constexpr int KS = D / 32;          // 16x16x32 steps for q.K
-  constexpr int VH = D / 16;          // halves of one V row per lane
-  constexpr int NE = VH;              // P.V blocks of 16 output rows
-  constexpr int TPB = 16 / G;         // query tokens per column block
-  constexpr int BPT = BS >= kTile ? 1 : kTile / BS;
-  static_assert(BPT <= 2, "a tile spans at most two blocks");
+  constexpr int KS = D / 32;                 // 16x16x32 steps of q.K
+  constexpr int NE = D / 16;                 // P.V blocks of 16 output rows
+  constexpr int VH = D / 16;                 // output row d = VH * r + e
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPW = 64 / CPR;              // rows one wave loads per round
+  constexpr int ROUNDS = kKeys / (kWaves * RPW);
+  static_assert(ROUNDS >= 1 && BS % RPW == 0, "a wave's load rows lie in one block");
+  constexpr int TILE = kKeys * 2 * D;        // bytes of one K or V step tile
+  constexpr int COLS_W = 16 * CB;            // columns per wave
+  constexpr int COLS_WG = kWaves * COLS_W;   // columns per workgroup
+  constexpr int TOK_W = COLS_W / G;          // query tokens per wave
   using vrow_t = typename VRow<D>::type;
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][TILE];  // [buf][K|V]
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int quad = lane >> 4;
   const int col = lane & 15;
 
-  // ---- which sequence, KV head and column block ---------------------------
-  int bid = blockIdx.x;
-  const int g = bid % a.num_kv_heads;
-  bid /= a.num_kv_heads;
-  const int qb = bid % a.qblocks;
-  const int s = bid / a.qblocks;
+  // ---- workgroup -> (sequence, KV head, column block) ----------------------
+  // Workgroups go to the 8 XCDs round robin.  Renumbered so that each XCD
+  // takes a contiguous range, every column block of one (sequence, KV head)
+  // runs on the XCD whose L2 holds that head's K/V; within a pair the
+  // latest tokens (the most keys) start first.
+  const unsigned nwg = gridDim.x, bid = blockIdx.x;
+  const unsigned per = nwg / 8u, rem = nwg % 8u, xcd = bid % 8u;
+  unsigned lid = xcd * per + (xcd < rem ? xcd : rem) + bid / 8u;
+  const int qb = a.qblocks - 1 - (int)(lid % (unsigned)a.qblocks);
+  lid /= (unsigned)a.qblocks;
+  const int g = (int)(lid % (unsigned)a.num_kv_heads);
+  const int s = (int)(lid / (unsigned)a.num_kv_heads);
   const int q0 = a.qstart[s];
   const int T = a.qstart[s + 1] - q0;
   int n = a.cl[s];
   n = n < 0 ? 0 : (n > a.max_tokens ? a.max_tokens : n);
-  const int cb = qb * kPrefillWaves + w;  // column block within the sequence
-  const int i_first = cb * TPB;
-  if (T <= 0 || T > n || i_first >= T) return;  // nothing for this wave
-  const int i_last = min(T - 1, i_first + TPB - 1);
-  const int tok = i_first + col / G;          // this lane's column: token, head
-  const int hh = col % G;
-  const bool col_valid = tok < T;
-  // last key each column sees (-1 for columns past the chunk: they see none)
-  const int p_col = col_valid ? n - T + tok : -1;
-  const int p_max = n - T + i_last;           // wave-uniform
-  const int p_min = i_first + TPB - 1 < T ? n - T + i_first : -1;
-  const int tile_end = p_max / kTile + 1;
+  const int wg_tok0 = qb * (COLS_WG / G);
+  if (T <= 0 || T > n || wg_tok0 >= T) return;  // the whole workgroup
+  const int wg_last = min(T - 1, wg_tok0 + COLS_WG / G - 1);
+  const int nsteps = (n - T + wg_last) / kKeys + 1;
 
-  // ---- q as the B operand: lane (quad, col) = column col, chunk 4j + quad ---
-  half8_t qb_op[KS];
-  {
-    const half_t* qh =
-        reinterpret_cast<const half_t*>(a.q) +
-        ((size_t)(q0 + (col_valid ? tok : 0)) * a.num_q_heads + g * G + hh) * D;
+  // this wave's columns: token w_tok0 + (16 cb + col) / G, head col % G
+  const int w_tok0 = wg_tok0 + w * TOK_W;
+  const int w_pmax = w_tok0 < T ? n - T + min(T - 1, w_tok0 + TOK_W - 1) : -1;
+  const int w_pmin = w_tok0 + TOK_W - 1 < T ? n - T + w_tok0 : -1;
+  const int hh = col % G;
+  int tok[CB], p_col[CB];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (col_valid)
-        qb_op[j] = __builtin_bit_cast(half8_t, load16(qh + (4 * j + quad) * 8));
-      else
-        qb_op[j] = __builtin_bit_cast(half8_t, u32x4_t{0u, 0u, 0u, 0u});
-    }
+  for (int cb = 0; cb < CB; ++cb) {
+    tok[cb] = w_tok0 + (16 * cb + col) / G;
+    p_col[cb] = tok[cb] < T ? n - T + tok[cb] : -1;  // last key the column sees
   }
 
-  const size_t head_stride = (size_t)BS * D;
-  const size_t block_stride = 2 * (size_t)a.num_kv_heads * head_stride;
-  const size_t v_offset = (size_t)a.num_kv_heads * head_stride;
-  const half_t* kvh = reinterpret_cast<const half_t*>(a.kv) + (size_t)g * head_stride;
-  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
-
-  auto fetch_ids = [&](int tile, int (&out)[BPT]) {
-    if (tile >= tile_end) tile = tile_end - 1;
+  // ---- q as the B operand: lane (quad, col), chunk 4j + quad of its row -----
+  half8_t qop[CB][KS];
 #pragma unroll
-    for (int jj = 0; jj < BPT; ++jj) {
-      const int lb = BS >= kTile ? tile * kTile / BS : tile * BPT + jj;
-      const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
-      out[jj] = (v < 0 || v >= a.num_blocks) ? 0 : v;
-    }
-  };
-
-  struct Buf {
-    u32x4_t k[KS];
-    vrow_t v[4];
-  };
-  Buf buf[DEPTH];
-
-  auto issue = [&](int tile, const int (&blk)[BPT], Buf& b) {
-    if (tile >= tile_end) tile = tile_end - 1;  // look-ahead past the range
-    const int row0 = BS > kTile ? (tile % (BS / kTile)) * kTile : 0;
-    const int kb_id = BPT == 1 ? blk[0] : (col >= BS ? blk[BPT - 1] : blk[0]);
-    const half_t* kb = kvh + (size_t)kb_id * block_stride;
-    const uint32_t krow = (uint32_t)(BPT == 1 ? row0 + col : col % BS) * (D * 2);
-#pragma unroll
-    for (int j = 0; j < KS; ++j) b.k[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * quad + i;
-      const int vb_id = BPT == 1 ? blk[0] : (t >= BS ? blk[BPT - 1] : blk[0]);
-      const half_t* vb = kvh + (size_t)vb_id * block_stride + v_offset;
-      const uint32_t off =
-          (uint32_t)(BPT == 1 ? row0 + t : t % BS) * (D * 2) + col * (VH * 2);
-      if constexpr (D == 128)
-        b.v[i] = kv_load16<NT>(vb, off);
-      else
-        b.v[i] = kv_load8<NT>(vb, off);
-    }
-  };
-
-  float m = kMaxInit;  // running max of column `col` (same in all four quads)
-  float l = 0.f;
-  float4_t acc[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
-  const float cs = a.scale_log2;
-
-  auto compute = [&](int tile, Buf& b) {
-    float4_t sc = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb) {
+    const bool ok = tok[cb] < T;
+    const half_t* qh = reinterpret_cast<const half_t*>(a.q) +
+                       ((size_t)(q0 + (ok ? tok[cb] : 0)) * a.num_q_heads + g * G + hh) * D;
 #pragma unroll
     for (int j = 0; j < KS; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, b.k[j]), qb_op[j],
-                                                   sc, 0, 0, 0);
-    float y[4];
+      qop[cb][j] = ok ? __builtin_bit_cast(half8_t, load16(qh + (4 * j + quad) * 8))
+                      : __builtin_bit_cast(half8_t, u32x4_t{0u, 0u, 0u, 0u});
+  }
+
+  // ---- K/V step loads: wave w, round j loads rows (j * 4 + w) * RPW + lane / CPR
+  const size_t head_bytes = (size_t)BS * D * 2;
+  const size_t block_bytes = 2 * (size_t)a.num_kv_heads * head_bytes;
+  const size_t v_bytes = (size_t)a.num_kv_heads * head_bytes;
+  const char* kvg = reinterpret_cast<const char*>(a.kv) + (size_t)g * head_bytes;
+  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
+  const int lrow = lane / CPR;
+  const int lch = lane % CPR;
+
+  int ids[ROUNDS];
+  u32x4_t stk[ROUNDS], stv[ROUNDS];
+  auto fetch_ids = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = sc[i] * cs;
-    if ((tile + 1) * kTile - 1 > p_min || (tile + 1) * kTile > n) {
-      // the causal edge (or the end of the context) crosses this tile
+    for (int j = 0; j < ROUNDS; ++j) {
+      const int lb = (st * kKeys + (j * kWaves + w) * RPW) / BS;  // wave-uniform
+      const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
+      ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
+    }
+  };
+  auto issue = [&](int st) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tile * kTile + 4 * quad + i;
-        if (t > p_col) y[i] = -INFINITY;
-        if (t >= n) b.v[i] = VRow<D>::zero();  // rows past the context: never weighed
+    for (int j = 0; j < ROUNDS; ++j) {
+      const int key0 = st * kKeys + (j * kWaves + w) * RPW;
+      const char* base = kvg + (size_t)ids[j] * block_bytes;
+      const uint32_t off = (uint32_t)(((key0 % BS) + lrow) * (2 * D) + lch * 16);
+      stk[j] = load16_at(base, off);
+      stv[j] = load16_at(base + v_bytes, off);
+    }
+  };
+  auto stash = [&](int st, int b) {
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) {
+      const int r = (j * kWaves + w) * RPW + lrow;
+      const uint32_t o = tile_off<D>(r, lch);
+      u32x4_t v = stv[j];
+      if (st * kKeys + r >= n) v = u32x4_t{0u, 0u, 0u, 0u};  // past the context
+      *reinterpret_cast<u32x4_t*>(&lds[b][0][o]) = stk[j];
+      *reinterpret_cast<u32x4_t*>(&lds[b][1][o]) = v;
+    }
+  };
+
+  float m[CB], l[CB];
+  float4_t acc[CB][NE];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    m[cb] = kMaxInit;
+    l[cb] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[cb][e] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float cs = a.scale_log2;
+
+  auto compute = [&](int st, int b) {
+    const unsigned char* kt = lds[b][0];
+    const unsigned char* vt = lds[b][1];
+    float4_t sc[CB][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4_t kr[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        kr[j] = *reinterpret_cast<const u32x4_t*>(kt + tile_off<D>(16 * kk + col, 4 * j + quad));
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        sc[cb][kk] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          sc[cb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[j]),
+                                                              qop[cb][j], sc[cb][kk], 0, 0, 0);
       }
     }
-    float ym = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-    ym = fmaxf(ym, __shfl_xor(ym, 16));
-    ym = fmaxf(ym, __shfl_xor(ym, 32));
-    const float m_new = fmaxf(m, ym);
-    const float alpha = fast_exp2(m - m_new);
-    float pw[4];
+    // V rows 4 quad + i of both tiles, this lane's D/16 values of each
+    vrow_t vr[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pw[i] = fast_exp2(y[i] - m_new) * kPScale;
-    l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
-    const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
-    const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
-    const auto l01 = __builtin_amdgcn_cvt_pkrtz(pw[0] - (float)h01[0], pw[1] - (float)h01[1]);
-    const auto l23 = __builtin_amdgcn_cvt_pkrtz(pw[2] - (float)h23[0], pw[3] - (float)h23[1]);
-    const half4_t phi = __builtin_bit_cast(
-        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
-    const half4_t plo = __builtin_bit_cast(
-        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
-    if (wave_any(alpha != 1.f)) {
+    for (int jv = 0; jv < 8; ++jv) {
+      const int r = (jv >> 2) * 16 + 4 * quad + (jv & 3);
+      if constexpr (D == 128)
+        vr[jv] = *reinterpret_cast<const u32x4_t*>(vt + tile_off<D>(r, col));
+      else
+        vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + tile_off<D>(r, col >> 1) + (col & 1) * 8);
+    }
+    const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n;
+    half8_t phi[CB], plo[CB];
 #pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+    for (int cb = 0; cb < CB; ++cb) {
+      float y[8];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[4 * kk + i] = sc[cb][kk][i] * cs;
+      if (edge) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = st * kKeys + (k >> 2) * 16 + 4 * quad + (k & 3);
+          if (t > p_col[cb]) y[k] = -INFINITY;
+        }
+      }
+      float ym = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                       fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      ym = fmaxf(ym, __shfl_xor(ym, 16));
+      ym = fmaxf(ym, __shfl_xor(ym, 32));
+      const float m_new = fmaxf(m[cb], ym);
+      const float alpha = fast_exp2(m[cb] - m_new);
+      float pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(y[k] - m_new) * kPScale;
+      l[cb] = fmaf(l[cb], alpha,
+                   ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7])));
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const auto h = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
+        const auto r = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - (float)h[0],
+                                                  pw[2 * k + 1] - (float)h[1]);
+        hw[k] = __builtin_bit_cast(uint32_t, h);
+        lw[k] = __builtin_bit_cast(uint32_t, r);
+      }
+      phi[cb] = __builtin_bit_cast(half8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
+      plo[cb] = __builtin_bit_cast(half8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
+      if (wave_any(alpha != 1.f)) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
+      }
+      m[cb] = m_new;
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       const int wd = e >> 1;
       const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t d0 = __builtin_amdgcn_perm(b.v[1][wd], b.v[0][wd], sel);
-      const uint32_t d1 = __builtin_amdgcn_perm(b.v[3][wd], b.v[2][wd], sel);
-      const half4_t av = __builtin_bit_cast(half4_t, u32x2_t{d0, d1});
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[e], 0, 0, 0);
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[e], 0, 0, 0);
-    }
-    m = m_new;
-  };
-
-  // ---- key tiles 0 .. tile_end - 1, DEPTH - 1 tiles in flight ahead ---------
-  {
-    int nb[BPT];
+      const half8_t av = __builtin_bit_cast(
+          half8_t, u32x4_t{__builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel),
+                           __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel),
+                           __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel),
+                           __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel)});
 #pragma unroll
-    for (int k = 0; k < DEPTH - 1; ++k) {
-      fetch_ids(k, nb);
-      issue(k, nb, buf[k]);
-    }
-    fetch_ids(DEPTH - 1, nb);
-    int tile = 0;
-    while (tile < tile_end) {
-#pragma unroll
-      for (int k = 0; k < DEPTH; ++k) {
-        int cur[BPT];
-#pragma unroll
-        for (int jj = 0; jj < BPT; ++jj) cur[jj] = nb[jj];
-        issue(tile + DEPTH - 1, cur, buf[(k + DEPTH - 1) % DEPTH]);
-        fetch_ids(tile + DEPTH, nb);
-        compute(tile, buf[k]);
-        ++tile;
-        if (tile >= tile_end) break;
+      for (int cb = 0; cb < CB; ++cb) {
+        acc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[cb], acc[cb][e], 0, 0, 0);
+        acc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[cb], acc[cb][e], 0, 0, 0);
       }
     }
+  };
+
+  // ---- steps 0 .. nsteps - 1: step st + 1 is loaded while st is computed ----
+  fetch_ids(0);
+  issue(0);
+  fetch_ids(1);
+  stash(0, 0);
+  if (nsteps > 1) {
+    issue(1);
+    fetch_ids(2);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int b = st & 1;
+    if (st * kKeys <= w_pmax) compute(st, b);
+    if (st + 1 < nsteps) stash(st + 1, b ^ 1);
+    if (st + 2 < nsteps) {
+      issue(st + 2);
+      fetch_ids(st + 3);
+    }
+    __syncthreads();
   }
 
-  // ---- normalise and store: lane (quad, col) holds rows d = VH*(4 quad + i) + e
-  float lt = l;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-  if (col_valid) {
-    const float inv = 1.f / lt;
-    float* o = a.out + ((size_t)(q0 + tok) * a.num_q_heads + g * G + hh) * D;
+  // ---- normalise and store: lane (quad, col) holds d = VH * (4 quad + i) + e
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int cb = 0; cb < CB; ++cb) {
+    float lt = l[cb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (tok[cb] < T) {
+      const float inv = 1.f / lt;
+      float* o = a.out + ((size_t)(q0 + tok[cb]) * a.num_q_heads + g * G + hh) * D;
 #pragma unroll
-      for (int e = 0; e < NE; ++e) o[VH * (4 * quad + i) + e] = acc[e][i] * inv;
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e4 = 0; e4 < NE / 4; ++e4)
+          *reinterpret_cast<float4_t*>(o + VH * (4 * quad + i) + 4 * e4) =
+              float4_t{acc[cb][4 * e4][i], acc[cb][4 * e4 + 1][i], acc[cb][4 * e4 + 2][i],
+                       acc[cb][4 * e4 + 3][i]} * inv;
+      }
     }
   }
 }
 
-template <int D, int BS, int G, int DEPTH>
-int launch_depth(const PrefillArgs& a, hipStream_t stream) {
+template <int D, int BS, int G, int CB>
+int launch_cb(const PrefillArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.num_seqs * a.qblocks * a.num_kv_heads);
   if (grid == 0) return 0;
-  if (a.cached_kv)
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, DEPTH, false>), dim3(grid),
-                       dim3(kPrefillWaves * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, DEPTH, true>), dim3(grid),
-                       dim3(kPrefillWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, CB>), dim3(grid), dim3(kWaves * 64), 0,
+                     stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 template <int D, int BS, int G>
 int launch_one(const PrefillArgs& a, hipStream_t stream) {
-  switch (a.variant) {
-    case 1: return launch_depth<D, BS, G, 2>(a, stream);
-    case 2: return launch_depth<D, BS, G, 4>(a, stream);
-    default: return launch_depth<D, BS, G, 3>(a, stream);
-  }
+  return a.variant == 1 ? launch_cb<D, BS, G, 1>(a, stream) : launch_cb<D, BS, G, 2>(a, stream);
 }
 
 template <int D, int BS>
@@ -286,7 +348,7 @@ int by_block(const PrefillArgs& a, int block_size, int group, hipStream_t stream
 
 }  // namespace
 
-int prefill_columns_per_workgroup() { return kPrefillWaves * 16; }
+int prefill_columns_per_workgroup(int variant) { return kWaves * 16 * (variant == 1 ? 1 : 2); }
 
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream) {

@@ -141,6 +141,36 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 }
 
 // True when any lane of the wave has `pred` set (wave-uniform).
+// Max / sum over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
+// rows), result in all four.  v_permlane32_swap exchanges the upper half of
+// one register with the lower half of the other, v_permlane16_swap the odd
+// rows of one with the even rows of the other: with both registers holding
+// x, each lane ends up with the pair {x[i], x[i ^ 32]} (then {.., i ^ 16}),
+// so one VALU op per stage replaces an LDS-routed shuffle.  Written as
+// inline asm with both registers read-write: this compiler folds the
+// builtin's second result into its first.  The s_nop covers the wait
+// states a permlane needs after a VALU write of its operands.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float rows4_max(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  float c = fmaxf(a, b), d = c;
+  permlane16_swap(c, d);
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  float c = a + b, d = c;
+  permlane16_swap(c, d);
+  return c + d;
+}
+
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
 }

@@ -182,22 +182,25 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   auto compute = [&](int st, int b) {
     const unsigned char* kt = lds[b][0];
     const unsigned char* vt = lds[b][1];
-    float4_t sc[CB][2];
+    u32x4_t kr[2][KS];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4_t kr[KS];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int j = 0; j < KS; ++j)
-        kr[j] = *reinterpret_cast<const u32x4_t*>(kt + tile_off<D>(16 * kk + col, 4 * j + quad));
+        kr[kk][j] =
+            *reinterpret_cast<const u32x4_t*>(kt + tile_off<D>(16 * kk + col, 4 * j + quad));
+    // 2 * CB independent accumulations, interleaved over the contraction
+    float4_t sc[CB][2];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        sc[cb][kk] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < KS; ++j)
-          sc[cb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[j]),
-                                                              qop[cb][j], sc[cb][kk], 0, 0, 0);
-      }
-    }
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          sc[cb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8_t, kr[kk][j]), qop[cb][j], sc[cb][kk], 0, 0, 0);
     // V rows 4 quad + i of both tiles, this lane's D/16 values of each
     vrow_t vr[8];
 #pragma unroll
@@ -226,8 +229,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       }
       float ym = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
                        fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-      ym = fmaxf(ym, __shfl_xor(ym, 16));
-      ym = fmaxf(ym, __shfl_xor(ym, 32));
+      ym = rows4_max(ym);
       const float m_new = fmaxf(m[cb], ym);
       const float alpha = fast_exp2(m[cb] - m_new);
       float pw[8];
@@ -252,20 +254,34 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       }
       m[cb] = m_new;
     }
+    // P.V in pairs of output blocks: each accumulator's hi and lo products
+    // are 2 * CB instructions apart
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const int wd = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const half8_t av = __builtin_bit_cast(
-          half8_t, u32x4_t{__builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel),
-                           __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel),
-                           __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel),
-                           __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel)});
+    for (int e0 = 0; e0 < NE; e0 += 2) {
+      half8_t av[2];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        acc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, phi[cb], acc[cb][e], 0, 0, 0);
-        acc[cb][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, plo[cb], acc[cb][e], 0, 0, 0);
+      for (int ee = 0; ee < 2; ++ee) {
+        const int e = e0 + ee;
+        const int wd = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        av[ee] = __builtin_bit_cast(
+            half8_t, u32x4_t{__builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel),
+                             __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel),
+                             __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel),
+                             __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel)});
       }
+#pragma unroll
+      for (int ee = 0; ee < 2; ++ee)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ee], phi[cb],
+                                                                    acc[cb][e0 + ee], 0, 0, 0);
+#pragma unroll
+      for (int ee = 0; ee < 2; ++ee)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ee], plo[cb],
+                                                                    acc[cb][e0 + ee], 0, 0, 0);
     }
   };
 
@@ -293,9 +309,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   // ---- normalise and store: lane (quad, col) holds d = VH * (4 quad + i) + e
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    float lt = l[cb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = rows4_sum(l[cb]);
     if (tok[cb] < T) {
       const float inv = 1.f / lt;
       float* o = a.out + ((size_t)(q0 + tok[cb]) * a.num_q_heads + g * G + hh) * D;

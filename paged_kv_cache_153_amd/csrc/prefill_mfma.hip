@@ -20,14 +20,16 @@
 //   S^T = K q^T  two 16-key tiles x D/32 v_mfma_f32_16x16x32_f16 (K rows are
 //                the A operand, q the B operand);
 //   online softmax per column in log2 units, the causal mask only on steps
-//                that cross the diagonal or the end of the context;
+//                that cross the diagonal or the end of the context; the
+//                reference value moves only when a score passes it by more
+//                than 2^8, so most steps need no cross-lane max or rescale;
 //   O^T += V^T P^T  one v_mfma_f32_16x16x32_f16 per 16 output rows and per
 //                weight part: the C layout of the two S tiles gives each lane
 //                keys 4q..4q+3 of both tiles, which is the B layout of a
 //                32-deep contraction once the contraction index is relabelled
 //                (k = 8q + j  ->  key 4q + j of tile j / 4); V is read with
 //                the same relabelling, and the weights go in as fp16 hi + lo
-//                parts scaled by 2^15, which keeps ~21 bits of each weight.
+//                parts, which keeps ~21 bits of each weight.
 // LDS rows are 2D bytes with 16-byte chunks XOR-swizzled by the row, so that
 // the 16 lanes that read one chunk of 16 different K rows hit distinct banks.
 #include "device_common.h"
@@ -36,7 +38,12 @@
 namespace pa {
 namespace {
 
-constexpr float kPScale = 32768.f;  // 2^15
+// The softmax reference m of a column moves only when a score exceeds it by
+// more than kSlack (log2 units), so most steps skip the cross-lane max and
+// the rescale.  Weights are exp2(y - m + kPLog) <= 2^(kSlack + kPLog) = 2^15,
+// inside fp16 range for the hi/lo split.
+constexpr float kSlack = 8.f;
+constexpr float kPLog = 7.f;
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kKeys = 32;           // keys per step: two 16-key MFMA tiles
 
@@ -227,16 +234,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
           if (t > p_col[cb]) y[k] = -INFINITY;
         }
       }
-      float ym = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
-                       fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-      ym = rows4_max(ym);
-      const float m_new = fmaxf(m[cb], ym);
-      const float alpha = fast_exp2(m[cb] - m_new);
+      const float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                             fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      if (wave_any(lm > m[cb] + kSlack)) {
+        // some column's reference must move: to the column's max, exactly
+        const float m_new = fmaxf(m[cb], rows4_max(lm));
+        const float alpha = fast_exp2(m[cb] - m_new);
+        l[cb] *= alpha;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
+        m[cb] = m_new;
+      }
+      const float mo = m[cb] - kPLog;
       float pw[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(y[k] - m_new) * kPScale;
-      l[cb] = fmaf(l[cb], alpha,
-                   ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7])));
+      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(y[k] - mo);
+      l[cb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -248,11 +261,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       }
       phi[cb] = __builtin_bit_cast(half8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
       plo[cb] = __builtin_bit_cast(half8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
-      if (wave_any(alpha != 1.f)) {
-#pragma unroll
-        for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
-      }
-      m[cb] = m_new;
     }
     // P.V in pairs of output blocks: each accumulator's hi and lo products
     // are 2 * CB instructions apart

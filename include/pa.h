@@ -192,6 +192,8 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
  *   query_start    device, [num_seqs + 1] int32, non-decreasing, from 0 to
  *                  total_queries
  *   max_query_len  host bound on every T_s (sizes the grid)
+ *   scale          > 0 and finite (the kernel takes the running max on the
+ *                  raw scores); PA_ERR_INVALID_ARG otherwise
  *   kernel         PA_KERNEL_AUTO or PA_KERNEL_MFMA (PA_KV_CACHED is accepted
  *                  and has no effect: every K/V row is read by several
  *                  query blocks, so the prefill always uses cached loads)

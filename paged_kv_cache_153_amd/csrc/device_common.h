@@ -141,6 +141,17 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 }
 
 // True when any lane of the wave has `pred` set (wave-uniform).
+// 16-byte global -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
+// from `src` land at byte 16 l of the wave-uniform LDS address `dst`,
+// without passing through registers; vmcnt tracks completion.  The builtin
+// exists only for the device, hence the guard (the host pass compiles the
+// kernel body too, and must still emit the launch stub).
+__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+
 // Max / sum over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
 // rows), result in all four.  v_permlane32_swap exchanges the upper half of
 // one register with the lower half of the other, v_permlane16_swap the odd

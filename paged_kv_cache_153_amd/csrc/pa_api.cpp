@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -432,6 +433,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   if (kernel & ~(0xFF | PA_KV_CACHED)) return fail(PA_ERR_INVALID_ARG, "kernel flags");
   if ((kernel & 0xFF) != PA_KERNEL_AUTO && (kernel & 0xFF) != PA_KERNEL_MFMA)
     return fail(PA_ERR_UNSUPPORTED, "prefill runs on the matrix cores only");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "prefill scale must be positive and finite");
   const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
   if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   if (num_seqs == 0 || total_queries == 0 || max_query_len == 0) return PA_OK;

@@ -35,6 +35,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -46,6 +48,8 @@ constexpr float kSlack = 8.f;
 constexpr float kPLog = 7.f;
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kKeys = 32;           // keys per step: two 16-key MFMA tiles
+constexpr int kBufs = 4;            // LDS step buffers
+constexpr int kAhead = 3;           // steps in flight ahead of the one computed
 
 template <int D>
 struct VRow;  // per-lane share of one V row: 16 bytes (D=128) or 8 bytes (D=64)
@@ -81,7 +85,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   constexpr int TOK_W = COLS_W / G;          // query tokens per wave
   using vrow_t = typename VRow<D>::type;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][TILE];  // [buf][K|V]
+  // [buffer][K|V]: step st lives in buffer st % kBufs; its rows arrive by
+  // direct global->LDS loads issued kAhead steps before it is used
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kBufs][2][TILE];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -143,52 +149,59 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const int lrow = lane / CPR;
   const int lch = lane % CPR;
 
+  // Step sl goes to buffer sl % kBufs.  Wave w's round j fills rows
+  // (4 j + w) * RPW .. + RPW - 1 of the K and the V tile: lane l lands at
+  // byte 16 l of that 1 KiB piece, i.e. row + l / CPR, physical chunk
+  // l % CPR, so it loads logical chunk (l % CPR) ^ (row & (CPR - 1)).  Rows
+  // past the context load row n - 1 instead (finite; their weights are 0).
+  // Steps past the last re-read it, so every step issues the same loads and
+  // the wait counts stay fixed.
+  constexpr int LPS = 2 * ROUNDS;  // loads per lane per step
   int ids[ROUNDS];
-  u32x4_t stk[ROUNDS], stv[ROUNDS];
-  auto fetch_ids = [&](int st) {
+  auto fetch_ids = [&](int sl) {
+    const int sd = min(sl, nsteps - 1);
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
-      const int lb = (st * kKeys + (j * kWaves + w) * RPW) / BS;  // wave-uniform
+      const int k0 = min(sd * kKeys + (j * kWaves + w) * RPW, n - 1);
+      const int lb = k0 / BS;  // wave-uniform: the piece's rows share a block
       const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
       ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
     }
   };
-  auto issue = [&](int st) {
+  auto issue = [&](int sl, auto B) {
+    constexpr int b = decltype(B)::value;
+    const int sd = min(sl, nsteps - 1);
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
-      const int key0 = st * kKeys + (j * kWaves + w) * RPW;
-      const char* base = kvg + (size_t)ids[j] * block_bytes;
-      const uint32_t off = (uint32_t)(((key0 % BS) + lrow) * (2 * D) + lch * 16);
-      stk[j] = load16_at(base, off);
-      stv[j] = load16_at(base + v_bytes, off);
-    }
-  };
-  auto stash = [&](int st, int b) {
-#pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) {
-      const int r = (j * kWaves + w) * RPW + lrow;
-      const uint32_t o = tile_off<D>(r, lch);
-      u32x4_t v = stv[j];
-      if (st * kKeys + r >= n) v = u32x4_t{0u, 0u, 0u, 0u};  // past the context
-      *reinterpret_cast<u32x4_t*>(&lds[b][0][o]) = stk[j];
-      *reinterpret_cast<u32x4_t*>(&lds[b][1][o]) = v;
+      const int piece = j * kWaves + w;
+      const int r = piece * RPW + lrow;
+      const int key = min(sd * kKeys + r, n - 1);
+      const int c = lch ^ (r & (CPR - 1));
+      const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D) + c * 16;
+      load_lds16(src, &lds[b][0][piece * 1024]);
+      load_lds16(src + v_bytes, &lds[b][1][piece * 1024]);
     }
   };
 
-  float m[CB], l[CB];
-  float4_t acc[CB][NE];
+  // acc: O^T blocks; acl: the weight sums, as one more block whose V rows
+  // are all ones (the matrix cores add the weights, so numerator and
+  // denominator sum the same rounded parts)
+  float m[CB];
+  float4_t acc[CB][NE], acl[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     m[cb] = kMaxInit;
-    l[cb] = 0.f;
+    acl[cb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[cb][e] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float cs = a.scale_log2;
+  const half8_t ones = __builtin_bit_cast(
+      half8_t, u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u});
+  const float cs = a.scale_log2;  // > 0: the max is taken on the raw scores
 
-  auto compute = [&](int st, int b) {
+  auto qk = [&](auto B, float4_t (&sc)[CB][2]) {
+    constexpr int b = decltype(B)::value;
     const unsigned char* kt = lds[b][0];
-    const unsigned char* vt = lds[b][1];
     u32x4_t kr[2][KS];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -197,7 +210,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
         kr[kk][j] =
             *reinterpret_cast<const u32x4_t*>(kt + tile_off<D>(16 * kk + col, 4 * j + quad));
     // 2 * CB independent accumulations, interleaved over the contraction
-    float4_t sc[CB][2];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) sc[cb][0] = sc[cb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -208,6 +220,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
         for (int cb = 0; cb < CB; ++cb)
           sc[cb][kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               __builtin_bit_cast(half8_t, kr[kk][j]), qop[cb][j], sc[cb][kk], 0, 0, 0);
+  };
+
+  auto softmax_pv = [&](int st, auto B, const float4_t (&sc)[CB][2]) {
+    constexpr int b = decltype(B)::value;
+    const unsigned char* vt = lds[b][1];
     // V rows 4 quad + i of both tiles, this lane's D/16 values of each
     vrow_t vr[8];
 #pragma unroll
@@ -222,11 +239,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     half8_t phi[CB], plo[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      float y[8];
+      float y[8];  // raw scores; in log2 units they are cs * y
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[4 * kk + i] = sc[cb][kk][i] * cs;
+        for (int i = 0; i < 4; ++i) y[4 * kk + i] = sc[cb][kk][i];
       if (edge) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -234,28 +251,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
           if (t > p_col[cb]) y[k] = -INFINITY;
         }
       }
-      const float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
-                             fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      const float lm = cs * fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                                  fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
       if (wave_any(lm > m[cb] + kSlack)) {
         // some column's reference must move: to the column's max, exactly
         const float m_new = fmaxf(m[cb], rows4_max(lm));
         const float alpha = fast_exp2(m[cb] - m_new);
-        l[cb] *= alpha;
+        acl[cb] *= alpha;
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
         m[cb] = m_new;
       }
-      const float mo = m[cb] - kPLog;
+      const float off = kPLog - m[cb];
       float pw[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(y[k] - mo);
-      l[cb] += ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(fmaf(y[k], cs, off));
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const auto h = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
-        const auto r = __builtin_amdgcn_cvt_pkrtz(pw[2 * k] - (float)h[0],
-                                                  pw[2 * k + 1] - (float)h[1]);
+        const auto r = __builtin_amdgcn_cvt_pkrtz(fmaf((float)h[0], -1.f, pw[2 * k]),
+                                                  fmaf((float)h[1], -1.f, pw[2 * k + 1]));
         hw[k] = __builtin_bit_cast(uint32_t, h);
         lw[k] = __builtin_bit_cast(uint32_t, r);
       }
@@ -264,6 +280,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     }
     // P.V in pairs of output blocks: each accumulator's hi and lo products
     // are 2 * CB instructions apart
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, phi[cb], acl[cb], 0, 0, 0);
 #pragma unroll
     for (int e0 = 0; e0 < NE; e0 += 2) {
       half8_t av[2];
@@ -291,33 +310,64 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
           acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ee], plo[cb],
                                                                     acc[cb][e0 + ee], 0, 0, 0);
     }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo[cb], acl[cb], 0, 0, 0);
   };
 
-  // ---- steps 0 .. nsteps - 1: step st + 1 is loaded while st is computed ----
+  // ---- steps 0 .. nsteps - 1 ----------------------------------------------
+  // Iteration st: wait until step st + 1 has landed (own loads, then the
+  // barrier for everyone's), issue step st + kAhead into the buffer step
+  // st - 1 used, then run q.K of step st + 1 on the matrix cores while the
+  // softmax of step st runs on the vector ALUs, and P.V of step st.
+  auto vm_wait = [](auto N) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(N)::value) : "memory");
+  };
+  auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   fetch_ids(0);
-  issue(0);
+  issue(0, I0{});
   fetch_ids(1);
-  stash(0, 0);
-  if (nsteps > 1) {
-    issue(1);
-    fetch_ids(2);
-  }
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int b = st & 1;
-    if (st * kKeys <= w_pmax) compute(st, b);
-    if (st + 1 < nsteps) stash(st + 1, b ^ 1);
-    if (st + 2 < nsteps) {
-      issue(st + 2);
-      fetch_ids(st + 3);
+  issue(1, I1{});
+  fetch_ids(2);
+  issue(2, I2{});
+  fetch_ids(3);
+  vm_wait(std::integral_constant<int, 2 * LPS>{});
+  barrier();
+  float4_t sc[CB][2];
+  if (w_pmax >= 0) qk(I0{}, sc);
+  auto step = [&](int st, auto B) {
+    constexpr int b = decltype(B)::value;
+    vm_wait(std::integral_constant<int, LPS>{});
+    barrier();
+    issue(st + kAhead, std::integral_constant<int, (b + kAhead) % kBufs>{});
+    fetch_ids(st + kAhead + 1);
+    if (st * kKeys <= w_pmax) {
+      float4_t sn[CB][2];
+      qk(std::integral_constant<int, (b + 1) % kBufs>{}, sn);
+      softmax_pv(st, B, sc);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        sc[cb][0] = sn[cb][0];
+        sc[cb][1] = sn[cb][1];
+      }
     }
-    __syncthreads();
+  };
+  for (int st = 0; st < nsteps; st += kBufs) {  // fixed buffers in each trip
+    step(st, I0{});
+    if (st + 1 < nsteps) step(st + 1, I1{});
+    if (st + 2 < nsteps) step(st + 2, I2{});
+    if (st + 3 < nsteps) step(st + 3, I3{});
   }
+  vm_wait(std::integral_constant<int, 0>{});  // no load may land after the exit
 
   // ---- normalise and store: lane (quad, col) holds d = VH * (4 quad + i) + e
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const float lt = rows4_sum(l[cb]);
+    const float lt = acl[cb][0];
     if (tok[cb] < T) {
       const float inv = 1.f / lt;
       float* o = a.out + ((size_t)(q0 + tok[cb]) * a.num_q_heads + g * G + hh) * D;

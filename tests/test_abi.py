@@ -340,7 +340,8 @@ def _prefill_status(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=0), -2), (dict(dtype=2), -2), (dict(kernel=1), -2), (dict(D=96), -2),
     (dict(bs=24), -2), (dict(Hq=6), -2), (dict(Hq=7), -1), (dict(kernel=0x200), -1),
-    (dict(NB=0), -1), (dict(S=-1), -1),
+    (dict(NB=0), -1), (dict(S=-1), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
+    (dict(scale=float("inf")), -1), (dict(scale=float("nan")), -1),
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert _prefill_status(**kw) == status

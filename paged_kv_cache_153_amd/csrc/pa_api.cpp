@@ -455,10 +455,11 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = (int)max_tokens_ll;
-  {  // PA_TUNE_VARIANT=0|1 overrides the columns per wave (tuning experiments only)
+  {  // PA_TUNE_VARIANT=0..2 (tuning experiments only): 1 = 16 columns per wave,
+     // 2 = 32 columns without the interleaved instruction schedule
     const char* e = std::getenv("PA_TUNE_VARIANT");
     const int forced = e ? std::atoi(e) : -1;
-    a.variant = forced >= 0 && forced <= 1 ? forced : 0;
+    a.variant = forced >= 0 && forced <= 2 ? forced : 0;
   }
   const long long cols = (long long)max_query_len * group;
   const int per_wg = pa::prefill_columns_per_workgroup(a.variant);

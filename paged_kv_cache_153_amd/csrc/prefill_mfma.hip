@@ -69,7 +69,7 @@ __device__ __forceinline__ uint32_t tile_off(int r, int c) {
   return (uint32_t)(r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
 }
 
-template <int D, int BS, int G, int CB>
+template <int D, int BS, int G, int CB, bool SCHED>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KS = D / 32;                 // 16x16x32 steps of q.K
@@ -222,7 +222,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
               __builtin_bit_cast(half8_t, kr[kk][j]), qop[cb][j], sc[cb][kk], 0, 0, 0);
   };
 
-  auto softmax_pv = [&](int st, auto B, const float4_t (&sc)[CB][2]) {
+  // softmax and P.V of step st; q.K of the next step (buffer Bn) is issued
+  // between the max and the exponentials, so its matrix-core work overlaps
+  // the vector work of this step
+  auto softmax_pv = [&](int st, auto B, const float4_t (&sc)[CB][2], auto Bn,
+                        float4_t (&sn)[CB][2]) {
     constexpr int b = decltype(B)::value;
     const unsigned char* vt = lds[b][1];
     // V rows 4 quad + i of both tiles, this lane's D/16 values of each
@@ -236,23 +240,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
         vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + tile_off<D>(r, col >> 1) + (col & 1) * 8);
     }
     const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n;
-    half8_t phi[CB], plo[CB];
+    float y[CB][8];  // raw scores; in log2 units they are cs * y
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      float y[8];  // raw scores; in log2 units they are cs * y
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[4 * kk + i] = sc[cb][kk][i];
+        for (int i = 0; i < 4; ++i) y[cb][4 * kk + i] = sc[cb][kk][i];
       if (edge) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int t = st * kKeys + (k >> 2) * 16 + 4 * quad + (k & 3);
-          if (t > p_col[cb]) y[k] = -INFINITY;
+          if (t > p_col[cb]) y[cb][k] = -INFINITY;
         }
       }
-      const float lm = cs * fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
-                                  fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      const float lm = cs * fmaxf(fmaxf(fmaxf(y[cb][0], y[cb][1]), fmaxf(y[cb][2], y[cb][3])),
+                                  fmaxf(fmaxf(y[cb][4], y[cb][5]), fmaxf(y[cb][6], y[cb][7])));
       if (wave_any(lm > m[cb] + kSlack)) {
         // some column's reference must move: to the column's max, exactly
         const float m_new = fmaxf(m[cb], rows4_max(lm));
@@ -262,10 +265,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
         for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
         m[cb] = m_new;
       }
+    }
+    qk(Bn, sn);
+    half8_t phi[CB], plo[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
       const float off = kPLog - m[cb];
       float pw[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(fmaf(y[k], cs, off));
+      for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(fmaf(y[cb][k], cs, off));
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -313,6 +321,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo[cb], acl[cb], 0, 0, 0);
+    if constexpr (SCHED) {
+      // K reads first, then each q.K product followed by vector work
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS * CB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
   };
 
   // ---- steps 0 .. nsteps - 1 ----------------------------------------------
@@ -347,8 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     fetch_ids(st + kAhead + 1);
     if (st * kKeys <= w_pmax) {
       float4_t sn[CB][2];
-      qk(std::integral_constant<int, (b + 1) % kBufs>{}, sn);
-      softmax_pv(st, B, sc);
+      softmax_pv(st, B, sc, std::integral_constant<int, (b + 1) % kBufs>{}, sn);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         sc[cb][0] = sn[cb][0];
@@ -383,18 +399,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   }
 }
 
-template <int D, int BS, int G, int CB>
+template <int D, int BS, int G, int CB, bool SCHED>
 int launch_cb(const PrefillArgs& a, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)a.num_seqs * a.qblocks * a.num_kv_heads);
   if (grid == 0) return 0;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, CB>), dim3(grid), dim3(kWaves * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, CB, SCHED>), dim3(grid), dim3(kWaves * 64),
+                     0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 template <int D, int BS, int G>
 int launch_one(const PrefillArgs& a, hipStream_t stream) {
-  return a.variant == 1 ? launch_cb<D, BS, G, 1>(a, stream) : launch_cb<D, BS, G, 2>(a, stream);
+  switch (a.variant) {
+    case 1: return launch_cb<D, BS, G, 1, false>(a, stream);
+    case 2: return launch_cb<D, BS, G, 2, false>(a, stream);
+    default: return launch_cb<D, BS, G, 2, true>(a, stream);
+  }
 }
 
 template <int D, int BS>

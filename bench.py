@@ -102,7 +102,8 @@ class Step:
     """Holds the block manager, device buffers and the per-step logic."""
 
     def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
-                 window=0, kv_dtype="f16", kv_loads="auto", prefix_cache=False):
+                 window=0, kv_dtype="f16", kv_loads="auto", prefix_cache=False,
+                 upload="kernel"):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -226,6 +227,7 @@ class Step:
                                       sliding_window=window)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         # one packed host->device transfer per step: slots | pairs | lens | tables
+        self.upload = upload
         self.n_i32 = 2 * S + 2 * S + S + S * self.mb
         self.d_pack = torch.empty(self.n_i32, dtype=torch.int32, device=dev)
         self.d_slots, self.d_pairs, self.d_lens, self.d_tables = self._views(self.d_pack)
@@ -284,7 +286,10 @@ class Step:
         buf["event"].synchronize()          # its previous copies have left pinned memory
         ncow = self.host_step(buf)
         maxlen = int(buf["lens"].max())
-        self.d_pack.copy_(buf["pack"], non_blocking=True)
+        if self.upload == "kernel":
+            pa.stage_from_host(self.d_pack, buf["pack"])
+        else:
+            self.d_pack.copy_(buf["pack"], non_blocking=True)
         buf["event"].record()
         pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
                        cow_pairs=self.d_pairs[:ncow] if ncow else None, kv_scales=self.kv_scales)
@@ -553,6 +558,9 @@ def main():
     ap.add_argument("--prefix-cache", action="store_true",
                     help="shared_prefix: admit the requests through the block manager's prefix "
                          "cache (block-hash lookup) instead of sharing the prefix by hand")
+    ap.add_argument("--upload", default="kernel", choices=["kernel", "dma"],
+                    help="per-step host->device upload of tables/lengths/slots: a kernel "
+                         "reading the pinned buffer (pa_stage_from_host) or a DMA copy")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill"],
                     help="prefill: chunked-prefill attention (pa_prefill) instead of decode")
     ap.add_argument("--chunk", type=int, default=512, help="prefill: new tokens per sequence")
@@ -585,7 +593,8 @@ def main():
         return
     st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
               args.partition, dev, context=args.context, window=args.window,
-              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads, prefix_cache=args.prefix_cache)
+              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads, prefix_cache=args.prefix_cache,
+              upload=args.upload)
     step_fn = st.run
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -642,6 +651,8 @@ def main():
             "sliding_window": args.window or None,
             "kv_cache": "int8 codes + f32 row scales" if st.int8 else w["dtype"],
             "kv_loads": "cached" if st.cached_kv else "streaming (non-temporal)",
+            "upload": ("pa_stage_from_host kernel" if st.upload == "kernel"
+                       else "DMA copy (torch copy_)"),
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),

@@ -117,6 +117,23 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
                    int block_size, int dtype, void* stream);
 
 /* -------------------------------------------------------------------------
+ * 1b. Per-step upload of the host bookkeeping ([KVPA] §5.3: the block table
+ *     lives on the host and is copied to the GPU for each attention call)
+ *
+ * Copies `bytes` from page-locked host memory (hipHostMalloc, e.g. a torch
+ * pin_memory tensor; the GPU addresses it directly) to device memory with a
+ * kernel on `stream` that reads the host buffer over the bus, instead of a
+ * DMA transfer: for the few tens of kilobytes a decode step uploads (block
+ * tables, lengths, slots, copy pairs) this saves the copy engine's round
+ * trip and hand-off to the compute queue.  The host must not change `src`
+ * until the stream has passed this call (record an event after it).
+ *   dst    device, 16-byte aligned
+ *   src    page-locked host, 16-byte aligned
+ *   bytes  >= 0, a multiple of 4 (0 = nothing to do)
+ * ------------------------------------------------------------------------- */
+int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream);
+
+/* -------------------------------------------------------------------------
  * 2. Decode attention ([KVPA] §2.1 formula, §4.3 block-table addressing,
  *    §7.2 online softmax; [NANO] §2.4 kernel structure; [KV2P] §5.3 GQA)
  *

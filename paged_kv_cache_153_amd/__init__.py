@@ -61,6 +61,7 @@ _SIGNATURES = {
     "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
                               _c.c_int, _c.c_int, _P]),
+    "pa_stage_from_host": (_c.c_int, [_P, _P, _c.c_int64, _P]),
     "pa_bm_create": (_P, [_c.c_int64, _c.c_int]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_allocate": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
@@ -163,6 +164,22 @@ def _need_cuda(*tensors):
             raise ValueError("tensors must be on the GPU")
         if t is not None and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def stage_from_host(dst, src, stream=None):
+    """Copy the page-locked host tensor ``src`` into the device tensor ``dst``
+    (same number of bytes, both contiguous) with a kernel that reads the host
+    buffer directly; enqueued on ``stream`` (default: the current stream)."""
+    if not src.is_pinned() or src.is_cuda:
+        raise TypeError("src must be a pinned host tensor")
+    if not dst.is_cuda or not dst.is_contiguous() or not src.is_contiguous():
+        raise TypeError("dst must be a contiguous device tensor and src contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src sizes differ")
+    _check(lib().pa_stage_from_host(dst.data_ptr(), src.data_ptr(), nbytes,
+                                    _stream(dst.device, stream)))
+    return dst
 
 
 def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None,

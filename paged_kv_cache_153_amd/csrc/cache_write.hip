@@ -135,7 +135,35 @@ void copy_blocks(void* buf, const int32_t* cow_pairs, int64_t num_cow, int64_t b
   }
 }
 
+// Host -> device upload of a small page-locked buffer by a kernel that reads
+// it over the bus (16-byte loads, then a 4-byte tail): the per-step tables
+// reach the GPU without a copy-engine transfer and its hand-off to the
+// compute queue.
+__global__ __launch_bounds__(256) void stage_kernel(u32x4_t* __restrict__ dst,
+                                                    const u32x4_t* __restrict__ src, int64_t n16,
+                                                    uint32_t* __restrict__ dst_tail,
+                                                    const uint32_t* __restrict__ src_tail,
+                                                    int tail) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+  if (blockIdx.x == 0 && (int)threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+}
+
 }  // namespace
+
+int launch_stage(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int tail = (int)((bytes % 16) / 4);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL(stage_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<u32x4_t*>(dst), reinterpret_cast<const u32x4_t*>(src), n16,
+                     reinterpret_cast<uint32_t*>(dst) + 4 * n16,
+                     reinterpret_cast<const uint32_t*>(src) + 4 * n16, tail);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 int launch_cache_write(const void* key, const void* value, void* kv, float* scales,
                        const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,

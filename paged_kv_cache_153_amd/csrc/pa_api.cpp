@@ -264,6 +264,17 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv
   return rc ? fail(PA_ERR_UNSUPPORTED, "cache write") : PA_OK;
 }
 
+int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream_) {
+  pa::clear_error();
+  if (bytes < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (bytes == 0) return PA_OK;
+  if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(dst) || !aligned16(src) || bytes % 4)
+    return fail(PA_ERR_INVALID_ARG, "dst/src must be 16-byte aligned and bytes a multiple of 4");
+  const int rc = pa::launch_stage(dst, src, bytes, reinterpret_cast<hipStream_t>(stream_));
+  return rc ? fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError())) : PA_OK;
+}
+
 int pa_decode(float* out, const void* query, const void* kv_cache, const float* kv_scales,
               const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
               int head_dim, int block_size, int max_blocks_per_seq, int max_context_len,

@@ -351,3 +351,19 @@ def test_prefill_null_pointers_and_empty_batch():
     fake = ctypes.c_void_p(1 << 20)
     assert _prefill_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, qs=None) == -1
     assert _prefill_status(S=0) == 0 and _prefill_status(total=0) == 0
+
+
+@pytest.mark.parametrize("dst,src,nbytes,status", [
+    (None, 1 << 20, 64, -1), (1 << 20, None, 64, -1), ((1 << 20) + 4, 1 << 20, 64, -1),
+    (1 << 20, (1 << 20) + 8, 64, -1), (1 << 20, 1 << 20, 66, -1), (1 << 20, 1 << 20, -4, -1),
+])
+def test_stage_from_host_rejects_bad_arguments(dst, src, nbytes, status):
+    """Checked on the host before anything is enqueued (the pointers are never
+    dereferenced)."""
+    d = ctypes.c_void_p(dst) if dst else None
+    s = ctypes.c_void_p(src) if src else None
+    assert pa.lib().pa_stage_from_host(d, s, nbytes, None) == status
+
+
+def test_stage_from_host_zero_bytes_is_a_no_op():
+    assert pa.lib().pa_stage_from_host(None, None, 0, None) == 0

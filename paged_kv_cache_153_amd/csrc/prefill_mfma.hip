@@ -30,8 +30,10 @@
 //                (k = 8q + j  ->  key 4q + j of tile j / 4); V is read with
 //                the same relabelling, and the weights go in as fp16 hi + lo
 //                parts, which keeps ~21 bits of each weight.
-// LDS rows are 2D bytes with 16-byte chunks XOR-swizzled by the row, so that
-// the 16 lanes that read one chunk of 16 different K rows hit distinct banks.
+// LDS rows are 2D bytes.  K rows have their 16-byte chunks XOR-swizzled by
+// the row, so that the 16 lanes that read one chunk of 16 different K rows
+// hit distinct banks; V rows are plain, since the lanes of a quad read one V
+// row whole (measured: an XOR swizzle by row there costs a two-way conflict).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -177,9 +179,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       const int r = piece * RPW + lrow;
       const int key = min(sd * kKeys + r, n - 1);
       const int c = lch ^ (r & (CPR - 1));
-      const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D) + c * 16;
-      load_lds16(src, &lds[b][0][piece * 1024]);
-      load_lds16(src + v_bytes, &lds[b][1][piece * 1024]);
+      const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D);
+      load_lds16(src + c * 16, &lds[b][0][piece * 1024]);            // K: swizzled
+      load_lds16(src + v_bytes + lch * 16, &lds[b][1][piece * 1024]);  // V: plain rows
     }
   };
 
@@ -235,9 +237,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     for (int jv = 0; jv < 8; ++jv) {
       const int r = (jv >> 2) * 16 + 4 * quad + (jv & 3);
       if constexpr (D == 128)
-        vr[jv] = *reinterpret_cast<const u32x4_t*>(vt + tile_off<D>(r, col));
+        vr[jv] = *reinterpret_cast<const u32x4_t*>(vt + r * (2 * D) + col * 16);
       else
-        vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + tile_off<D>(r, col >> 1) + (col & 1) * 8);
+        vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + r * (2 * D) + col * 8);
     }
     const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n;
     float y[CB][8];  // raw scores; in log2 units they are cs * y

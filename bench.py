@@ -210,7 +210,7 @@ class Step:
         if self.int8:
             self.pool = synth.int8_codes((nb, 2, Hkv, bs, D), g, dev,
                                          chunk_rows=max(1, (1 << 26) // (2 * Hkv * bs * D)))
-            self.kv_scales = (torch.rand((nb, 2, Hkv, bs), generator=g, device=dev) * 0.02
+            self.kv_scales = (torch.rand((nb, Hkv, 2, bs), generator=g, device=dev) * 0.02
                               + 0.01) * w["std"]
         else:
             self.pool = synth.normal((nb, 2, Hkv, bs, D), tdt, g, dev, w["std"],

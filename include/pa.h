@@ -57,7 +57,7 @@ typedef enum pa_dtype {
   PA_F16 = 1, /* IEEE binary16 */
   /* INT8 KV cache ([KV2P] §5.2: INT8 halves the cache; one scale per group
    * of 128 elements).  kv_cache holds int8 codes, and a separate kv_scales
-   * array [num_blocks, 2, num_kv_heads, block_size] float32 holds one scale
+   * array [num_blocks, num_kv_heads, 2, block_size] float32 holds one scale
    * per (token, KV head) row of K and of V (the row of head_dim values is
    * the group).  Value = code * scale.  pa_cache_write takes binary16 key
    * and value rows and quantises them; pa_decode takes a binary16 query.
@@ -100,7 +100,7 @@ typedef enum pa_kernel {
  *                (binary16 for PA_I8), contiguous, 16-byte aligned
  *   kv_cache     device, [num_blocks, 2, num_kv_heads, block_size, head_dim],
  *                dtype, contiguous, 16-byte aligned; index 1 of dim 1 is V
- *   kv_scales    PA_I8: device, [num_blocks, 2, num_kv_heads, block_size]
+ *   kv_scales    PA_I8: device, [num_blocks, num_kv_heads, 2, block_size]
  *                float32, 16-byte aligned (num_kv_heads * block_size even);
  *                otherwise NULL
  *   slot_mapping device, [num_tokens] int64; slot < 0 skips the row; slots

@@ -16,7 +16,8 @@ Readings (the pages give no formula)
 * Group = the ``head_dim`` values of one token of one KV head, for K and for
   V separately: one group of 128 elements at head_dim 128 (the page's
   example), the whole 64-element row at head_dim 64.  Each group has its own
-  float32 scale, stored beside the codes: ``scales[block, 0|1, head, row]``.
+  float32 scale, stored beside the codes as ``scales[block, head, 0|1, row]``
+  (the K and V scales of one block and head side by side).
 * Symmetric quantisation: ``scale = amax / 127`` with ``amax = max |x|`` over
   the group, codes ``q = clamp(rint(x / scale), -127, 127)`` (round half to
   even), dequantised value ``q * scale``.  A group that is all zeros has
@@ -63,7 +64,7 @@ def cache_write_i8_ref(kv_codes, kv_scales, key, value, slot_mapping, cow_pairs=
     """The slot-mapped write of ``cache.cache_write_ref`` into an INT8 pool.
 
     kv_codes:     [NB, 2, Hkv, bs, D] int8
-    kv_scales:    [NB, 2, Hkv, bs] float32
+    kv_scales:    [NB, Hkv, 2, bs] float32
     key, value:   [T, Hkv, D] float16
     slot_mapping: [T] (negative = skip); cow_pairs: (src, dst) block copies,
                   applied first, codes and scales alike
@@ -82,13 +83,15 @@ def cache_write_i8_ref(kv_codes, kv_scales, key, value, slot_mapping, cow_pairs=
             continue
         block, offset = divmod(int(slot), block_size)
         codes[block, 0, :, offset, :] = kq[i]
-        scales[block, 0, :, offset] = ks[i]
+        scales[block, :, 0, offset] = ks[i]
         codes[block, 1, :, offset, :] = vq[i]
-        scales[block, 1, :, offset] = vs[i]
+        scales[block, :, 1, offset] = vs[i]
     return codes, scales
 
 
 def decode_i8_ref(q, kv_codes, kv_scales, block_tables, context_lens, scale, window=0):
-    """Decode attention over the dequantised INT8 pool (float64)."""
-    return decode_ref(q, dequantize_ref(kv_codes, kv_scales), block_tables, context_lens, scale,
+    """Decode attention over the dequantised INT8 pool (float64); scales
+    [NB, Hkv, 2, bs] as ``cache_write_i8_ref`` writes them."""
+    per_row = np.swapaxes(np.asarray(kv_scales), 1, 2)    # -> [NB, 2, Hkv, bs], as the codes
+    return decode_ref(q, dequantize_ref(kv_codes, per_row), block_tables, context_lens, scale,
                       window=window)

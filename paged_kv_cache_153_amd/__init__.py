@@ -130,10 +130,10 @@ def _dtype_code(t):
 
 
 def kv_scales_like(kv_cache):
-    """A zeroed float32 scale array [NB, 2, Hkv, bs] for an INT8 pool."""
+    """A zeroed float32 scale array [NB, Hkv, 2, bs] for an INT8 pool."""
     torch = _torch()
     nb, two, hkv, bs, _ = kv_cache.shape
-    return torch.zeros((nb, two, hkv, bs), dtype=torch.float32, device=kv_cache.device)
+    return torch.zeros((nb, hkv, two, bs), dtype=torch.float32, device=kv_cache.device)
 
 
 def _scales_ptr(kv_cache, kv_scales):
@@ -145,8 +145,8 @@ def _scales_ptr(kv_cache, kv_scales):
         return None
     nb, two, hkv, bs, _ = kv_cache.shape
     if kv_scales is None or kv_scales.dtype != torch.float32 or \
-            tuple(kv_scales.shape) != (nb, two, hkv, bs):
-        raise TypeError("an INT8 pool needs kv_scales float32 [NB, 2, Hkv, bs]")
+            tuple(kv_scales.shape) != (nb, hkv, two, bs):
+        raise TypeError("an INT8 pool needs kv_scales float32 [NB, Hkv, 2, bs]")
     _need_cuda(kv_scales)
     return kv_scales.data_ptr()
 

@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256) void cache_write_i8_kernel(const u32x4_t* __re
     }
     const int64_t b = slot / block_size;
     const int64_t r = slot - b * block_size;
-    const int64_t srow = ((b * 2 + kv) * num_kv_heads + h) * block_size + r;  // scale index
-    codes[srow * TPR + c] = u32x2_t{w[0], w[1]};
+    const int64_t crow = ((b * 2 + kv) * num_kv_heads + h) * block_size + r;  // [NB, 2, Hkv, BS]
+    const int64_t srow = ((b * num_kv_heads + h) * 2 + kv) * block_size + r;  // [NB, Hkv, 2, BS]
+    codes[crow * TPR + c] = u32x2_t{w[0], w[1]};
     if (c == 0) scales[srow] = sc;
   }
 }

@@ -103,14 +103,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
     }
   }
 
-  // codes: [NB, 2, Hkv, BS, D] bytes; scales: [NB, 2, Hkv, BS] floats
+  // codes: [NB, 2, Hkv, BS, D] bytes; scales: [NB, Hkv, 2, BS] floats
   const size_t head_stride = (size_t)BS * D;
   const size_t block_stride = 2 * (size_t)a.num_kv_heads * head_stride;
   const size_t v_offset = (size_t)a.num_kv_heads * head_stride;
   const int8_t* kvh = reinterpret_cast<const int8_t*>(a.kv) + (size_t)g * head_stride;
   const size_t sblock_stride = 2 * (size_t)a.num_kv_heads * BS;
-  const size_t sv_offset = (size_t)a.num_kv_heads * BS;
-  const float* sch = a.kv_scales + (size_t)g * BS;
+  const size_t sv_offset = BS;  // scales [NB, Hkv, 2, BS]: K then V of one head, one line
+  const float* sch = a.kv_scales + (size_t)g * 2 * BS;
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
 
   int ids[BPT];

@@ -26,7 +26,7 @@ struct DecodeArgs {
   float* ws_l;              // [S, Hq, NP] partition sum of exp2(y - m)
   const void* q;            // [S, Hq, D]
   const void* kv;           // [NB, 2, Hkv, BS, D]
-  const float* kv_scales;   // INT8 pool: [NB, 2, Hkv, BS] row scales; else null
+  const float* kv_scales;   // INT8 pool: [NB, Hkv, 2, BS] row scales; else null
   const int32_t* bt;        // [S, MB]
   const int32_t* cl;        // [S]
   int64_t num_blocks;       // NB
@@ -88,7 +88,7 @@ int decode_mfma_occupancy(const DecodeArgs& a, int head_dim, int block_size, int
 int decode_valu_i8_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
 int decode_mfma_i8_occupancy(const DecodeArgs& a, int head_dim, int block_size, int group);
 // elem_bytes 4 / 2: byte copies; 1: INT8 pool, f16 inputs quantised per
-// row with their scales written to `scales` ([NB, 2, Hkv, BS] floats).
+// row with their scales written to `scales` ([NB, Hkv, 2, BS] floats).
 int launch_stage(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 int launch_cache_write(const void* key, const void* value, void* kv, float* scales,
                        const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,

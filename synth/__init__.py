@@ -57,7 +57,7 @@ class DecodeInputs:
     scale: float
     seed: int
     meta: dict = field(default_factory=dict)
-    kv_scales: torch.Tensor = None   # INT8 pools: [NB, 2, Hkv, bs] float32
+    kv_scales: torch.Tensor = None   # INT8 pools: [NB, Hkv, 2, bs] float32
 
     @property
     def num_seqs(self):
@@ -173,7 +173,7 @@ def int8_codes(shape, gen, device, code_std=42.0, chunk_rows=None):
 
 def int8_pool(x, seed=None, fill_unused=None):
     """The same queries, tables and lengths as ``x`` over a freshly drawn INT8
-    pool: codes [NB, 2, Hkv, bs, D] int8 and scales [NB, 2, Hkv, bs] float32.
+    pool: codes [NB, 2, Hkv, bs, D] int8 and scales [NB, Hkv, 2, bs] float32.
     ``fill_unused`` (e.g. NaN) overwrites the scales of rows no context covers."""
     nb, two, hkv, bs, d = x.kv_cache.shape
     device = x.kv_cache.device
@@ -182,7 +182,7 @@ def int8_pool(x, seed=None, fill_unused=None):
     codes = int8_codes((nb, two, hkv, bs, d), g, device,
                        chunk_rows=max(1, (1 << 26) // (2 * hkv * bs * d)))
     std = float(x.meta.get("std", 1.0))
-    scales = (torch.rand((nb, two, hkv, bs), generator=g, device=device) * 0.02 + 0.01) * std
+    scales = (torch.rand((nb, hkv, two, bs), generator=g, device=device) * 0.02 + 0.01) * std
     if fill_unused is not None:
         covered = torch.zeros((nb, bs), dtype=torch.bool)
         tables = x.block_tables.cpu()

@@ -323,14 +323,15 @@ def quant_failing(quantize, dequantize):
 
 def i8_cache_round_trip(cache_write_i8, quantize, dequantize):
     """Rows written at the slots of the page's printed ranges come back, through
-    the page's table, as their own quantisation (codes and per-row scales in
-    [block, K|V, head, row]); untouched rows and scales stay."""
+    the page's table, as their own quantisation (codes in [block, K|V, head,
+    row], per-row scales in [block, head, K|V, row]); untouched rows and
+    scales stay."""
     ex = page_example()
     bs, n = ex["block_size"], ex["num_tokens"]
     rng = np.random.default_rng(2)
     hkv, d = 3, 16
     codes = rng.integers(-127, 128, (10, 2, hkv, bs, d)).astype(np.int8)
-    scales = rng.uniform(0.1, 1, (10, 2, hkv, bs)).astype(np.float32)
+    scales = rng.uniform(0.1, 1, (10, hkv, 2, bs)).astype(np.float32)
     key = (rng.standard_normal((n, hkv, d)) * 3).astype(np.float16)
     value = rng.standard_normal((n, hkv, d)).astype(np.float16)
     slots = np.empty(n, dtype=np.int64)
@@ -345,13 +346,13 @@ def i8_cache_round_trip(cache_write_i8, quantize, dequantize):
     for t in range(n):
         b, r = table[t // bs], t % bs
         ok &= np.array_equal(c2[b, 0, :, r], kq[t]) and np.array_equal(c2[b, 1, :, r], vq[t])
-        ok &= np.array_equal(s2[b, 0, :, r], ks[t]) and np.array_equal(s2[b, 1, :, r], vs[t])
+        ok &= np.array_equal(s2[b, :, 0, r], ks[t]) and np.array_equal(s2[b, :, 1, r], vs[t])
     # block 3 holds tokens 96..99 in rows 0..3 only; blocks 0 and 4 are not in the table
     ok &= np.array_equal(c2[3, :, :, 4:], codes[3, :, :, 4:])
     ok &= np.array_equal(s2[3, :, :, 4:], scales[3, :, :, 4:])
     ok &= np.array_equal(c2[0], codes[0]) and np.array_equal(s2[4], scales[4])
     # dequantised keys are within half a step of the written ones
-    back = dequantize(c2[table[0], 0, :, :16].transpose(1, 0, 2), s2[table[0], 0, :, :16].T)
+    back = dequantize(c2[table[0], 0, :, :16].transpose(1, 0, 2), s2[table[0], :, 0, :16].T)
     ok &= np.all(np.abs(back - key[:16].astype(np.float64)) <= ks[:16, :, None] * 0.5001)
     return bool(ok)
 
@@ -360,7 +361,7 @@ def i8_cow_before_scatter(cache_write_i8):
     """Copies go first and carry codes and scales; the source stays intact."""
     rng = np.random.default_rng(3)
     codes = rng.integers(-127, 128, (4, 2, 2, 8, 16)).astype(np.int8)
-    scales = rng.uniform(0.1, 1, (4, 2, 2, 8)).astype(np.float32)
+    scales = rng.uniform(0.1, 1, (4, 2, 2, 8)).astype(np.float32)   # [NB, Hkv, K|V, bs]
     key = np.full((1, 2, 16), 2.0, dtype=np.float16)
     value = np.full((1, 2, 16), -4.0, dtype=np.float16)
     c2, s2 = cache_write_i8(codes, scales, key, value, np.array([2 * 8 + 5]), [(1, 2)])
@@ -368,7 +369,7 @@ def i8_cow_before_scatter(cache_write_i8):
     ok &= np.array_equal(np.delete(c2[2], 5, axis=2), np.delete(codes[1], 5, axis=2))
     ok &= np.array_equal(np.delete(s2[2], 5, axis=2), np.delete(scales[1], 5, axis=2))
     ok &= np.all(c2[2, 0, :, 5] == 127) and np.all(c2[2, 1, :, 5] == -127)
-    ok &= np.allclose(s2[2, 0, :, 5], 2 / 127) and np.allclose(s2[2, 1, :, 5], 4 / 127)
+    ok &= np.allclose(s2[2, :, 0, 5], 2 / 127) and np.allclose(s2[2, :, 1, 5], 4 / 127)
     return bool(ok)
 
 
@@ -380,7 +381,7 @@ def i8_decode_is_sdpa_on_dequantised(decode_i8, dequantize):
     nbs = [-(-n // bs) for n in lens]
     nb = sum(nbs) + 2
     codes = rng.integers(-127, 128, (nb, 2, hkv, bs, d)).astype(np.int8)
-    scales = rng.uniform(0.001, 0.05, (nb, 2, hkv, bs)).astype(np.float32)
+    scales = rng.uniform(0.001, 0.05, (nb, hkv, 2, bs)).astype(np.float32)
     perm = rng.permutation(nb)
     tables = np.full((len(lens), max(nbs)), -1)
     pos = 0
@@ -392,8 +393,8 @@ def i8_decode_is_sdpa_on_dequantised(decode_i8, dequantize):
     for s, n in enumerate(lens):
         t = np.arange(n)
         blk = tables[s][t // bs]
-        kk = codes[blk, 0, :, t % bs, :].astype(np.float64) * scales[blk, 0, :, t % bs][..., None]
-        vv = codes[blk, 1, :, t % bs, :].astype(np.float64) * scales[blk, 1, :, t % bs][..., None]
+        kk = codes[blk, 0, :, t % bs, :].astype(np.float64) * scales[blk, :, 0, t % bs][..., None]
+        vv = codes[blk, 1, :, t % bs, :].astype(np.float64) * scales[blk, :, 1, t % bs][..., None]
         kt = torch.from_numpy(kk).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
         vt = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
         ref = torch.nn.functional.scaled_dot_product_attention(

@@ -136,7 +136,7 @@ def test_decode_single_token_is_its_value_row(device):
                 b = int(x.block_tables[s, 0])
                 for h in range(16):
                     want = (x.kv_cache[b, 1, h // 4, 0].double() *
-                            float(x.kv_scales[b, 1, h // 4, 0])).numpy()
+                            float(x.kv_scales[b, h // 4, 1, 0])).numpy()
                     assert np.abs(got[s, h] - want).max() <= 2e-5 * np.abs(want).max() + 1e-7
 
 
@@ -144,7 +144,7 @@ def test_decode_large_scales(device):
     """Scales up to ~500 (rows with values near the f16 maximum): the weights
     times V scales must not overflow inside the kernels."""
     x = _ragged(16, 128, 16, 2, seed=53, lens=(3, 90, 400))
-    x.kv_scales[:, 1] *= 20000.0
+    x.kv_scales[:, :, 1] *= 20000.0
     want = ref(x)
     for kern in ("valu", "mfma"):
         for part in (-1, -2, 64):

@@ -212,7 +212,7 @@ def i8_write_mutant(mistake):
             b, r = divmod(int(slot), bs)
             rs = 0 if mistake == "scale_row_zero" else r
             codes[b, 0, :, r], codes[b, 1, :, r] = kq[i], vq[i]
-            scales[b, 0, :, rs], scales[b, 1, :, rs] = ks[i], vs[i]
+            scales[b, :, 0, rs], scales[b, :, 1, rs] = ks[i], vs[i]
         return codes, scales
     return write
 

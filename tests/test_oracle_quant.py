@@ -63,7 +63,7 @@ def test_i8_cow_copies_codes_and_scales_first():
 def test_i8_negative_slot_writes_nothing():
     rng = np.random.default_rng(4)
     codes = rng.integers(-127, 128, (3, 2, 1, 4, 8)).astype(np.int8)
-    scales = rng.uniform(0.1, 1, (3, 2, 1, 4)).astype(np.float32)
+    scales = rng.uniform(0.1, 1, (3, 1, 2, 4)).astype(np.float32)
     key = np.ones((2, 1, 8), dtype=np.float16)
     c2, s2 = oracle.cache_write_i8_ref(codes, scales, key, key, np.array([-1, -5]))
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
@@ -82,5 +82,5 @@ def test_i8_decode_close_to_fp16_decode():
     codes, scales = oracle.quantize_rows_ref(kv)
     args = (x.q.numpy(), x.block_tables.numpy(), x.context_lens.numpy(), x.scale)
     a = oracle.decode_ref(args[0], kv, *args[1:])
-    b = oracle.decode_i8_ref(args[0], codes, scales, *args[1:])
+    b = oracle.decode_i8_ref(args[0], codes, np.swapaxes(scales, 1, 2), *args[1:])
     assert np.abs(a - b).max() < 0.05 and not np.array_equal(a, b)

@@ -61,9 +61,8 @@ struct PrefillArgs {
   int max_tokens;           // MB * BS
   int qblocks;              // workgroups per (sequence, KV head)
   float scale_log2;
-  int variant;              // 0: 32 columns per wave, 1: 16, 2: 32 unscheduled
 };
-int prefill_columns_per_workgroup(int variant);
+int prefill_columns_per_workgroup();
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream);
 

@@ -466,14 +466,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = (int)max_tokens_ll;
-  {  // PA_TUNE_VARIANT=0..2 (tuning experiments only): 1 = 16 columns per wave,
-     // 2 = 32 columns without the interleaved instruction schedule
-    const char* e = std::getenv("PA_TUNE_VARIANT");
-    const int forced = e ? std::atoi(e) : -1;
-    a.variant = forced >= 0 && forced <= 2 ? forced : 0;
-  }
   const long long cols = (long long)max_query_len * group;
-  const int per_wg = pa::prefill_columns_per_workgroup(a.variant);
+  const int per_wg = pa::prefill_columns_per_workgroup();
   a.qblocks = (int)((cols + per_wg - 1) / per_wg);
   if ((long long)num_seqs * a.qblocks * num_kv_heads >= (1LL << 31))
     return fail(PA_ERR_INVALID_ARG, "grid too large");

@@ -10,13 +10,13 @@
 // block_tables[s, t / BS].
 //
 // Columns are (query token, head) pairs of one KV head, head fastest; a wave
-// owns CB blocks of 16 columns and a workgroup of four waves 64 * CB columns
+// owns CB = 2 blocks of 16 columns and a workgroup of four waves 128 columns
 // of one (sequence, KV head).  The workgroup walks the keys in steps of 32:
-// each step's K and V rows (32 x 2D bytes each) are loaded once, with plain
-// (cached) 16-byte loads whose block ids come from scalar loads, into a
-// double-buffered LDS tile, and every wave takes its matrix operands from
-// there — the prefill reads each K/V row once per workgroup, not once per
-// wave.  Per step and column block:
+// each step's K and V rows (32 x 2D bytes each) arrive by direct global->LDS
+// loads (16 bytes per lane, no registers; block ids from scalar loads),
+// issued three steps ahead into four LDS buffers, and every wave takes its
+// matrix operands from there — the prefill reads each K/V row from L2 once
+// per workgroup, not once per wave.  Per step and column block:
 //   S^T = K q^T  two 16-key tiles x D/32 v_mfma_f32_16x16x32_f16 (K rows are
 //                the A operand, q the B operand);
 //   online softmax per column in log2 units, the causal mask only on steps
@@ -29,7 +29,10 @@
 //                32-deep contraction once the contraction index is relabelled
 //                (k = 8q + j  ->  key 4q + j of tile j / 4); V is read with
 //                the same relabelling, and the weights go in as fp16 hi + lo
-//                parts, which keeps ~21 bits of each weight.
+//                parts, which keeps ~21 bits of each weight;
+//   the weight sums as one more block whose V rows are all ones.
+// q.K of step st + 1 is issued between the max and the exponentials of step
+// st, so the matrix cores have work while the vector ALUs do the softmax.
 // LDS rows are 2D bytes.  K rows have their 16-byte chunks XOR-swizzled by
 // the row, so that the 16 lanes that read one chunk of 16 different K rows
 // hit distinct banks; V rows are plain, since the lanes of a quad read one V
@@ -71,8 +74,9 @@ __device__ __forceinline__ uint32_t tile_off(int r, int c) {
   return (uint32_t)(r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
 }
 
-template <int D, int BS, int G, int CB, bool SCHED>
+template <int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int CB = 2;  // 16-column blocks per wave
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KS = D / 32;                 // 16x16x32 steps of q.K
   constexpr int NE = D / 16;                 // P.V blocks of 16 output rows
@@ -323,8 +327,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo[cb], acl[cb], 0, 0, 0);
-    if constexpr (SCHED) {
-      // K reads first, then each q.K product followed by vector work
+    {  // K reads first, then each q.K product followed by vector work
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
 #pragma unroll
       for (int i = 0; i < 2 * KS * CB; ++i) {
@@ -401,22 +404,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   }
 }
 
-template <int D, int BS, int G, int CB, bool SCHED>
-int launch_cb(const PrefillArgs& a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((size_t)a.num_seqs * a.qblocks * a.num_kv_heads);
-  if (grid == 0) return 0;
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G, CB, SCHED>), dim3(grid), dim3(kWaves * 64),
-                     0, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : 2;
-}
-
 template <int D, int BS, int G>
 int launch_one(const PrefillArgs& a, hipStream_t stream) {
-  switch (a.variant) {
-    case 1: return launch_cb<D, BS, G, 1, false>(a, stream);
-    case 2: return launch_cb<D, BS, G, 2, false>(a, stream);
-    default: return launch_cb<D, BS, G, 2, true>(a, stream);
-  }
+  const unsigned grid = (unsigned)((size_t)a.num_seqs * a.qblocks * a.num_kv_heads);
+  if (grid == 0) return 0;
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, BS, G>), dim3(grid), dim3(kWaves * 64), 0, stream,
+                     a);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 template <int D, int BS>
@@ -442,7 +436,7 @@ int by_block(const PrefillArgs& a, int block_size, int group, hipStream_t stream
 
 }  // namespace
 
-int prefill_columns_per_workgroup(int variant) { return kWaves * 16 * (variant == 1 ? 1 : 2); }
+int prefill_columns_per_workgroup() { return kWaves * 32; }
 
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream) {

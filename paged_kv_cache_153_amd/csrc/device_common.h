@@ -152,7 +152,7 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
 #endif
 }
 
-// Max / sum over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
+// Max over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
 // rows), result in all four.  v_permlane32_swap exchanges the upper half of
 // one register with the lower half of the other, v_permlane16_swap the odd
 // rows of one with the even rows of the other: with both registers holding
@@ -173,13 +173,6 @@ __device__ __forceinline__ float rows4_max(float x) {
   float c = fmaxf(a, b), d = c;
   permlane16_swap(c, d);
   return fmaxf(c, d);
-}
-__device__ __forceinline__ float rows4_sum(float x) {
-  float a = x, b = x;
-  permlane32_swap(a, b);
-  float c = a + b, d = c;
-  permlane16_swap(c, d);
-  return c + d;
 }
 
 __device__ __forceinline__ bool wave_any(bool pred) {

@@ -128,7 +128,8 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  * trip and hand-off to the compute queue.  The host must not change `src`
  * until the stream has passed this call (record an event after it).
  *   dst    device, 16-byte aligned
- *   src    page-locked host, 16-byte aligned
+ *   src    page-locked host (hipHostMalloc), 16-byte aligned; anything else
+ *          (pageable or device memory) is PA_ERR_INVALID_ARG
  *   bytes  >= 0, a multiple of 4 (0 = nothing to do)
  * ------------------------------------------------------------------------- */
 int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream);

@@ -271,6 +271,13 @@ int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream_)
   if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(dst) || !aligned16(src) || bytes % 4)
     return fail(PA_ERR_INVALID_ARG, "dst/src must be 16-byte aligned and bytes a multiple of 4");
+  {  // the kernel dereferences src on the GPU: it must be page-locked host memory
+    hipPointerAttribute_t at{};
+    if (hipPointerGetAttributes(&at, src) != hipSuccess || at.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();  // clear the lookup's error for the caller's next call
+      return fail(PA_ERR_INVALID_ARG, "src is not page-locked host memory (hipHostMalloc)");
+    }
+  }
   const int rc = pa::launch_stage(dst, src, bytes, reinterpret_cast<hipStream_t>(stream_));
   return rc ? fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError())) : PA_OK;
 }

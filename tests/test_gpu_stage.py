@@ -38,3 +38,16 @@ def test_alternating_buffers_are_never_stale(device):
         pa.stage_from_host(dst, b)
         want.copy_(torch.arange(n, dtype=torch.int32, device=device) * 7 + step)
         assert torch.equal(dst, want), step
+
+
+def test_pageable_source_is_rejected(device):
+    """The kernel dereferences src on the GPU, so a pageable host buffer must
+    be refused on the host (PA_ERR_INVALID_ARG), and so must device memory."""
+    import ctypes
+    buf = (ctypes.c_int32 * 64)()                       # ordinary host memory
+    addr = ctypes.addressof(buf)
+    addr16 = addr + (-addr % 16)
+    dst = torch.empty(32, dtype=torch.int32, device=device)
+    assert pa.lib().pa_stage_from_host(dst.data_ptr(), addr16, 64, None) == -1
+    dev_src = torch.zeros(32, dtype=torch.int32, device=device)
+    assert pa.lib().pa_stage_from_host(dst.data_ptr(), dev_src.data_ptr(), 64, None) == -1

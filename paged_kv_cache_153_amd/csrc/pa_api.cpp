@@ -26,12 +26,9 @@ thread_local std::string g_last_error;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool check_mode() {
-  static const bool on = [] {
-    const char* e = std::getenv("PA_CHECK");
-    return e && e[0] == '1';
-  }();
-  return on;
+bool check_mode() {  // read on every call, so a caller can switch it at run time
+  const char* e = std::getenv("PA_CHECK");
+  return e && e[0] == '1';
 }
 
 // Schedule used when the caller passes partition_size 0 (measured on
@@ -190,6 +187,37 @@ int check_write_arrays(const int64_t* slots, int64_t num_tokens, const int32_t* 
   }
   for (int32_t b : dsts)
     if (srcs.count(b)) return fail(PA_ERR_INVALID_ARG, "PA_CHECK: a destination is also a source");
+  return PA_OK;
+}
+
+int check_prefill_arrays(const int32_t* bt, const int32_t* cl, const int32_t* qstart,
+                         int num_seqs, int total_queries, int max_query_len, int max_blocks,
+                         int block_size, int64_t num_blocks, hipStream_t stream) {
+  std::vector<int32_t> lens(num_seqs), qs(num_seqs + 1), table((size_t)num_seqs * max_blocks);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(lens.data(), cl, lens.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(qs.data(), qstart, qs.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(table.data(), bt, table.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(PA_ERR_HIP, "PA_CHECK: copying prefill arrays to the host failed");
+  if (qs[0] != 0 || qs[num_seqs] != total_queries)
+    return fail(PA_ERR_INVALID_ARG, "PA_CHECK: query_start must run from 0 to total_queries");
+  for (int s = 0; s < num_seqs; ++s) {
+    const int t = qs[s + 1] - qs[s];
+    if (t < 0 || t > max_query_len)
+      return fail(PA_ERR_INVALID_ARG, "PA_CHECK: chunk length of sequence " + std::to_string(s) +
+                                          " outside [0, max_query_len]");
+    const int n = lens[s];
+    if (n < 0 || (int64_t)n > (int64_t)max_blocks * block_size)
+      return fail(PA_ERR_INVALID_ARG, "PA_CHECK: context_lens[" + std::to_string(s) +
+                                          "] out of range");
+    const int nb = (n + block_size - 1) / block_size;
+    for (int i = 0; i < nb; ++i) {
+      const int32_t b = table[(size_t)s * max_blocks + i];
+      if (b < 0 || b >= num_blocks)
+        return fail(PA_ERR_INVALID_ARG, "PA_CHECK: block_tables[" + std::to_string(s) + "," +
+                                            std::to_string(i) + "] out of range");
+    }
+  }
   return PA_OK;
 }
 
@@ -460,6 +488,12 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
     return fail(PA_ERR_INVALID_ARG, "null device pointer");
   if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache))
     return fail(PA_ERR_INVALID_ARG, "out/query/kv_cache must be 16-byte aligned");
+  if (pa::check_mode()) {
+    if (int st = pa::check_prefill_arrays(block_tables, context_lens, query_start, num_seqs,
+                                          total_queries, max_query_len, max_blocks_per_seq,
+                                          block_size, num_blocks, stream))
+      return st;
+  }
   pa::PrefillArgs a{};
   a.out = out;
   a.q = query;

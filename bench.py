@@ -103,7 +103,7 @@ class Step:
 
     def __init__(self, name, bs, seed, steps_total, kernel, partition, device, context=0,
                  window=0, kv_dtype="f16", kv_loads="auto", prefix_cache=False,
-                 upload="kernel"):
+                 upload="fused"):
         import torch
         import paged_kv_cache_153_amd as pa
         import synth
@@ -236,10 +236,17 @@ class Step:
             h = torch.empty(self.n_i32, dtype=torch.int32).pin_memory()
             slots, pairs, lens, tables = self._views(h)
             stream = torch.cuda.current_stream(dev).cuda_stream
+            dtype_code = pa.I8 if self.int8 else pa.F32 if w["dtype"] == "f32" else pa.F16
+            fused = ((self.d_pack.data_ptr(), h.data_ptr(), self.n_i32 * 4,
+                      self.new_k.data_ptr(), self.new_v.data_ptr(), self.pool.data_ptr(),
+                      self.kv_scales.data_ptr() if self.int8 else None, slots.data_ptr(), S),
+                     pairs.data_ptr(),
+                     (nb, Hkv, D, bs, dtype_code, stream))
             self.bufs.append(dict(pack=h, slots=slots, pairs=pairs, lens=lens, tables=tables,
                                   event=torch.cuda.Event(),
                                   stage_args=(self.d_pack.data_ptr(), h.data_ptr(),
-                                              self.n_i32 * 4, stream)))
+                                              self.n_i32 * 4, stream),
+                                  fused_args=fused))
         self.k = 0
         self.kv_bytes = []       # algorithmic decode bytes per step
         self.ctx_tokens = []
@@ -289,17 +296,25 @@ class Step:
         buf["event"].synchronize()          # its previous copies have left pinned memory
         ncow = self.host_step(buf)
         maxlen = int(buf["lens"].max())
-        if self.upload == "kernel":
-            # the C call with its arguments prepared once per buffer (the
-            # binding's checks would add host time to every step)
-            rc = pa.lib().pa_stage_from_host(*buf["stage_args"])
+        # the C calls take arguments prepared once per buffer (the binding's
+        # checks would add host time to every step)
+        if self.upload == "fused":   # upload + K/V scatter in one launch
+            a = buf["fused_args"]
+            rc = pa.lib().pa_stage_and_write(*a[0], a[1] if ncow else None, ncow, *a[2])
             if rc != 0:
                 raise pa.PAError(rc, pa.lib().pa_last_error().decode())
+            buf["event"].record()
         else:
-            self.d_pack.copy_(buf["pack"], non_blocking=True)
-        buf["event"].record()
-        pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
-                       cow_pairs=self.d_pairs[:ncow] if ncow else None, kv_scales=self.kv_scales)
+            if self.upload == "kernel":
+                rc = pa.lib().pa_stage_from_host(*buf["stage_args"])
+                if rc != 0:
+                    raise pa.PAError(rc, pa.lib().pa_last_error().decode())
+            else:
+                self.d_pack.copy_(buf["pack"], non_blocking=True)
+            buf["event"].record()
+            pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
+                           cow_pairs=self.d_pairs[:ncow] if ncow else None,
+                           kv_scales=self.kv_scales)
         if timed_events is not None:
             timed_events[0].record()
         pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
@@ -576,9 +591,10 @@ def main():
     ap.add_argument("--prefix-cache", action="store_true",
                     help="shared_prefix: admit the requests through the block manager's prefix "
                          "cache (block-hash lookup) instead of sharing the prefix by hand")
-    ap.add_argument("--upload", default="kernel", choices=["kernel", "dma"],
-                    help="per-step host->device upload of tables/lengths/slots: a kernel "
-                         "reading the pinned buffer (pa_stage_from_host) or a DMA copy")
+    ap.add_argument("--upload", default="fused", choices=["fused", "kernel", "dma"],
+                    help="per-step host->device upload of tables/lengths/slots: in the same "
+                         "launch as the K/V scatter (pa_stage_and_write), a kernel of its own "
+                         "(pa_stage_from_host) or a DMA copy")
     ap.add_argument("--mode", default="decode", choices=["decode", "prefill"],
                     help="prefill: chunked-prefill attention (pa_prefill) instead of decode")
     ap.add_argument("--chunk", type=int, default=512, help="prefill: new tokens per sequence")
@@ -669,8 +685,9 @@ def main():
             "sliding_window": args.window or None,
             "kv_cache": "int8 codes + f32 row scales" if st.int8 else w["dtype"],
             "kv_loads": "cached" if st.cached_kv else "streaming (non-temporal)",
-            "upload": ("pa_stage_from_host kernel" if st.upload == "kernel"
-                       else "DMA copy (torch copy_)"),
+            "upload": {"fused": "pa_stage_and_write (upload + scatter, one launch)",
+                       "kernel": "pa_stage_from_host kernel",
+                       "dma": "DMA copy (torch copy_)"}[st.upload],
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),

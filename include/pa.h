@@ -134,6 +134,20 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache,
  * ------------------------------------------------------------------------- */
 int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream);
 
+/* The upload above and pa_cache_write in one launch (any copy-on-write pairs
+ * in a launch before it): the step's tables reach stage_dst while the new
+ * rows are scattered, saving a launch and its gap per decode step.  Same
+ * arguments, rules and results as the two calls, with one more rule:
+ * slot_mapping and cow_pairs are read by the launch that fills stage_dst, so
+ * they must point to device memory or to page-locked host memory (e.g.
+ * inside stage_src) — never into stage_dst; PA_ERR_INVALID_ARG otherwise. */
+int pa_stage_and_write(void* stage_dst, const void* stage_src, int64_t stage_bytes,
+                       const void* key, const void* value, void* kv_cache, float* kv_scales,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       const int32_t* cow_pairs, int64_t num_cow, int64_t num_blocks,
+                       int num_kv_heads, int head_dim, int block_size, int dtype,
+                       void* stream);
+
 /* -------------------------------------------------------------------------
  * 2. Decode attention ([KVPA] §2.1 formula, §4.3 block-table addressing,
  *    §7.2 online softmax; [NANO] §2.4 kernel structure; [KV2P] §5.3 GQA)

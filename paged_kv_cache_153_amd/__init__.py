@@ -62,6 +62,9 @@ _SIGNATURES = {
                               _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
                               _c.c_int, _c.c_int, _P]),
     "pa_stage_from_host": (_c.c_int, [_P, _P, _c.c_int64, _P]),
+    "pa_stage_and_write": (_c.c_int, [_P, _P, _c.c_int64, _P, _P, _P, _P, _P, _c.c_int64, _P,
+                                      _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_int,
+                                      _c.c_int, _P]),
     "pa_bm_create": (_P, [_c.c_int64, _c.c_int]),
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_allocate": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
@@ -188,7 +191,7 @@ def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None,
     scatter ``key``/``value`` [T, Hkv, D] into ``kv_cache`` [NB, 2, Hkv, bs, D]
     at ``slot_mapping`` [T] int64 (negative = skip).  Enqueued on ``stream``.
     An int8 ``kv_cache`` takes float16 key/value rows, quantised per row into
-    codes plus ``kv_scales`` [NB, 2, Hkv, bs] float32."""
+    codes plus ``kv_scales`` [NB, Hkv, 2, bs] float32."""
     torch = _torch()
     _need_cuda(key, value, kv_cache, slot_mapping, cow_pairs)
     nb, two, hkv, bs, d = kv_cache.shape
@@ -209,6 +212,46 @@ def cache_write(key, value, kv_cache, slot_mapping, cow_pairs=None, stream=None,
                                 slot_mapping.data_ptr(), key.shape[0],
                                 cow_pairs.data_ptr() if ncow else None, ncow, nb, hkv, d, bs,
                                 _dtype_code(kv_cache), _stream(kv_cache.device, stream)))
+
+
+def stage_and_write(stage_dst, stage_src, key, value, kv_cache, slot_mapping, cow_pairs=None,
+                    stream=None, kv_scales=None):
+    """``stage_from_host(stage_dst, stage_src)`` and ``cache_write(...)`` in one
+    launch.  ``slot_mapping`` [T] int64 and ``cow_pairs`` [k, 2] int32 may be
+    device tensors or pinned host tensors (for instance views into
+    ``stage_src``), but not views into ``stage_dst``."""
+    torch = _torch()
+    _need_cuda(key, value, kv_cache, stage_dst)
+    if not stage_src.is_pinned() or stage_src.is_cuda:
+        raise TypeError("stage_src must be a pinned host tensor")
+    if not stage_dst.is_contiguous() or not stage_src.is_contiguous():
+        raise TypeError("stage_dst and stage_src must be contiguous")
+    nbytes = stage_src.numel() * stage_src.element_size()
+    if stage_dst.numel() * stage_dst.element_size() != nbytes:
+        raise ValueError("stage_dst and stage_src sizes differ")
+    for t in (slot_mapping, cow_pairs):
+        if t is not None and not (t.is_cuda or t.is_pinned()):
+            raise TypeError("slot_mapping / cow_pairs must be device or pinned host tensors")
+    nb, two, hkv, bs, d = kv_cache.shape
+    if two != 2 or key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
+        raise ValueError("shape mismatch between key/value and kv_cache")
+    in_dtype = torch.float16 if kv_cache.dtype == torch.int8 else kv_cache.dtype
+    if key.dtype != in_dtype or value.dtype != in_dtype:
+        raise TypeError("key and value must have the pool's dtype (float16 for an int8 pool)")
+    sp = _scales_ptr(kv_cache, kv_scales)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise TypeError("slot_mapping must be int64 [T]")
+    ncow = 0
+    if cow_pairs is not None:
+        if cow_pairs.dtype != torch.int32 or cow_pairs.dim() != 2 or cow_pairs.shape[1] != 2:
+            raise TypeError("cow_pairs must be int32 [k, 2]")
+        ncow = cow_pairs.shape[0]
+    _check(lib().pa_stage_and_write(stage_dst.data_ptr(), stage_src.data_ptr(), nbytes,
+                                    key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(), sp,
+                                    slot_mapping.data_ptr(), key.shape[0],
+                                    cow_pairs.data_ptr() if ncow else None, ncow, nb, hkv, d, bs,
+                                    _dtype_code(kv_cache), _stream(kv_cache.device, stream)))
+    return stage_dst
 
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

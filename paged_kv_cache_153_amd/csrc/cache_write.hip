@@ -28,20 +28,20 @@
 namespace pa {
 namespace {
 
-// grid-stride over num_tokens * Hkv * CPR chunks (CPR = 16-byte chunks per row)
-__global__ __launch_bounds__(256) void cache_write_kernel(const u32x4_t* __restrict__ key,
-                                                          const u32x4_t* __restrict__ value,
-                                                          u32x4_t* __restrict__ kv,
-                                                          const int64_t* __restrict__ slots,
-                                                          int64_t num_tokens, int num_kv_heads,
-                                                          int cpr, int block_size,
-                                                          int64_t num_blocks) {
+// Thread `first`, then every `stride`-th, over num_tokens * Hkv * CPR chunks
+// (CPR = 16-byte chunks per row).
+__device__ __forceinline__ void scatter_chunks(const u32x4_t* __restrict__ key,
+                                               const u32x4_t* __restrict__ value,
+                                               u32x4_t* __restrict__ kv,
+                                               const int64_t* __restrict__ slots,
+                                               int64_t num_tokens, int num_kv_heads, int cpr,
+                                               int block_size, int64_t num_blocks,
+                                               int64_t first, int64_t stride) {
   const int64_t per_token = (int64_t)num_kv_heads * cpr;
   const int64_t total = num_tokens * per_token;
   const int64_t head_chunks = (int64_t)block_size * cpr;
   const int64_t v_off = (int64_t)num_kv_heads * head_chunks;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t idx = first; idx < total; idx += stride) {
     const int64_t i = idx / per_token;
     const int64_t rem = idx - i * per_token;  // h * cpr + chunk
     const int64_t slot = slots[i];
@@ -54,6 +54,18 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const u32x4_t* __restr
     kv[dst] = key[idx];
     kv[dst + v_off] = value[idx];
   }
+}
+
+__global__ __launch_bounds__(256) void cache_write_kernel(const u32x4_t* __restrict__ key,
+                                                          const u32x4_t* __restrict__ value,
+                                                          u32x4_t* __restrict__ kv,
+                                                          const int64_t* __restrict__ slots,
+                                                          int64_t num_tokens, int num_kv_heads,
+                                                          int cpr, int block_size,
+                                                          int64_t num_blocks) {
+  scatter_chunks(key, value, kv, slots, num_tokens, num_kv_heads, cpr, block_size, num_blocks,
+                 (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                 (int64_t)gridDim.x * blockDim.x);
 }
 
 // blockIdx.y = pair index; grid-stride over the block's chunks in x
@@ -75,17 +87,15 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4_t* __restrict__ 
 // Grid-stride over num_tokens * Hkv * 2 * TPR threads; TPR divides the
 // stride, so a row's threads always run the same iteration together.
 template <int TPR>
-__global__ __launch_bounds__(256) void cache_write_i8_kernel(const u32x4_t* __restrict__ key,
-                                                             const u32x4_t* __restrict__ value,
-                                                             u32x2_t* __restrict__ codes,
-                                                             float* __restrict__ scales,
-                                                             const int64_t* __restrict__ slots,
-                                                             int64_t num_tokens,
-                                                             int num_kv_heads, int block_size,
-                                                             int64_t num_blocks) {
+__device__ __forceinline__ void scatter_i8(const u32x4_t* __restrict__ key,
+                                           const u32x4_t* __restrict__ value,
+                                           u32x2_t* __restrict__ codes,
+                                           float* __restrict__ scales,
+                                           const int64_t* __restrict__ slots, int64_t num_tokens,
+                                           int num_kv_heads, int block_size, int64_t num_blocks,
+                                           int64_t first, int64_t stride) {
   const int64_t total = num_tokens * num_kv_heads * 2 * TPR;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t idx = first; idx < total; idx += stride) {
     const int c = (int)(idx % TPR);
     const int64_t row = idx / TPR;  // (i * Hkv + h) * 2 + kv
     const int kv = (int)(row & 1);
@@ -123,6 +133,20 @@ __global__ __launch_bounds__(256) void cache_write_i8_kernel(const u32x4_t* __re
   }
 }
 
+template <int TPR>
+__global__ __launch_bounds__(256) void cache_write_i8_kernel(const u32x4_t* __restrict__ key,
+                                                             const u32x4_t* __restrict__ value,
+                                                             u32x2_t* __restrict__ codes,
+                                                             float* __restrict__ scales,
+                                                             const int64_t* __restrict__ slots,
+                                                             int64_t num_tokens,
+                                                             int num_kv_heads, int block_size,
+                                                             int64_t num_blocks) {
+  scatter_i8<TPR>(key, value, codes, scales, slots, num_tokens, num_kv_heads, block_size,
+                  num_blocks, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                  (int64_t)gridDim.x * blockDim.x);
+}
+
 void copy_blocks(void* buf, const int32_t* cow_pairs, int64_t num_cow, int64_t block_chunks,
                  int64_t num_blocks, hipStream_t stream, int* rc) {
   const int64_t per_pair = (block_chunks + 255) / 256;
@@ -140,15 +164,45 @@ void copy_blocks(void* buf, const int32_t* cow_pairs, int64_t num_cow, int64_t b
 // it over the bus (16-byte loads, then a 4-byte tail): the per-step tables
 // reach the GPU without a copy-engine transfer and its hand-off to the
 // compute queue.
+__device__ __forceinline__ void stage_chunks(u32x4_t* __restrict__ dst,
+                                             const u32x4_t* __restrict__ src, int64_t n16,
+                                             int tail, int64_t first, int64_t stride,
+                                             bool tail_block) {
+  for (int64_t i = first; i < n16; i += stride) dst[i] = src[i];
+  if (tail_block && (int)threadIdx.x < tail)
+    reinterpret_cast<uint32_t*>(dst + n16)[threadIdx.x] =
+        reinterpret_cast<const uint32_t*>(src + n16)[threadIdx.x];
+}
+
 __global__ __launch_bounds__(256) void stage_kernel(u32x4_t* __restrict__ dst,
                                                     const u32x4_t* __restrict__ src, int64_t n16,
-                                                    uint32_t* __restrict__ dst_tail,
-                                                    const uint32_t* __restrict__ src_tail,
                                                     int tail) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
-  if (blockIdx.x == 0 && (int)threadIdx.x < tail) dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+  stage_chunks(dst, src, n16, tail, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+               (int64_t)gridDim.x * blockDim.x, blockIdx.x == 0);
+}
+
+// The upload and the K/V scatter in one launch: workgroups [0, stage_wgs)
+// upload, the rest scatter (TPR = 0: byte copies of 16-byte chunks; 8 / 16:
+// INT8 quantisation).  The two parts touch disjoint memory.
+template <int TPR>
+__global__ __launch_bounds__(256) void stage_write_kernel(
+    u32x4_t* __restrict__ stage_dst, const u32x4_t* __restrict__ stage_src, int64_t n16,
+    int tail, int stage_wgs, const u32x4_t* __restrict__ key, const u32x4_t* __restrict__ value,
+    void* __restrict__ kv, float* __restrict__ scales, const int64_t* __restrict__ slots,
+    int64_t num_tokens, int num_kv_heads, int cpr, int block_size, int64_t num_blocks) {
+  if ((int)blockIdx.x < stage_wgs) {
+    stage_chunks(stage_dst, stage_src, n16, tail, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                 (int64_t)stage_wgs * blockDim.x, blockIdx.x == 0);
+    return;
+  }
+  const int64_t first = (int64_t)(blockIdx.x - stage_wgs) * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)(gridDim.x - stage_wgs) * blockDim.x;
+  if constexpr (TPR == 0)
+    scatter_chunks(key, value, reinterpret_cast<u32x4_t*>(kv), slots, num_tokens, num_kv_heads,
+                   cpr, block_size, num_blocks, first, stride);
+  else
+    scatter_i8<TPR>(key, value, reinterpret_cast<u32x2_t*>(kv), scales, slots, num_tokens,
+                    num_kv_heads, block_size, num_blocks, first, stride);
 }
 
 }  // namespace
@@ -161,8 +215,53 @@ int launch_stage(void* dst, const void* src, int64_t bytes, hipStream_t stream) 
   if (blocks > 256) blocks = 256;
   hipLaunchKernelGGL(stage_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<u32x4_t*>(dst), reinterpret_cast<const u32x4_t*>(src), n16,
-                     reinterpret_cast<uint32_t*>(dst) + 4 * n16,
-                     reinterpret_cast<const uint32_t*>(src) + 4 * n16, tail);
+                     tail);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int launch_stage_write(void* stage_dst, const void* stage_src, int64_t stage_bytes,
+                       const void* key, const void* value, void* kv, float* scales,
+                       const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,
+                       int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                       int block_size, int elem_bytes, hipStream_t stream) {
+  int rc = 0;
+  if (num_cow > 0) {  // copies go first, in a launch of their own
+    copy_blocks(kv, cow_pairs, num_cow, 2LL * num_kv_heads * block_size * head_dim * elem_bytes / 16,
+                num_blocks, stream, &rc);
+    if (elem_bytes == 1)
+      copy_blocks(scales, cow_pairs, num_cow, 2LL * num_kv_heads * block_size * 4 / 16,
+                  num_blocks, stream, &rc);
+    if (rc) return rc;
+  }
+  const int64_t n16 = stage_bytes / 16;
+  const int tail = (int)((stage_bytes % 16) / 4);
+  int64_t sw = (n16 + 255) / 256;
+  sw = sw < 1 ? 1 : (sw > 64 ? 64 : sw);
+  const int tpr = elem_bytes == 1 ? head_dim / 8 : 0;
+  const int cpr = head_dim * elem_bytes / 16;
+  const int64_t total = elem_bytes == 1 ? num_tokens * num_kv_heads * 2 * tpr
+                                        : num_tokens * num_kv_heads * cpr;
+  int64_t ww = (total + 255) / 256;
+  ww = ww < 1 ? 1 : (ww > 65536 ? 65536 : ww);
+  const dim3 grid((unsigned)(sw + ww));
+  auto* sd = reinterpret_cast<u32x4_t*>(stage_dst);
+  const auto* ss = reinterpret_cast<const u32x4_t*>(stage_src);
+  const auto* k = reinterpret_cast<const u32x4_t*>(key);
+  const auto* v = reinterpret_cast<const u32x4_t*>(value);
+  if (tpr == 16)
+    hipLaunchKernelGGL(stage_write_kernel<16>, grid, dim3(256), 0, stream, sd, ss, n16, tail,
+                       (int)sw, k, v, kv, scales, slots, num_tokens, num_kv_heads, cpr,
+                       block_size, num_blocks);
+  else if (tpr == 8)
+    hipLaunchKernelGGL(stage_write_kernel<8>, grid, dim3(256), 0, stream, sd, ss, n16, tail,
+                       (int)sw, k, v, kv, scales, slots, num_tokens, num_kv_heads, cpr,
+                       block_size, num_blocks);
+  else if (tpr == 0)
+    hipLaunchKernelGGL(stage_write_kernel<0>, grid, dim3(256), 0, stream, sd, ss, n16, tail,
+                       (int)sw, k, v, kv, scales, slots, num_tokens, num_kv_heads, cpr,
+                       block_size, num_blocks);
+  else
+    return 1;
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

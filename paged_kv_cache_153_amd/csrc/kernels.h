@@ -89,6 +89,11 @@ int decode_mfma_i8_occupancy(const DecodeArgs& a, int head_dim, int block_size, 
 // elem_bytes 4 / 2: byte copies; 1: INT8 pool, f16 inputs quantised per
 // row with their scales written to `scales` ([NB, Hkv, 2, BS] floats).
 int launch_stage(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+int launch_stage_write(void* stage_dst, const void* stage_src, int64_t stage_bytes,
+                       const void* key, const void* value, void* kv, float* scales,
+                       const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,
+                       int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                       int block_size, int elem_bytes, hipStream_t stream);
 int launch_cache_write(const void* key, const void* value, void* kv, float* scales,
                        const int64_t* slots, int64_t num_tokens, const int32_t* cow_pairs,
                        int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,

@@ -168,8 +168,8 @@ int check_write_arrays(const int64_t* slots, int64_t num_tokens, const int32_t* 
   std::vector<int64_t> sl(num_tokens);
   std::vector<int32_t> pr(2 * num_cow);
   if (hipStreamSynchronize(stream) != hipSuccess ||
-      (num_tokens && hipMemcpy(sl.data(), slots, sl.size() * 8, hipMemcpyDeviceToHost)) ||
-      (num_cow && hipMemcpy(pr.data(), pairs, pr.size() * 4, hipMemcpyDeviceToHost)))
+      (num_tokens && hipMemcpy(sl.data(), slots, sl.size() * 8, hipMemcpyDefault)) ||
+      (num_cow && hipMemcpy(pr.data(), pairs, pr.size() * 4, hipMemcpyDefault)))
     return fail(PA_ERR_HIP, "PA_CHECK: copying slots to the host failed");
   std::unordered_set<int64_t> seen;
   for (int64_t s : sl) {
@@ -253,19 +253,20 @@ const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
 
 const char* pa_version(void) { return "pa 0.1 gfx950"; }
 
-int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv_scales,
+namespace {
+// Host-side checks shared by pa_cache_write and pa_stage_and_write; on
+// success *eb is the element size.
+int validate_write(const void* key, const void* value, void* kv_cache, float* kv_scales,
                    const int64_t* slot_mapping, int64_t num_tokens, const int32_t* cow_pairs,
                    int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
-                   int block_size, int dtype, void* stream_) {
-  pa::clear_error();
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+                   int block_size, int dtype, int* eb) {
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_I8)
     return fail(PA_ERR_UNSUPPORTED, "dtype");
-  const int eb = dtype == PA_F32 ? 4 : dtype == PA_F16 ? 2 : 1;
+  *eb = dtype == PA_F32 ? 4 : dtype == PA_F16 ? 2 : 1;
   if (num_tokens < 0 || num_cow < 0) return fail(PA_ERR_INVALID_ARG, "negative count");
   if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
-  if ((head_dim * eb) % 16) return fail(PA_ERR_UNSUPPORTED, "head_dim * element size % 16 != 0");
+  if ((head_dim * *eb) % 16) return fail(PA_ERR_UNSUPPORTED, "head_dim * element size % 16 != 0");
   if (dtype == PA_I8) {
     if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "INT8 head_dim");
     if ((2LL * num_kv_heads * block_size * 4) % 16)
@@ -279,6 +280,32 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv
   if (num_tokens > 0 && (!key || !value || !slot_mapping || !aligned16(key) || !aligned16(value)))
     return fail(PA_ERR_INVALID_ARG, "key/value/slot_mapping null or unaligned");
   if (num_cow > 0 && !cow_pairs) return fail(PA_ERR_INVALID_ARG, "cow_pairs null");
+  return PA_OK;
+}
+
+// The memory type of `p` as the GPU sees it: device, page-locked host, or
+// neither (pageable host memory, a bad pointer).
+hipMemoryType gpu_memory_type(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the lookup's error for the caller's next call
+    return hipMemoryTypeUnregistered;
+  }
+  return at.type;
+}
+}  // namespace
+
+int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv_scales,
+                   const int64_t* slot_mapping, int64_t num_tokens, const int32_t* cow_pairs,
+                   int64_t num_cow, int64_t num_blocks, int num_kv_heads, int head_dim,
+                   int block_size, int dtype, void* stream_) {
+  pa::clear_error();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int eb = 0;
+  if (int st = validate_write(key, value, kv_cache, kv_scales, slot_mapping, num_tokens,
+                              cow_pairs, num_cow, num_blocks, num_kv_heads, head_dim,
+                              block_size, dtype, &eb))
+    return st;
   if (num_tokens == 0 && num_cow == 0) return PA_OK;
   if (pa::check_mode()) {
     if (int st = pa::check_write_arrays(slot_mapping, num_tokens, cow_pairs, num_cow, num_blocks,
@@ -292,6 +319,56 @@ int pa_cache_write(const void* key, const void* value, void* kv_cache, float* kv
   return rc ? fail(PA_ERR_UNSUPPORTED, "cache write") : PA_OK;
 }
 
+int pa_stage_and_write(void* stage_dst, const void* stage_src, int64_t stage_bytes,
+                       const void* key, const void* value, void* kv_cache, float* kv_scales,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       const int32_t* cow_pairs, int64_t num_cow, int64_t num_blocks,
+                       int num_kv_heads, int head_dim, int block_size, int dtype,
+                       void* stream_) {
+  pa::clear_error();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int eb = 0;
+  if (int st = validate_write(key, value, kv_cache, kv_scales, slot_mapping, num_tokens,
+                              cow_pairs, num_cow, num_blocks, num_kv_heads, head_dim,
+                              block_size, dtype, &eb))
+    return st;
+  if (stage_bytes < 0 || stage_bytes % 4) return fail(PA_ERR_INVALID_ARG, "stage_bytes");
+  if (stage_bytes > 0 && (!stage_dst || !stage_src || !aligned16(stage_dst) ||
+                          !aligned16(stage_src)))
+    return fail(PA_ERR_INVALID_ARG, "stage_dst/stage_src null or not 16-byte aligned");
+  if (stage_bytes > 0 && gpu_memory_type(stage_src) != hipMemoryTypeHost)
+    return fail(PA_ERR_INVALID_ARG, "stage_src is not page-locked host memory (hipHostMalloc)");
+  // slots and pairs are read by the same launch that fills stage_dst: they
+  // must come from elsewhere (device memory or page-locked host memory)
+  auto inside_dst = [&](const void* p) {
+    const char* c = static_cast<const char*>(p);
+    const char* d = static_cast<const char*>(stage_dst);
+    return stage_bytes > 0 && c >= d && c < d + stage_bytes;
+  };
+  auto gpu_readable = [&](const void* p) {
+    const hipMemoryType t = gpu_memory_type(p);
+    return t == hipMemoryTypeHost || t == hipMemoryTypeDevice;
+  };
+  if (num_tokens > 0 && (inside_dst(slot_mapping) || !gpu_readable(slot_mapping)))
+    return fail(PA_ERR_INVALID_ARG,
+                "slot_mapping must be device or page-locked host memory outside stage_dst");
+  if (num_cow > 0 && (inside_dst(cow_pairs) || !gpu_readable(cow_pairs)))
+    return fail(PA_ERR_INVALID_ARG,
+                "cow_pairs must be device or page-locked host memory outside stage_dst");
+  if (num_tokens == 0 && num_cow == 0 && stage_bytes == 0) return PA_OK;
+  if (pa::check_mode()) {
+    if (int st = pa::check_write_arrays(slot_mapping, num_tokens, cow_pairs, num_cow, num_blocks,
+                                        block_size, stream))
+      return st;
+  }
+  const int rc = pa::launch_stage_write(stage_dst, stage_src, stage_bytes, key, value, kv_cache,
+                                        kv_scales, slot_mapping, num_tokens, cow_pairs, num_cow,
+                                        num_blocks, num_kv_heads, head_dim, block_size, eb,
+                                        stream);
+  if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
+  return rc ? fail(PA_ERR_UNSUPPORTED, "cache write") : PA_OK;
+}
+
 int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream_) {
   pa::clear_error();
   if (bytes < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
@@ -299,13 +376,9 @@ int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream_)
   if (!dst || !src) return fail(PA_ERR_INVALID_ARG, "null pointer");
   if (!aligned16(dst) || !aligned16(src) || bytes % 4)
     return fail(PA_ERR_INVALID_ARG, "dst/src must be 16-byte aligned and bytes a multiple of 4");
-  {  // the kernel dereferences src on the GPU: it must be page-locked host memory
-    hipPointerAttribute_t at{};
-    if (hipPointerGetAttributes(&at, src) != hipSuccess || at.type != hipMemoryTypeHost) {
-      (void)hipGetLastError();  // clear the lookup's error for the caller's next call
-      return fail(PA_ERR_INVALID_ARG, "src is not page-locked host memory (hipHostMalloc)");
-    }
-  }
+  // the kernel dereferences src on the GPU: it must be page-locked host memory
+  if (gpu_memory_type(src) != hipMemoryTypeHost)
+    return fail(PA_ERR_INVALID_ARG, "src is not page-locked host memory (hipHostMalloc)");
   const int rc = pa::launch_stage(dst, src, bytes, reinterpret_cast<hipStream_t>(stream_));
   return rc ? fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError())) : PA_OK;
 }

@@ -51,3 +51,52 @@ def test_pageable_source_is_rejected(device):
     assert pa.lib().pa_stage_from_host(dst.data_ptr(), addr16, 64, None) == -1
     dev_src = torch.zeros(32, dtype=torch.int32, device=device)
     assert pa.lib().pa_stage_from_host(dst.data_ptr(), dev_src.data_ptr(), 64, None) == -1
+
+
+def _step_inputs(device, dtype, seed):
+    """A pool, new rows and a pinned pack whose slots/pairs sections the fused
+    call reads from host memory."""
+    import synth
+    x = synth.make_decode_inputs([40, 17, 100], 8, 2, 128, 16, dtype="f16", seed=seed,
+                                 num_blocks=24)
+    if dtype == "i8":
+        x = synth.int8_pool(x, seed=seed + 1)
+    k, v = synth.rows(3, 2, 128, dtype="f16", seed=seed + 2)
+    pack = torch.zeros(64 + 6 * 5, dtype=torch.int32).pin_memory()
+    slots = pack[0:6].view(torch.int64)                  # 3 int64 slots
+    pairs = pack[6:10].view(2, 2)
+    slots.copy_(torch.tensor([5 * 16 + 3, 9 * 16 + 15, 2 * 16]))
+    pairs.copy_(torch.tensor([[1, 20], [4, 21]], dtype=torch.int32))   # into spare blocks
+    pack[10:].copy_(torch.arange(pack.numel() - 10, dtype=torch.int32) * 3 + seed)
+    return x, k.to(device), v.to(device), pack, slots, pairs
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("with_cow", [False, True])
+def test_stage_and_write_equals_the_two_calls(device, dtype, with_cow):
+    """One fused launch leaves exactly what pa_stage_from_host followed by
+    pa_cache_write leaves: the staged bytes, the pool (and INT8 scales)."""
+    x, k, v, pack, slots, pairs = _step_inputs(device, dtype, seed=11 if with_cow else 12)
+    cow = pairs if with_cow else None
+    g1, g2 = x.to(device), x.to(device)
+    d1 = torch.full((pack.numel(),), -7, dtype=torch.int32, device=device)
+    d2 = d1.clone()
+    pa.stage_from_host(d1, pack)
+    pa.cache_write(k, v, g1.kv_cache, slots.to(device),
+                   cow_pairs=cow.to(device) if with_cow else None, kv_scales=g1.kv_scales)
+    pa.stage_and_write(d2, pack, k, v, g2.kv_cache, slots, cow_pairs=cow, kv_scales=g2.kv_scales)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(d2.cpu(), pack)
+    assert torch.equal(g1.kv_cache, g2.kv_cache)
+    if dtype == "i8":
+        assert torch.equal(g1.kv_scales.view(torch.int32), g2.kv_scales.view(torch.int32))
+
+
+def test_stage_and_write_refuses_slots_inside_the_destination(device):
+    x, k, v, pack, slots, pairs = _step_inputs(device, "f16", seed=13)
+    g = x.to(device)
+    dst = torch.zeros(pack.numel(), dtype=torch.int32, device=device)
+    inside = dst[0:6].view(torch.int64)                  # would be read while being written
+    with pytest.raises(pa.PAError) as e:
+        pa.stage_and_write(dst, pack, k, v, g.kv_cache, inside)
+    assert e.value.status == -1

@@ -25,7 +25,8 @@
 //    first, so weights down to ~2e-9 of the running max stay normal fp16.
 //    The sum l uses the same scaled weights, so the scale cancels in O / l.
 //  * The running max per head needs one max across the four lane groups
-//    (two butterfly steps); everything else stays in the lane.
+//    (two permlane swaps, no LDS traffic); everything else stays in the
+//    lane.
 #include "device_common.h"
 #include "decode_epilogue.h"
 #include "decode_schedule.h"
@@ -53,6 +54,149 @@ struct VRow<64> {
   static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
 };
 
+// One 16-token tile in registers: K as the A operand of q.K (lane (quad,
+// col): row col, 16-byte chunks 4j + quad) and four V rows (lane (quad, col):
+// row 4*quad + i, chunk col).
+template <int D>
+struct MfmaTile {
+  u32x4_t k[D / 32];
+  typename VRow<D>::type v[4];
+};
+
+// Issues the loads of one tile.  kb0 / kb1 point at the K rows of the
+// (block, KV head) that hold the tile's first / last eight tokens (the same
+// block unless BS == 8); the V rows sit v_offset elements further; row0 is
+// the tile's first row in its block (BS == 32: 0 or 16).
+template <int D, int BS, bool NT>
+__device__ __forceinline__ void load_tile(const half_t* kb0, const half_t* kb1, size_t v_offset,
+                                          int row0, int quad, int col, MfmaTile<D>& t) {
+  constexpr int KS = D / 32;
+  constexpr int VH = D / 16;
+  if constexpr (BS >= kTile) {
+    const half_t* vb = kb0 + v_offset;
+    const uint32_t krow = (uint32_t)(row0 + col) * (D * 2);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) t.k[j] = kv_load16<NT>(kb0, krow + (4 * j + quad) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)(row0 + 4 * quad + i) * (D * 2) + col * (VH * 2);
+      if constexpr (D == 128)
+        t.v[i] = kv_load16<NT>(vb, off);
+      else
+        t.v[i] = kv_load8<NT>(vb, off);
+    }
+  } else {
+    // a tile spans two 8-row blocks: lanes pick their block
+    const half_t* kb = col >= BS ? kb1 : kb0;
+    const uint32_t krow = (uint32_t)(col % BS) * (D * 2);
+#pragma unroll
+    for (int j = 0; j < KS; ++j) t.k[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * quad + i;
+      const half_t* vb = (r >= BS ? kb1 : kb0) + v_offset;
+      const uint32_t off = (uint32_t)(r % BS) * (D * 2) + col * (VH * 2);
+      if constexpr (D == 128)
+        t.v[i] = kv_load16<NT>(vb, off);
+      else
+        t.v[i] = kv_load8<NT>(vb, off);
+    }
+  }
+}
+
+// Online-softmax state of one wave: running max m of head `col` (the same in
+// all four quads), this lane's share l of the (2^15-scaled) weight sum, and
+// O^T blocks acc[e] (lane (quad, col): d = VH*(4*quad + i) + e of head col).
+template <int D>
+struct MfmaState {
+  float m;
+  float l;
+  float4_t acc[D / 16];
+  __device__ __forceinline__ void reset() {
+    m = kMaxInit;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 16; ++e) acc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// q of the G heads of (s, g) as the B operand of q.K: lane (quad, col) =
+// head col, chunk 4j + quad.  The padding columns col >= G load head col % G
+// (every lane loads, so the load count never depends on the lane): their
+// scores are finite and get weight zero, so they reach no output.
+template <int D, int G>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int g, int quad, int col,
+                                       half8_t (&qb)[D / 32]) {
+  const half_t* qh = reinterpret_cast<const half_t*>(a.q) +
+                     ((size_t)s * a.num_q_heads + g * G + col % G) * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    qb[j] = __builtin_bit_cast(half8_t, load16(qh + (4 * j + quad) * 8));
+}
+
+// Scores, online-softmax update and P.V of one tile (absolute tile index
+// `tile` of a sequence whose keys are tokens [lo, n)).
+template <int D, int G>
+__device__ __forceinline__ void compute_tile(MfmaState<D>& st, const half8_t (&qb)[D / 32],
+                                             MfmaTile<D>& t, int tile, int lo, int n, float cs,
+                                             int quad, int col) {
+  constexpr int KS = D / 32;
+  constexpr int NE = D / 16;
+  float4_t sc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KS; ++j)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, t.k[j]), qb[j], sc, 0,
+                                                 0, 0);
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = sc[i] * cs;
+  if ((tile + 1) * kTile > n || tile * kTile < lo) {  // partial tile: non-keys
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tile * kTile + 4 * quad + i;
+      if (tok >= n || tok < lo) {
+        y[i] = -INFINITY;
+        t.v[i] = VRow<D>::zero();
+      }
+    }
+  }
+  const float ym = rows4_max(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
+  const float m_new = fmaxf(st.m, ym);
+  const float alpha = fast_exp2(st.m - m_new);
+  // exp2 first, then an exact power-of-two scale: the max token weighs
+  // exactly 2^15, so a lone token reproduces its V row bit for bit
+  float pw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pw[i] = col < G ? fast_exp2(y[i] - m_new) * kPScale : 0.f;
+  st.l = fmaf(st.l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
+  // fp16 hi + lo split of the weights (B operand of P.V)
+  const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
+  const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
+  const auto l01 = __builtin_amdgcn_cvt_pkrtz(pw[0] - (float)h01[0], pw[1] - (float)h01[1]);
+  const auto l23 = __builtin_amdgcn_cvt_pkrtz(pw[2] - (float)h23[0], pw[3] - (float)h23[1]);
+  const half4_t phi = __builtin_bit_cast(
+      half4_t, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
+  const half4_t plo = __builtin_bit_cast(
+      half4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
+  // rescale only when some head's running max moved (alpha == 1 otherwise)
+  if (wave_any(alpha != 1.f)) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) st.acc[e] *= alpha;
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    // A operand: tokens 4*quad .. 4*quad+3 of dim (chunk col, half e)
+    const int wd = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t d0 = __builtin_amdgcn_perm(t.v[1][wd], t.v[0][wd], sel);
+    const uint32_t d1 = __builtin_amdgcn_perm(t.v[3][wd], t.v[2][wd], sel);
+    const half4_t av = __builtin_bit_cast(half4_t, u32x2_t{d0, d1});
+    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, st.acc[e], 0, 0, 0);
+    st.acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, st.acc[e], 0, 0, 0);
+  }
+  st.m = m_new;
+}
+
 // DEPTH 2: the next tile's loads are issued before the current tile is
 // computed (register double buffer, 2 waves per SIMD).  DEPTH 1: one tile
 // per wave in flight and twice the waves per SIMD to hide the latency.
@@ -62,31 +206,18 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
                                              int tile_end, const Sink& sink) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G >= 1 && G <= 16, "group");
-  constexpr int KS = D / 32;                 // 16x16x32 steps for q.K
   constexpr int VH = D / 16;                 // halves of one V row per lane
   constexpr int NE = VH;                     // P.V blocks of 16 output rows
   constexpr int BPT = BS >= kTile ? 1 : kTile / BS;
   static_assert(BPT <= 2, "a tile spans at most two blocks");
-  using vrow_t = typename VRow<D>::type;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int quad = lane >> 4;
   const int col = lane & 15;
-  const int Hq = a.num_q_heads;
 
-  // ---- q as the B operand of q.K: lane (quad, col) = head col, chunk 4j+quad
-  half8_t qb[KS];
-  {
-    const half_t* qh = reinterpret_cast<const half_t*>(a.q) + ((size_t)s * Hq + g * G) * D;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (col < G)
-        qb[j] = __builtin_bit_cast(half8_t, load16(qh + col * D + (4 * j + quad) * 8));
-      else
-        qb[j] = __builtin_bit_cast(half8_t, u32x4_t{0u, 0u, 0u, 0u});
-    }
-  }
+  half8_t qb[D / 32];
+  load_q<D, G>(a, s, g, quad, col, qb);
 
   const size_t head_stride = (size_t)BS * D;
   const size_t block_stride = 2 * (size_t)a.num_kv_heads * head_stride;
@@ -111,114 +242,18 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
     }
   };
 
-  float m = kMaxInit;  // running max of head `col` (same in all four quads)
-  float l = 0.f;       // this lane's share of the (2^15-scaled) weight sum
-  float4_t acc[NE];
-#pragma unroll
-  for (int e = 0; e < NE; ++e) acc[e] = float4_t{0.f, 0.f, 0.f, 0.f};
+  MfmaState<D> st;
+  st.reset();
   const float cs = a.scale_log2;
+  MfmaTile<D> tA, tB;
 
-  u32x4_t kA[KS], kB[KS];
-  vrow_t vA[4], vB[4];
-
-  auto issue = [&](int tile, int k_it, u32x4_t (&kr)[KS], vrow_t (&vr)[4]) {
+  auto issue = [&](int tile, int k_it, MfmaTile<D>& t) {
     const int sel = k_it & 63;
-    int blk[BPT];
-#pragma unroll
-    for (int jj = 0; jj < BPT; ++jj) blk[jj] = readlane(ids[jj], sel);
+    const int b0 = readlane(ids[0], sel);
+    const int b1 = readlane(ids[BPT - 1], sel);
     const int row0 = BS > kTile ? (tile % (BS / kTile)) * kTile : 0;
-    if constexpr (BPT == 1) {
-      // one block: wave-uniform base, per-lane unsigned offsets
-      const half_t* kb = kvh + (size_t)blk[0] * block_stride;
-      const half_t* vb = kb + v_offset;
-      const uint32_t krow = (uint32_t)(row0 + col) * (D * 2);
-#pragma unroll
-      for (int j = 0; j < KS; ++j) kr[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t off = (uint32_t)(row0 + 4 * quad + i) * (D * 2) + col * (VH * 2);
-        if constexpr (D == 128)
-          vr[i] = kv_load16<NT>(vb, off);
-        else
-          vr[i] = kv_load8<NT>(vb, off);
-      }
-    } else {
-      // a tile spans two 8-row blocks: lanes pick their block
-      const int bk = col >= BS ? blk[BPT - 1] : blk[0];
-      const half_t* kb = kvh + (size_t)bk * block_stride;
-      const uint32_t krow = (uint32_t)(col % BS) * (D * 2);
-#pragma unroll
-      for (int j = 0; j < KS; ++j) kr[j] = kv_load16<NT>(kb, krow + (4 * j + quad) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * quad + i;
-        const half_t* vb = kvh + (size_t)(t >= BS ? blk[BPT - 1] : blk[0]) * block_stride +
-                           v_offset;
-        const uint32_t off = (uint32_t)(t % BS) * (D * 2) + col * (VH * 2);
-        if constexpr (D == 128)
-          vr[i] = kv_load16<NT>(vb, off);
-        else
-          vr[i] = kv_load8<NT>(vb, off);
-      }
-    }
-  };
-
-  auto compute = [&](int tile, u32x4_t (&kr)[KS], vrow_t (&vr)[4]) {
-    float4_t sc = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < KS; ++j)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kr[j]), qb[j], sc,
-                                                   0, 0, 0);
-    float y[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = sc[i] * cs;
-    if ((tile + 1) * kTile > n || tile * kTile < lo) {  // partial tile: non-keys
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tile * kTile + 4 * quad + i;
-        if (tok >= n || tok < lo) {
-          y[i] = -INFINITY;
-          vr[i] = VRow<D>::zero();
-        }
-      }
-    }
-    float ym = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-    ym = fmaxf(ym, __shfl_xor(ym, 16));
-    ym = fmaxf(ym, __shfl_xor(ym, 32));
-    const float m_new = fmaxf(m, ym);
-    const float alpha = fast_exp2(m - m_new);
-    // exp2 first, then an exact power-of-two scale: the max token weighs
-    // exactly 2^15, so a lone token reproduces its V row bit for bit
-    float pw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pw[i] = col < G ? fast_exp2(y[i] - m_new) * kPScale : 0.f;
-    l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
-    // fp16 hi + lo split of the weights (B operand of P.V)
-    const auto h01 = __builtin_amdgcn_cvt_pkrtz(pw[0], pw[1]);
-    const auto h23 = __builtin_amdgcn_cvt_pkrtz(pw[2], pw[3]);
-    const auto l01 = __builtin_amdgcn_cvt_pkrtz(pw[0] - (float)h01[0], pw[1] - (float)h01[1]);
-    const auto l23 = __builtin_amdgcn_cvt_pkrtz(pw[2] - (float)h23[0], pw[3] - (float)h23[1]);
-    const half4_t phi = __builtin_bit_cast(
-        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)});
-    const half4_t plo = __builtin_bit_cast(
-        half4_t, u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
-    // rescale only when some head's running max moved (alpha == 1 otherwise)
-    if (wave_any(alpha != 1.f)) {
-#pragma unroll
-      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
-    }
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      // A operand: tokens 4*quad .. 4*quad+3 of dim (chunk col, half e)
-      const int wd = e >> 1;
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t d0 = __builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel);
-      const uint32_t d1 = __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel);
-      const half4_t av = __builtin_bit_cast(half4_t, u32x2_t{d0, d1});
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[e], 0, 0, 0);
-      acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[e], 0, 0, 0);
-    }
-    m = m_new;
+    load_tile<D, BS, NT>(kvh + (size_t)b0 * block_stride, kvh + (size_t)b1 * block_stride,
+                         v_offset, row0, quad, col, t);
   };
 
   int tile = tile_begin + w;
@@ -227,44 +262,44 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   if constexpr (DEPTH == 1) {
     for (; tile < tile_end; tile += NW, ++k_it) {
       if (k_it > 0 && (k_it & 63) == 0) load_ids(k_it);
-      issue(tile, k_it, kA, vA);
-      compute(tile, kA, vA);
+      issue(tile, k_it, tA);
+      compute_tile<D, G>(st, qb, tA, tile, lo, n, cs, quad, col);
     }
   } else {
-    if (tile < tile_end) issue(tile, 0, kA, vA);
+    if (tile < tile_end) issue(tile, 0, tA);
     while (tile < tile_end) {
       int nxt = tile + NW;
       if (nxt < tile_end) {
         if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-        issue(nxt, k_it + 1, kB, vB);
+        issue(nxt, k_it + 1, tB);
       }
-      compute(tile, kA, vA);
+      compute_tile<D, G>(st, qb, tA, tile, lo, n, cs, quad, col);
       tile = nxt;
       ++k_it;
       if (tile >= tile_end) break;
       nxt = tile + NW;
       if (nxt < tile_end) {
         if (((k_it + 1) & 63) == 0) load_ids(k_it + 1);
-        issue(nxt, k_it + 1, kA, vA);
+        issue(nxt, k_it + 1, tA);
       }
-      compute(tile, kB, vB);
+      compute_tile<D, G>(st, qb, tB, tile, lo, n, cs, quad, col);
       tile = nxt;
       ++k_it;
     }
   }
 
   // ---- wave totals, then the NW-wave merge through LDS --------------------
-  float lt = l;
+  float lt = st.l;
   lt += __shfl_xor(lt, 16);
   lt += __shfl_xor(lt, 32);
   if (col < G) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.acc[w][col][VH * (4 * quad + i) + e] = acc[e][i];
+      for (int i = 0; i < 4; ++i) sm.acc[w][col][VH * (4 * quad + i) + e] = st.acc[e][i];
     }
     if (quad == 0) {
-      sm.m[w][col] = m;
+      sm.m[w][col] = st.m;
       sm.l[w][col] = lt;
     }
   }
@@ -287,15 +322,31 @@ unsigned grid_of(const DecodeArgs& a) {
   return (unsigned)a.num_seqs * a.num_parts * a.num_kv_heads;
 }
 
+// The register double buffer fits three workgroups per CU by its VGPRs;
+// two measured faster (sliding-window 70B decode 51 vs 63 us, ragged GQA
+// about 1%, the rest unchanged), so its launches reserve enough dynamic LDS
+// that a third cannot be resident.  The one-tile variant is not capped.
+constexpr int kDoubleBufferWorkgroupsPerCU = 2;
+constexpr size_t kLdsPerCU = 160 * 1024;
+
+template <int D, int G, int NW>
+size_t lds_reserve(int variant) {
+  if (variant == 1) return 0;
+  const size_t fixed = sizeof(DecodeSmem<G, D, NW>) + sizeof(int) * kBalancedMaxSeqs;
+  const size_t want = kLdsPerCU / (kDoubleBufferWorkgroupsPerCU + 1) + 256;
+  return want > fixed ? want - fixed : 0;
+}
+
 // mode 0: launch; mode 1: report resident workgroups per CU in *occ
 template <int D, int BS, int G, int NW>
 int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
+  const size_t dyn = lds_reserve<D, G, NW>(a.variant);
   if (mode == 1) {
     int n = 0;
     const void* fn =
         a.variant == 1 ? reinterpret_cast<const void*>(&decode_mfma_kernel<D, BS, G, NW, 1, true>)
                        : reinterpret_cast<const void*>(&decode_mfma_kernel<D, BS, G, NW, 2, true>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, 0) != hipSuccess) return 2;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, NW * 64, dyn) != hipSuccess) return 2;
     *occ = n;
     return 0;
   }
@@ -303,13 +354,13 @@ int launch_one(const DecodeArgs& a, hipStream_t stream, int mode, int* occ) {
   if (grid == 0) return 0;
   const dim3 g(grid), b(NW * 64);
   if (a.variant == 1 && a.cached_kv)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, false>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, false>), g, b, dyn, stream, a);
   else if (a.variant == 1)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, true>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 1, true>), g, b, dyn, stream, a);
   else if (a.cached_kv)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, false>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, false>), g, b, dyn, stream, a);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, true>), g, b, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BS, G, NW, 2, true>), g, b, dyn, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

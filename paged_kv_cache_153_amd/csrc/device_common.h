@@ -140,7 +140,6 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
   return *(const_i32*)(p);
 }
 
-// True when any lane of the wave has `pred` set (wave-uniform).
 // 16-byte global -> LDS load (global_load_lds_dwordx4): lane l's 16 bytes
 // from `src` land at byte 16 l of the wave-uniform LDS address `dst`,
 // without passing through registers; vmcnt tracks completion.  The builtin
@@ -175,6 +174,7 @@ __device__ __forceinline__ float rows4_max(float x) {
   return fmaxf(c, d);
 }
 
+// True when any lane of the wave has `pred` set (wave-uniform).
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
 }

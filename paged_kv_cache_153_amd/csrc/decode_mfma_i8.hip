@@ -120,16 +120,14 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
   const int Hq = a.num_q_heads;
 
   // ---- q as the B operand: lane (quad, col) = head col, d = quad*D/4 + 8j + e
+  // (padding columns col >= G load head col % G: finite scores, zero weight)
   half8_t qb[KS];
   {
-    const half_t* qh = reinterpret_cast<const half_t*>(a.q) + ((size_t)s * Hq + g * G) * D;
+    const half_t* qh =
+        reinterpret_cast<const half_t*>(a.q) + ((size_t)s * Hq + g * G + col % G) * D;
 #pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (col < G)
-        qb[j] = __builtin_bit_cast(half8_t, load16(qh + col * D + quad * (D / 4) + 8 * j));
-      else
-        qb[j] = __builtin_bit_cast(half8_t, u32x4_t{0u, 0u, 0u, 0u});
-    }
+    for (int j = 0; j < KS; ++j)
+      qb[j] = __builtin_bit_cast(half8_t, load16(qh + quad * (D / 4) + 8 * j));
   }
 
   const size_t head_stride = (size_t)BS * D;  // bytes
@@ -228,9 +226,9 @@ __device__ __forceinline__ void decode_range(const DecodeArgs& a, DecodeSmem<G, 
         }
       }
     }
-    float ym = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-    ym = fmaxf(ym, __shfl_xor(ym, 16));
-    ym = fmaxf(ym, __shfl_xor(ym, 32));
+    // max across the four lane rows by permlane swaps: no LDS round trip, so
+    // no wait on the scalar block-id loads in flight
+    const float ym = rows4_max(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
     const float m_new = fmaxf(m, ym);
     const float alpha = fast_exp2(m - m_new);
     float pw[4], pv[4];

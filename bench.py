@@ -648,6 +648,7 @@ def main():
     wall = time.perf_counter() - t0
     dec_ms = [a.elapsed_time(b) for a, b in ev]
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
     total_bytes = sum(st.kv_bytes)
     total_tokens = sum(st.ctx_tokens)
     step_s = wall / args.steps
@@ -693,6 +694,7 @@ def main():
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
         "seq_ctx_tokens_per_s": round(total_tokens / wall, 1),
         "decode_us": round(dec_avg_s * 1e6, 2),
+        "decode_us_median": round(dec_med_s * 1e6, 2),
         "decode_seq_ctx_tokens_per_s": round(total_tokens / args.steps / dec_avg_s, 1),
         "cow_pairs_per_step": round(sum(st.ncow) / args.steps, 3),
         "prefix_cache": st.prefix_info,

@@ -1,0 +1,171 @@
+"""GPU parity on seeded random configurations: every option of pa_decode
+drawn at once — pool dtype (f32, f16, INT8), head_dim, block size, query
+group (MHA to MQA), a length mix with empty, one-token and block-boundary
+contexts, sliding window, schedule (auto, single pass, balanced, fixed
+partitions), kernel family, load policy, table width and the host bound on
+the lengths — and random causal prefill chunks (chunk lengths, pasts,
+block size, head_dim, group).  Each case is checked against the fp64 oracle
+(max-abs error <= 5e-4) with every pool row outside the keys a query may
+see poisoned with NaN (for INT8 pools, their scales), so a read outside
+them fails the case.  The draws are seeded: a failing case id names its
+configuration exactly."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_153_amd as pa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-4
+DECODE_CASES = 96
+PREFILL_CASES = 32
+HEADS = [(4, 4), (8, 8), (8, 4), (8, 2), (16, 2), (16, 4), (32, 4), (8, 1), (4, 1)]
+
+
+def _length(rng, bs):
+    """One context length from a mix that favours the edges of the method."""
+    kind = rng.integers(0, 8)
+    if kind == 0:
+        return 0
+    if kind == 1:
+        return 1
+    if kind == 2:
+        return int(max(1, bs * rng.integers(1, 20) + rng.integers(-1, 2)))  # block edges
+    if kind == 3:
+        return int(max(1, 16 * rng.integers(1, 40) + rng.integers(-1, 2)))  # tile edges
+    if kind == 4:
+        return int(rng.integers(600, 2500))
+    return int(rng.integers(1, 600))
+
+
+def draw_decode(case):
+    rng = np.random.default_rng(1000 + case)
+    cfg = {}
+    cfg["dtype"] = ["f32", "f16", "f16", "i8"][rng.integers(0, 4)]
+    cfg["d"] = int([64, 128][rng.integers(0, 2)])
+    cfg["bs"] = int([8, 16, 32][rng.integers(0, 3)])
+    cfg["hq"], cfg["hkv"] = HEADS[rng.integers(0, len(HEADS))]
+    S = int(rng.integers(1, 25))
+    lens = [_length(rng, cfg["bs"]) for _ in range(S)]
+    while sum(lens) * cfg["hq"] > 400_000:        # keep the oracle to a second or so
+        lens[int(np.argmax(lens))] //= 2
+    cfg["lens"] = lens
+    cfg["window"] = 0 if rng.random() < 0.6 else int(rng.integers(1, 2000))
+    step = 16 * cfg["bs"] // math.gcd(16, cfg["bs"])
+    cfg["part"] = int([0, 0, -1, -2, step * rng.integers(1, 1 + 1024 // step)][rng.integers(0, 5)])
+    group = cfg["hq"] // cfg["hkv"]
+    kernels = ["auto", "valu"] + (["mfma"] if cfg["dtype"] != "f32" and group >= 2 else [])
+    cfg["kernel"] = kernels[rng.integers(0, len(kernels))]
+    cfg["cached"] = bool(rng.integers(0, 2))
+    cfg["extra_blocks"] = int(rng.integers(0, 4))      # table wider than needed
+    cfg["extra_len"] = int([0, 0, 37][rng.integers(0, 3)])  # host bound above the max
+    cfg["scale"] = None if rng.random() < 0.7 else float(rng.uniform(0.01, 0.3))
+    cfg["std"] = float([1.0, 0.5, 2.0][rng.integers(0, 3)])
+    return cfg
+
+
+def poison_before_window(x, window, codes_scales=None):
+    """NaN in the rows of sequence s that hold tokens t < n - W (the blocks
+    of different sequences are disjoint in these inputs).  For an INT8 pool
+    the rows' scales are poisoned instead."""
+    bs = x.block_size
+    for s, n in enumerate(x.context_lens.tolist()):
+        lo = max(0, n - window)
+        for t0 in range(0, lo, bs):
+            b = int(x.block_tables[s, t0 // bs])
+            rows = min(bs, lo - t0)
+            if codes_scales is None:
+                x.kv_cache[b, :, :, :rows] = float("nan")
+            else:
+                codes_scales[b, :, :, :rows] = float("nan")
+
+
+def build_decode(cfg, case):
+    mb = max(1, max(-(-n // cfg["bs"]) for n in cfg["lens"])) + cfg["extra_blocks"]
+    base = "f16" if cfg["dtype"] == "i8" else cfg["dtype"]
+    x = synth.make_decode_inputs(cfg["lens"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["bs"],
+                                 dtype=base, seed=5000 + case, std=cfg["std"],
+                                 scale=cfg["scale"], max_blocks=mb,
+                                 fill_unused=None if cfg["dtype"] == "i8" else float("nan"),
+                                 name=f"case{case}")
+    if cfg["dtype"] == "i8":
+        x = synth.int8_pool(x, fill_unused=float("nan"))
+        if cfg["window"]:
+            poison_before_window(x, cfg["window"], x.kv_scales)
+    elif cfg["window"]:
+        poison_before_window(x, cfg["window"])
+    return x
+
+
+@pytest.mark.parametrize("case", range(DECODE_CASES))
+def test_random_decode_config(device, case):
+    cfg = draw_decode(case)
+    print(f"  case {case}: {cfg}", flush=True)
+    x = build_decode(cfg, case)
+    if cfg["dtype"] == "i8":
+        want = oracle.decode_i8_ref(x.q.numpy(), x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                    x.block_tables.numpy(), x.context_lens.numpy(), x.scale,
+                                    window=cfg["window"])
+    else:
+        want = oracle.decode_ref(x.q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                                 x.context_lens.numpy(), x.scale, window=cfg["window"])
+    assert np.isfinite(want).all()
+    g = x.to(device)
+    out = pa.decode(g.q, g.kv_cache, g.block_tables, g.context_lens, scale=x.scale,
+                    max_context_len=max(cfg["lens"]) + cfg["extra_len"],
+                    partition_size=cfg["part"], kernel=cfg["kernel"], cached_kv=cfg["cached"],
+                    sliding_window=cfg["window"], kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), cfg
+    err = float(np.abs(got - want).max()) if want.size else 0.0
+    assert err <= TOL, (case, err, cfg)
+    for s, n in enumerate(cfg["lens"]):
+        if n == 0:
+            assert np.all(got[s] == 0), (case, s)
+
+
+def draw_prefill(case):
+    rng = np.random.default_rng(2000 + case)
+    cfg = {"d": int([64, 128][rng.integers(0, 2)]), "bs": int([8, 16, 32][rng.integers(0, 3)])}
+    cfg["hq"], cfg["hkv"] = HEADS[rng.integers(0, len(HEADS))]
+    S = int(rng.integers(1, 7))
+    chunks, lens = [], []
+    for _ in range(S):
+        t = int([0, 1, rng.integers(2, 40), rng.integers(40, 300)][rng.integers(0, 4)])
+        past = int([0, rng.integers(1, 64), rng.integers(64, 900)][rng.integers(0, 3)])
+        chunks.append(t)
+        lens.append(t + past)
+    if sum(chunks) == 0:  # at least one query row
+        chunks[0] = 1
+        lens[0] = max(lens[0], 1)
+    cfg["chunks"], cfg["lens"] = chunks, lens
+    return cfg
+
+
+@pytest.mark.parametrize("case", range(PREFILL_CASES))
+def test_random_prefill_config(device, case):
+    cfg = draw_prefill(case)
+    print(f"  prefill case {case}: {cfg}", flush=True)
+    x = synth.make_decode_inputs(cfg["lens"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["bs"],
+                                 dtype="f16", seed=7000 + case, fill_unused=float("nan"))
+    qstart = np.concatenate([[0], np.cumsum(cfg["chunks"])]).astype(np.int32)
+    total = int(qstart[-1])
+    q = synth.normal((total, cfg["hq"], cfg["d"]), torch.float16, synth._gen(7100 + case, "cpu"),
+                     "cpu")
+    want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                              x.context_lens.numpy(), qstart, x.scale)
+    out = pa.prefill(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
+                     x.context_lens.to(device), torch.from_numpy(qstart).to(device),
+                     scale=x.scale, max_query_len=max(1, max(cfg["chunks"])))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), cfg
+    err = float(np.abs(got - want).max()) if want.size else 0.0
+    assert err <= TOL, (case, err, cfg)

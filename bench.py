@@ -80,12 +80,14 @@ def source_fingerprint():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode dispatch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
-    none for this workload or the kernels changed since it was taken."""
+def measured_traffic(workload, mode="decode"):
+    """HBM bytes per decode (or prefill) dispatch from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when
+    there is none for this workload or the kernels changed since it was
+    taken."""
     import glob
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"decode_*_{workload}.md"))):
+    pattern = f"decode_*_{workload}.md" if mode == "decode" else f"prefill_*_prefill_{workload}.md"
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
         fields = {}
         for line in open(path):
             if " = " in line:
@@ -398,6 +400,58 @@ def cpu_baseline(st, budget_s=20.0, cap_wall_s=8.0):
                        f"{wall:.2f} s wall; {toks / wall:.4g} seq*ctx tokens/s")
 
 
+def prefill_cpu_baseline(q, x, S, T, n, budget_s=20.0, cap_wall_s=8.0, rows=16):
+    """Time the fp64 oracle (prefill_ref) on the host cores: groups of
+    ``rows`` consecutive query rows of the step's first sequences, each group
+    the last ``rows`` tokens of a context ending at its last row (host copies
+    of the sequences' blocks and queries are made first, outside the timed
+    region), computed by a pool of worker threads (BLAS limited to one thread
+    each) until about ``budget_s`` of CPU time or ``cap_wall_s`` of wall
+    time.  TFLOP/s of useful flops (4 * D * Hq per query row and key)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    import numpy as np
+    import oracle
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    bs, Hq, D = x.block_size, x.num_q_heads, x.head_dim
+    nseq = min(S, 4)
+    host = []
+    for s_ in range(nseq):
+        ids = x.block_tables[s_, :-(-n // bs)].long()
+        host.append((x.kv_cache[ids].cpu().numpy(), q[s_ * T:(s_ + 1) * T].cpu().numpy()))
+    groups = [(s_, i0) for i0 in range(0, T - rows + 1, rows) for s_ in range(nseq)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(groups)
+
+    def one(item):
+        s_, i0 = item
+        blocks, qs = host[s_]
+        ctx = n - T + i0 + rows                 # the group is the last `rows` tokens
+        return oracle.prefill_ref(qs[i0:i0 + rows], blocks, np.arange(blocks.shape[0])[None],
+                                  np.array([ctx]), np.array([0, rows]), x.scale)
+
+    done, flops = 0, 0.0
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        t0 = time.perf_counter()
+        while True:
+            batch = [groups[(done + k) % len(groups)] for k in range(workers)]
+            for f in [ex.submit(one, it) for it in batch]:
+                f.result()
+            for s_, i0 in batch:
+                keys = sum(n - T + i + 1 for i in range(i0, i0 + rows))
+                flops += 4.0 * D * Hq * keys
+            done += len(batch)
+            wall = time.perf_counter() - t0
+            if wall * workers >= budget_s or wall >= cap_wall_s:
+                break
+    return dict(value=round(flops / wall / 1e12, 6), unit="TFLOP/s", cores=workers,
+                kind="oracle",
+                sample=f"fp64 NumPy prefill oracle on {workers} worker threads (BLAS 1 thread "
+                       f"each): {done} groups of {rows} query rows from the first {nseq} "
+                       f"sequences' chunks ({done * rows} query rows, {flops:.4g} useful flops) "
+                       f"in {wall:.2f} s wall")
+
+
 def stream_ceiling(dev, tile_bytes=4096, nbytes=4 << 30, reps=5):
     """Measured HBM read ceiling on this GPU (libpa_probe.so): a linear
     grid-stride read and reads of 4 KiB (and, when the decode's K/V tiles
@@ -563,8 +617,12 @@ def prefill_bench(args, dev):
         "parity_max_abs_err": parity,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None},
-        "cpu_baseline": None,
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     # HBM bytes per pa_prefill dispatch (rocprofv3, committed
+                     # profile) for the configuration it was taken on
+                     "traffic": measured_traffic(args.workload, "prefill")
+                     if (S, T, n, bs) == (8, 512, 4096, w["bs"]) else None},
+        "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(q, x, S, T, n),
     }
     print(json.dumps(res), flush=True)
 

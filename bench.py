@@ -621,7 +621,7 @@ def prefill_bench(args, dev):
                      # HBM bytes per pa_prefill dispatch (rocprofv3, committed
                      # profile) for the configuration it was taken on
                      "traffic": measured_traffic(args.workload, "prefill")
-                     if (S, T, n, bs) == (8, 512, 4096, w["bs"]) else None},
+                     if (S, T, n, bs, args.seed) == (8, 512, 4096, w["bs"], 0) else None},
         "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(q, x, S, T, n),
     }
     print(json.dumps(res), flush=True)
@@ -769,7 +769,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(args.workload + ("_i8" if st.int8 else "")
                                         + (f"_w{args.window}" if args.window else ""))
-            if (args.kernel, args.partition, args.context) == ("auto", 0, 0) else None,
+            # only for the configuration the profile was taken on
+            if (args.kernel, args.partition, args.context, args.block_size, args.kv_loads,
+                args.seed) == ("auto", 0, 0, None, "auto", 0) else None,
         },
         "cpu_baseline": cpu,
     }

@@ -28,6 +28,7 @@ import argparse
 import json
 import math
 import os
+import random
 import sys
 import time
 
@@ -180,7 +181,7 @@ class Step:
                                 "cached_blocks": st_[0], "hit_blocks": st_[3],
                                 "missed_full_blocks": st_[4]}
             self.fork_child = S - 1
-            self.rng = torch.Generator().manual_seed(seed + 1)
+            self.parent_rng = random.Random(seed + 1)   # the parent forked each step
         elif name == "shared_prefix":
             self.prefix_seq = 1 << 41
             bm.allocate(self.prefix_seq, self.prefix)
@@ -196,7 +197,7 @@ class Step:
                     remaining[s] -= 1
             # every sequence was decoded once already: last token is appended per step
             self.fork_child = S - 1
-            self.rng = torch.Generator().manual_seed(seed + 1)
+            self.parent_rng = random.Random(seed + 1)   # the parent forked each step
         else:
             for s, n in enumerate(lens0):
                 bm.allocate(s, n - 1)        # the step appends token n
@@ -249,6 +250,17 @@ class Step:
                                   stage_args=(self.d_pack.data_ptr(), h.data_ptr(),
                                               self.n_i32 * 4, stream),
                                   fused_args=fused))
+        # pa_decode's arguments but the per-step length bound, prepared once
+        # (the binding's checks would add host time to every step)
+        self.decode_pre = (self.out.data_ptr(), self.q.data_ptr(), self.pool.data_ptr(),
+                           self.kv_scales.data_ptr() if self.int8 else None,
+                           self.d_tables.data_ptr(), self.d_lens.data_ptr(), S, Hq, Hkv, D, bs,
+                           self.mb)
+        self.decode_post = (nb, float(self.scale), int(window), int(partition),
+                            pa.KERNELS[kernel] | (pa.KV_CACHED if self.cached_kv else 0),
+                            self.ws.data_ptr(), self.ws.numel(), None,
+                            pa.I8 if self.int8 else pa.F32 if w["dtype"] == "f32" else pa.F16,
+                            torch.cuda.current_stream(dev).cuda_stream)
         self.k = 0
         self.kv_bytes = []       # algorithmic decode bytes per step
         self.ctx_tokens = []
@@ -272,9 +284,8 @@ class Step:
             except pa.PAError:
                 pass
             while True:
-                parent = int(self.torch.randint(0, self.S - 1, (1,), generator=self.rng))
-                _, n = self.bm.block_table(parent)
-                if n % self.bs:
+                parent = self.parent_rng.randrange(self.S - 1)
+                if self.bm.num_tokens(parent) % self.bs:
                     break
             self.bm.fork(parent, child)
         ncow = self.bm.append_slots_into(self.seqs, buf["slots"], buf["pairs"])
@@ -288,16 +299,18 @@ class Step:
     def key_tokens(self, lens):
         """Tokens the decode attends to: the whole context, or at most the
         last ``window`` tokens of each sequence."""
+        import numpy as np
+        ln = lens.numpy()
         if self.window > 0:
-            return int(lens.clamp(max=self.window).sum())
-        return int(lens.sum())
+            return int(np.minimum(ln, self.window).sum())
+        return int(ln.sum())
 
     def run(self, timed_events=None):
         torch, pa = self.torch, self.pa
         buf = self.bufs[self.k % 2]
         buf["event"].synchronize()          # its previous copies have left pinned memory
         ncow = self.host_step(buf)
-        maxlen = int(buf["lens"].max())
+        maxlen = int(buf["lens"].numpy().max())
         # the C calls take arguments prepared once per buffer (the binding's
         # checks would add host time to every step)
         if self.upload == "fused":   # upload + K/V scatter in one launch
@@ -319,10 +332,9 @@ class Step:
                            kv_scales=self.kv_scales)
         if timed_events is not None:
             timed_events[0].record()
-        pa.decode(self.q, self.pool, self.d_tables, self.d_lens, scale=self.scale,
-                  max_context_len=maxlen, partition_size=self.partition, kernel=self.kernel,
-                  out=self.out, workspace=self.ws, cached_kv=self.cached_kv,
-                  sliding_window=self.window, kv_scales=self.kv_scales)
+        rc = pa.lib().pa_decode(*self.decode_pre, maxlen, *self.decode_post)
+        if rc != 0:
+            raise pa.PAError(rc, pa.lib().pa_last_error().decode())
         if timed_events is not None:
             timed_events[1].record()
         self.k += 1

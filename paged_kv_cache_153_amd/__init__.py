@@ -71,7 +71,8 @@ _SIGNATURES = {
     "pa_bm_share": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int, _c.c_int64]),
     "pa_bm_fork": (_c.c_int, [_P, _c.c_int64, _c.c_int64]),
     "pa_bm_append_slot": (_c.c_int, [_P, _c.c_int64, _I64P, _I32P, _I32P]),
-    "pa_bm_append_slots": (_c.c_int, [_P, _I64P, _c.c_int, _I64P, _I32P,
+    # the batched calls take buffer addresses as plain integers (no ctypes.cast)
+    "pa_bm_append_slots": (_c.c_int, [_P, _P, _c.c_int, _P, _P,
                                       _c.POINTER(_c.c_int)]),
     "pa_bm_free": (_c.c_int, [_P, _c.c_int64]),
     "pa_bm_enable_prefix_cache": (_c.c_int, [_P, _c.c_int]),
@@ -81,7 +82,7 @@ _SIGNATURES = {
     "pa_bm_prefix_stats": (_c.c_int, [_P, _I64P]),
     "pa_bm_block_table": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int, _c.POINTER(_c.c_int),
                                      _I64P]),
-    "pa_bm_block_tables": (_c.c_int, [_P, _I64P, _c.c_int, _I32P, _c.c_int, _I32P]),
+    "pa_bm_block_tables": (_c.c_int, [_P, _P, _c.c_int, _P, _c.c_int, _P]),
     "pa_bm_stats": (_c.c_int, [_P, _I64P, _I64P, _I64P]),
     "pa_bm_ref_count": (_c.c_int, [_P, _c.c_int32]),
     "pa_strerror": (_c.c_char_p, [_c.c_int]),
@@ -361,11 +362,12 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
     return out
 
 
-def _ptr(t, ptype):
-    """Raw pointer of a contiguous CPU tensor (no copy)."""
+def _addr(t):
+    """Address of a contiguous CPU tensor's data (no copy), as an integer for
+    a ``c_void_p`` parameter."""
     if t.is_cuda or not t.is_contiguous():
         raise ValueError("expected a contiguous CPU tensor")
-    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ptype)
+    return t.data_ptr()
 
 
 # ---------------------------------------------------------------------------
@@ -431,6 +433,13 @@ class BlockManager:
                                        ctypes.byref(ntok)))
         return list(buf[:n.value]), ntok.value
 
+    def num_tokens(self, seq):
+        """Tokens of ``seq`` (its context length), without copying its table."""
+        n, ntok = ctypes.c_int(0), ctypes.c_int64(0)
+        _check(lib().pa_bm_block_table(self._h, int(seq), None, 0, ctypes.byref(n),
+                                       ctypes.byref(ntok)))
+        return ntok.value
+
     def block_tables(self, seqs, max_blocks):
         """Padded int32 tables [n, max_blocks] (-1 fill) and int32 lengths, as
         Python lists of rows (the caller copies them to the device)."""
@@ -448,15 +457,15 @@ class BlockManager:
         Returns the number of copy pairs written."""
         n = seqs.numel()
         k = ctypes.c_int(0)
-        _check(lib().pa_bm_append_slots(self._h, _ptr(seqs, _I64P), n, _ptr(slots, _I64P),
-                                        _ptr(cow_pairs, _I32P), ctypes.byref(k)))
+        _check(lib().pa_bm_append_slots(self._h, _addr(seqs), n, _addr(slots),
+                                        _addr(cow_pairs), ctypes.byref(k)))
         return k.value
 
     def block_tables_into(self, seqs, tables, context_lens):
         """Fill CPU int32 ``tables`` [n, MB] (-1 padded) and ``context_lens`` [n]."""
         n = seqs.numel()
-        _check(lib().pa_bm_block_tables(self._h, _ptr(seqs, _I64P), n, _ptr(tables, _I32P),
-                                        tables.shape[1], _ptr(context_lens, _I32P)))
+        _check(lib().pa_bm_block_tables(self._h, _addr(seqs), n, _addr(tables),
+                                        tables.shape[1], _addr(context_lens)))
 
     def stats(self):
         f, u, s = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()

@@ -33,7 +33,6 @@
 #include <set>
 #include <tuple>
 #include <unordered_map>
-#include <unordered_set>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -150,9 +149,11 @@ int plan_append(const pa_bm* bm, const pa_bm::Seq& s,
                 std::unordered_map<int32_t, int>& dropped) {
   if (s.num_tokens % bm->block_size == 0) return 1;
   const int32_t last = s.blocks.back();
-  const int live = bm->refs[last] - dropped[last];
-  if (live > 1) {
-    dropped[last] += 1;
+  if (bm->refs[last] <= 1) return 0;  // private last block: written in place
+  const auto it = dropped.find(last);
+  const int already = it == dropped.end() ? 0 : it->second;
+  if (bm->refs[last] - already > 1) {
+    dropped[last] = already + 1;
     return 1;
   }
   return 0;
@@ -292,23 +293,37 @@ int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, int n, int64_t* slots,
   if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
   if (n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_cow)
     return fail(PA_ERR_INVALID_ARG, "bad arguments");
-  std::unordered_set<int64_t> seen;
-  std::unordered_map<int32_t, int> dropped;
+  // the first position that repeats an earlier sequence (n if none), found
+  // by sorting (id, position) pairs: a batch reports the same first error a
+  // sequential run would, without a hash-set node per sequence
+  int first_repeat = n;
+  std::vector<pa_bm::Seq*> rows;
+  try {
+    std::vector<std::pair<int64_t, int>> order((size_t)n);
+    for (int i = 0; i < n; ++i) order[i] = {seqs[i], i};
+    std::sort(order.begin(), order.end());
+    for (int i = 1; i < n; ++i)
+      if (order[i].first == order[i - 1].first) first_repeat = std::min(first_repeat, order[i].second);
+    rows.resize((size_t)n);
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
+  std::unordered_map<int32_t, int> dropped;  // only shared last blocks enter
   int64_t needed = 0;
   for (int i = 0; i < n; ++i) {
-    if (!seen.insert(seqs[i]).second)
-      return fail(PA_ERR_INVALID_ARG, "sequence repeated in one batch");
+    if (i == first_repeat) return fail(PA_ERR_INVALID_ARG, "sequence repeated in one batch");
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
       return fail(PA_ERR_NOT_FOUND, "unknown sequence " + std::to_string(seqs[i]));
+    rows[i] = &it->second;  // stable: nothing is inserted or erased below
     // fail at the first sequence that would not fit, as a sequential run would
-    needed += plan_append(bm, it->second, dropped);
+    needed += plan_append(bm, *rows[i], dropped);
     if (bm->available() < needed) return fail(PA_ERR_OOM, "out of KV cache blocks");
   }
   int k = 0;
   for (int i = 0; i < n; ++i) {
     int32_t src, dst;
-    do_append(bm, seqs[i], bm->seqs.at(seqs[i]), &slots[i], &src, &dst);
+    do_append(bm, seqs[i], *rows[i], &slots[i], &src, &dst);
     if (src >= 0) {
       cow_pairs[2 * k] = src;
       cow_pairs[2 * k + 1] = dst;
@@ -347,6 +362,12 @@ int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int n, int32_t* tab
   if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
   if (n < 0 || max_blocks <= 0 || (n > 0 && (!seqs || !tables || !context_lens)))
     return fail(PA_ERR_INVALID_ARG, "bad arguments");
+  std::vector<const pa_bm::Seq*> rows;
+  try {
+    rows.resize((size_t)n);
+  } catch (...) {
+    return fail(PA_ERR_OOM, "host memory exhausted");
+  }
   for (int i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end())
@@ -355,12 +376,13 @@ int pa_bm_block_tables(const pa_bm* bm, const int64_t* seqs, int n, int32_t* tab
       return fail(PA_ERR_INVALID_ARG, "table longer than max_blocks");
     if (it->second.num_tokens > INT32_MAX)
       return fail(PA_ERR_INVALID_ARG, "context length does not fit int32");
+    rows[i] = &it->second;
   }
   for (int i = 0; i < n; ++i) {
-    const pa_bm::Seq& s = bm->seqs.at(seqs[i]);
+    const pa_bm::Seq& s = *rows[i];
     int32_t* row = tables + (int64_t)i * max_blocks;
-    const int len = (int)s.blocks.size();
-    for (int j = 0; j < max_blocks; ++j) row[j] = j < len ? s.blocks[j] : -1;
+    std::copy(s.blocks.begin(), s.blocks.end(), row);
+    std::fill(row + s.blocks.size(), row + max_blocks, -1);
     context_lens[i] = (int32_t)s.num_tokens;
   }
   return PA_OK;

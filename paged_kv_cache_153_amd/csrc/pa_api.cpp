@@ -10,7 +10,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -383,6 +385,43 @@ int pa_stage_from_host(void* dst, const void* src, int64_t bytes, void* stream_)
   return rc ? fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError())) : PA_OK;
 }
 
+namespace {
+
+// Resident workgroups per CU of the decode kernel a launch will use, cached
+// per (kernel family, dtype, head_dim, block size, group, variant, device):
+// the runtime's occupancy query would otherwise cost host time on every
+// balanced-schedule call.  0 if the query fails (not cached).
+int decode_occupancy(const pa::DecodeArgs& a, int use, int dtype, int head_dim, int block_size,
+                     int group) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const uint64_t key = ((uint64_t)(unsigned)dev << 40) | ((uint64_t)(unsigned)use << 32) |
+                       ((uint64_t)(unsigned)dtype << 24) | ((uint64_t)(unsigned)head_dim << 12) |
+                       ((uint64_t)(unsigned)block_size << 6) | ((uint64_t)(unsigned)group << 2) |
+                       (uint64_t)(a.variant & 3);
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int> cache;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int occ;
+  if (dtype == PA_I8)
+    occ = use == PA_KERNEL_MFMA ? pa::decode_mfma_i8_occupancy(a, head_dim, block_size, group)
+                                : pa::decode_valu_i8_occupancy(a, head_dim, block_size, group);
+  else
+    occ = use == PA_KERNEL_MFMA ? pa::decode_mfma_occupancy(a, head_dim, block_size, group)
+                                : pa::decode_valu_occupancy(a, dtype, head_dim, block_size, group);
+  if (occ > 0) {
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = occ;
+  }
+  return occ;
+}
+
+}  // namespace
+
 int pa_decode(float* out, const void* query, const void* kv_cache, const float* kv_scales,
               const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
               int head_dim, int block_size, int max_blocks_per_seq, int max_context_len,
@@ -499,14 +538,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);
   if (plan.schedule == pa::kScheduleBalanced) {
     // as many workgroups as are resident at once: one wave of the grid
-    int occ;
-    if (dtype == PA_I8)
-      occ = use == PA_KERNEL_MFMA ? pa::decode_mfma_i8_occupancy(a, head_dim, block_size, group)
-                                  : pa::decode_valu_i8_occupancy(a, head_dim, block_size, group);
-    else
-      occ = use == PA_KERNEL_MFMA
-                ? pa::decode_mfma_occupancy(a, head_dim, block_size, group)
-                : pa::decode_valu_occupancy(a, dtype, head_dim, block_size, group);
+    const int occ = decode_occupancy(a, use, dtype, head_dim, block_size, group);
     if (occ <= 0) return fail(PA_ERR_HIP, "occupancy query failed");
     a.num_workgroups = std::min(plan.workgroups, cus * std::min(occ, pa::kMaxWorkgroupsPerCU));
   }

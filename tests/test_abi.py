@@ -213,6 +213,7 @@ def test_native_block_manager_matches_model(ops, bs, nb):
             assert bm.ref_count(blk) == ref.ref_count(blk)
         for seq in ref.tables:
             assert bm.block_table(seq) == ref.block_table(seq)
+            assert bm.num_tokens(seq) == ref.block_table(seq)[1]
     seqs = sorted(ref.tables)
     if seqs:
         mb = max(1, max(len(ref.tables[s_]) for s_ in seqs))
@@ -367,3 +368,25 @@ def test_stage_from_host_rejects_bad_arguments(dst, src, nbytes, status):
 
 def test_stage_from_host_zero_bytes_is_a_no_op():
     assert pa.lib().pa_stage_from_host(None, None, 0, None) == 0
+
+
+def test_batch_append_reports_the_first_failure_and_changes_nothing():
+    """A batched append fails where a sequential run would first fail — an
+    unknown sequence before a repeated one gives NOT_FOUND, a repeat before
+    an unknown one INVALID_ARG — and leaves the manager untouched."""
+    bm = pa.BlockManager(16, 4)
+    bm.allocate(0, 3)
+    bm.allocate(1, 5)
+    before = (bm.stats(), bm.block_table(0), bm.block_table(1))
+    with pytest.raises(pa.PAError) as e:
+        bm.append_slots([0, 7, 0])
+    assert e.value.status == -5
+    with pytest.raises(pa.PAError) as e:
+        bm.append_slots([1, 1, 7])
+    assert e.value.status == -1
+    assert (bm.stats(), bm.block_table(0), bm.block_table(1)) == before
+    assert bm.num_tokens(0) == 3 and bm.num_tokens(1) == 5
+    slots, pairs = bm.append_slots([1, 0])
+    assert bm.num_tokens(0) == 4 and bm.num_tokens(1) == 6 and pairs == []
+    bm.close()
+

@@ -308,7 +308,8 @@ class Step:
     def run(self, timed_events=None):
         torch, pa = self.torch, self.pa
         buf = self.bufs[self.k % 2]
-        buf["event"].synchronize()          # its previous copies have left pinned memory
+        fence = buf.pop("fence", None) or buf["event"]
+        fence.synchronize()                 # its previous upload has left pinned memory
         ncow = self.host_step(buf)
         maxlen = int(buf["lens"].numpy().max())
         # the C calls take arguments prepared once per buffer (the binding's
@@ -318,7 +319,13 @@ class Step:
             rc = pa.lib().pa_stage_and_write(*a[0], a[1] if ncow else None, ncow, *a[2])
             if rc != 0:
                 raise pa.PAError(rc, pa.lib().pa_last_error().decode())
-            buf["event"].record()
+            # the pinned buffer may be refilled once this upload has run: in a
+            # timed step the event after the decode marks that (one queue
+            # marker fewer per step), otherwise a marker of its own
+            if timed_events is None:
+                buf["event"].record()
+            else:
+                buf["fence"] = timed_events[1]
         else:
             if self.upload == "kernel":
                 rc = pa.lib().pa_stage_from_host(*buf["stage_args"])

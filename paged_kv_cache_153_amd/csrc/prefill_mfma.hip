@@ -32,7 +32,9 @@
 //                parts, which keeps ~21 bits of each weight;
 //   the weight sums as one more block whose V rows are all ones.
 // q.K of step st + 1 is issued between the max and the exponentials of step
-// st, so the matrix cores have work while the vector ALUs do the softmax.
+// st, so the matrix cores have work while the vector ALUs do the softmax;
+// the softmax runs at raised wave priority (s_setprio) so that it overlaps
+// the other wave's matrix products.
 // LDS rows are 2D bytes.  K rows have their 16-byte chunks XOR-swizzled by
 // the row, so that the 16 lanes that read one chunk of 16 different K rows
 // hit distinct banks; V rows are plain, since the lanes of a quad read one V
@@ -235,6 +237,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
                         float4_t (&sn)[CB][2]) {
     constexpr int b = decltype(B)::value;
     const unsigned char* vt = lds[b][1];
+    // The wave takes issue priority for its vector work (V reads, max,
+    // exponentials, weight split) and drops it before its P.V products: the
+    // other wave of the SIMD is then usually in its matrix phase, whose
+    // issued MFMAs keep running, so the two phases overlap more (measured
+    // +3.5-5% on every head shape).  A wave's in-kernel priority, not a
+    // queue priority.
+    __builtin_amdgcn_s_setprio(1);
     // V rows 4 quad + i of both tiles, this lane's D/16 values of each
     vrow_t vr[8];
 #pragma unroll
@@ -292,6 +301,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       phi[cb] = __builtin_bit_cast(half8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
       plo[cb] = __builtin_bit_cast(half8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
     }
+    __builtin_amdgcn_s_setprio(0);
     // P.V in pairs of output blocks: each accumulator's hi and lo products
     // are 2 * CB instructions apart
 #pragma unroll

@@ -199,6 +199,27 @@ def test_full_size_sampled(device, name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_shared_prefix_full_size_sampled(device, bs):
+    """The shared-prefix workload at its full size (64 sequences over one
+    512-token prefix, private suffixes U[1, 2048]) in the launch the
+    benchmark uses for it: cached K/V loads, schedule chosen by the
+    library; sampled (sequence, head) pairs against the oracle."""
+    print(f"full-size shared prefix bs={bs}", flush=True)
+    x = synth.shared_prefix(seed=0, block_size=bs, device=device)
+    out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
+                    max_context_len=int(x.context_lens.max()), cached_kv=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    S, Hq = x.num_seqs, x.num_q_heads
+    rng = np.random.default_rng(bs)
+    samples = [(0, 0), (S - 1, Hq - 1)] + [(int(rng.integers(S)), int(rng.integers(Hq)))
+                                           for _ in range(4)]
+    _sampled_check(x, out, samples)
+    del x, out
+    torch.cuda.empty_cache()
+
+
 def test_cached_and_streaming_loads_agree(device):
     """The load policy changes no arithmetic where the schedule is the same
     (single pass, fixed partitions): bitwise equal.  Under the balanced

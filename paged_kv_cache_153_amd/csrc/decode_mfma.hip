@@ -42,15 +42,11 @@ struct VRow;  // per-lane share of one V row: 16 bytes (D=128) or 8 bytes (D=64)
 template <>
 struct VRow<128> {
   using type = u32x4_t;
-  static __device__ __forceinline__ type load(const half_t* p) { return load16(p); }
   static __device__ __forceinline__ type zero() { return type{0u, 0u, 0u, 0u}; }
 };
 template <>
 struct VRow<64> {
   using type = u32x2_t;
-  static __device__ __forceinline__ type load(const half_t* p) {
-    return *reinterpret_cast<const u32x2_t*>(p);
-  }
   static __device__ __forceinline__ type zero() { return type{0u, 0u}; }
 };
 

@@ -30,7 +30,11 @@
  *     buffers, but the result is then unspecified.  With the environment
  *     variable PA_CHECK=1 the library copies those arrays to the host,
  *     validates them and returns PA_ERR_INVALID_ARG instead (slow; for
- *     debugging).
+ *     debugging).  PA_CHECK is read on every call.
+ *   - Other environment switches: PA_LOG=1 (read when a block manager is
+ *     created) logs its allocations, shares and frees to stderr;
+ *     PA_TUNE_VARIANT=0..2 (read once per process) overrides the decode
+ *     kernels' pipeline variant, for tuning experiments only.
  */
 #ifndef PA_H_
 #define PA_H_

@@ -32,7 +32,8 @@
  *     validates them and returns PA_ERR_INVALID_ARG instead (slow; for
  *     debugging).  PA_CHECK is read on every call.
  *   - Other environment switches: PA_LOG=1 (read when a block manager is
- *     created) logs its allocations, shares and frees to stderr;
+ *     created) logs to stderr every block it takes from the free list and
+ *     every reference it drops;
  *     PA_TUNE_VARIANT=0..2 (read once per process) overrides the decode
  *     kernels' pipeline variant, for tuning experiments only.
  */

@@ -199,6 +199,31 @@ def test_full_size_sampled(device, name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_more_sequences_than_the_balanced_schedule_holds(device, dtype):
+    """1100 sequences (the balanced schedule keeps its tables of at most
+    1024 in LDS): asking for it falls back to fixed partitions; every output
+    against the oracle, for the requested and the automatic schedule."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, 200, 1100).tolist()
+    x = synth.make_decode_inputs(lens, 16, 4, 128, 16, dtype="f16", seed=22,
+                                 fill_unused=None if dtype == "i8" else float("nan"))
+    if dtype == "i8":
+        x = synth.int8_pool(x, fill_unused=float("nan"))
+        want = oracle.decode_i8_ref(x.q.numpy(), x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                    x.block_tables.numpy(), x.context_lens.numpy(), x.scale)
+    else:
+        want = ref_decode(x)
+    g = x.to(device)
+    for part in (-2, 0):
+        out = pa.decode(g.q, g.kv_cache, g.block_tables, g.context_lens, scale=x.scale,
+                        max_context_len=max(lens), partition_size=part, kv_scales=g.kv_scales)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), part
+        assert np.abs(got - want).max() <= TOL, part
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_shared_prefix_full_size_sampled(device, bs):
     """The shared-prefix workload at its full size (64 sequences over one

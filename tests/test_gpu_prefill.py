@@ -107,3 +107,31 @@ def test_llama7b_gqa_chunk_sampled(device):
                                       np.array([0, 1]), x.scale)
             err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
             assert err <= TOL, (s, i, err)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_long_chunk_70b_heads_sampled(device, bs):
+    """A 1536-token chunk at context 3000 and a fresh 700-token prompt, 64 q /
+    8 KV heads (many query blocks per (sequence, KV head)); sampled rows,
+    including the first and last of each chunk, against the oracle."""
+    lens, chunks = [3000, 700], [1536, 700]
+    x = synth.make_decode_inputs(lens, 64, 8, 128, bs, dtype="f16", seed=66 + bs, device=device,
+                                 fill_unused=float("nan"))
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = synth.normal((int(qs[-1]), 64, 128), torch.float16, synth._gen(67, device), device)
+    out = pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=max(chunks))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(bs)
+    for s in range(2):
+        n, T = lens[s], chunks[s]
+        nblk = -(-n // bs)
+        ids = x.block_tables[s, :nblk].long()
+        blocks = x.kv_cache[ids].cpu().numpy()
+        for i in [0, T - 1] + rng.integers(0, T, 4).tolist():
+            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
+                                      np.arange(nblk)[None], np.array([n - T + i + 1]),
+                                      np.array([0, 1]), x.scale)
+            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
+            assert err <= TOL, (s, i, err)

@@ -224,6 +224,27 @@ def test_more_sequences_than_the_balanced_schedule_holds(device, dtype):
         assert np.abs(got - want).max() <= TOL, part
 
 
+def test_one_very_long_context(device):
+    """One sequence of 150,001 tokens, 64 q / 8 KV heads: the whole batch's
+    work sits in one sequence, so balanced slices cut it into many pieces;
+    automatic, single-pass and fixed-partition schedules, every head."""
+    n = 150_001
+    x = synth.make_decode_inputs([n], 64, 8, 128, 16, dtype="f16", seed=23, device=device)
+    nblk = -(-n // 16)
+    blocks = x.kv_cache[x.block_tables[0, :nblk].long()].cpu().numpy()
+    want = oracle.decode_ref(x.q.cpu().numpy(), blocks, np.arange(nblk)[None], np.array([n]),
+                             x.scale)
+    for part in (0, -1, 2048):
+        out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
+                        max_context_len=n, partition_size=part)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), part
+        assert np.abs(got - want).max() <= TOL, part
+    del x, blocks
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_shared_prefix_full_size_sampled(device, bs):
     """The shared-prefix workload at its full size (64 sequences over one

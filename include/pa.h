@@ -197,7 +197,10 @@ int pa_stage_and_write(void* stage_dst, const void* stage_src, int64_t stage_byt
  *                  out == NULL only computes it and returns PA_OK.
  * Supported: dtype f32, f16 or PA_I8; head_dim 64 or 128; block_size 8, 16
  * or 32; G in {1, 2, 4, 8}.  MFMA needs f16 or PA_I8 and G >= 2.  Anything
- * else returns PA_ERR_UNSUPPORTED.
+ * else returns PA_ERR_UNSUPPORTED.  A launch holds at most 2^24 - 1
+ * workgroups: num_seqs * partitions * num_kv_heads (all but the balanced
+ * schedule) and num_seqs * num_q_heads (any split schedule's merge) above
+ * that return PA_ERR_INVALID_ARG, also for a size query.
  * ------------------------------------------------------------------------- */
 int pa_decode(float* out, const void* query, const void* kv_cache,
               const float* kv_scales, const int32_t* block_tables,
@@ -236,6 +239,8 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
  *                  query blocks, so the prefill always uses cached loads)
  * Sequences with T_s > n_s produce no output rows.  Supported: dtype
  * PA_F16; head_dim 64 or 128; block_size 8, 16 or 32; G in {1, 2, 4, 8}.
+ * num_seqs * num_kv_heads * ceil(max_query_len * G / 128) workgroups above
+ * 2^24 - 1 return PA_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 int pa_prefill(float* out, const void* query, const void* kv_cache,
                const int32_t* block_tables, const int32_t* context_lens,

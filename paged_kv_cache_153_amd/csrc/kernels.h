@@ -18,6 +18,9 @@ constexpr int kSchedulePartition = 1;  // ... per (sequence, KV head, partition)
 constexpr int kScheduleBalanced = 2;   // W workgroups, equal tile slices
 // Sequences the balanced schedule handles: its tile prefix lives in LDS.
 constexpr int kBalancedMaxSeqs = 1024;
+// Workgroups one launch may have: a dispatch counts at most 2^32 - 1
+// work-items, and every decode and prefill workgroup has 256.
+constexpr long long kMaxGridWorkgroups = (1LL << 32) / 256 - 1;
 
 struct DecodeArgs {
   float* out;               // [S, Hq, D] final output (single pass)

@@ -482,6 +482,14 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   }
   const pa::Plan plan = pa::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, ctx, part,
                                       cus);
+  // the decode has one workgroup per (sequence, partition, KV head) unless
+  // balanced; a merge after it has one per (sequence, query head)
+  if ((plan.schedule != pa::kScheduleBalanced &&
+       (long long)num_seqs * plan.num_parts * num_kv_heads > pa::kMaxGridWorkgroups) ||
+      (plan.schedule != pa::kScheduleSingle &&
+       (long long)num_seqs * num_q_heads > pa::kMaxGridWorkgroups))
+    return fail(PA_ERR_INVALID_ARG, "grid too large: lower max_context_len or num_seqs, or use "
+                                    "larger partitions");
   if (workspace_needed) *workspace_needed = plan.ws_bytes;
   if (!out) return PA_OK;  // size query
   if (num_seqs == 0) return PA_OK;
@@ -615,7 +623,7 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   const long long cols = (long long)max_query_len * group;
   const int per_wg = pa::prefill_columns_per_workgroup();
   a.qblocks = (int)((cols + per_wg - 1) / per_wg);
-  if ((long long)num_seqs * a.qblocks * num_kv_heads >= (1LL << 31))
+  if ((long long)num_seqs * a.qblocks * num_kv_heads > pa::kMaxGridWorkgroups)
     return fail(PA_ERR_INVALID_ARG, "grid too large");
   a.scale_log2 = scale * 1.4426950408889634f;
   const int rc = pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);

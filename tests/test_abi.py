@@ -90,6 +90,27 @@ def test_decode_reports_null_pointers_and_missing_workspace():
     assert st == -1
 
 
+@pytest.mark.parametrize("kw,fits", [
+    # partitions of 16 tokens over 64: S * 4 * Hkv decode workgroups
+    (dict(S=(1 << 18) - 1, Hq=16, Hkv=16, part=16), True),
+    (dict(S=1 << 18, Hq=16, Hkv=16, part=16), False),
+    # one partition, G = 8: the merge's S * Hq workgroups decide
+    (dict(S=(1 << 21) - 1, Hq=8, Hkv=1, part=64), True),
+    (dict(S=1 << 21, Hq=8, Hkv=1, part=64), False),
+    # single pass: S * Hkv workgroups, no merge
+    (dict(S=1 << 20, Hq=16, Hkv=16, part=-1), False),
+    (dict(S=(1 << 20) - 1, Hq=16, Hkv=16, part=-1), True),
+])
+def test_decode_rejects_grids_beyond_one_launch(kw, fits):
+    # a launch holds at most 2^24 - 1 workgroups of 256 work-items; the size
+    # query already refuses more (the count must not wrap around)
+    need = ctypes.c_size_t(7)
+    st = _decode_status(MB=4, maxlen=64, need=need, **kw)
+    assert st == (0 if fits else -1)
+    if not fits:
+        assert b"grid too large" in pa.lib().pa_last_error()
+
+
 def test_workspace_size_closed_form():
     # split partials: S*Hq*NP rows of D floats, plus m and l, each 256-aligned
     s, hq, d, maxlen, part = 16, 64, 128, 32768, 512
@@ -346,6 +367,15 @@ def _prefill_status(**kw):
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert _prefill_status(**kw) == status
+
+
+def test_prefill_rejects_a_grid_beyond_one_launch():
+    # S * Hkv * ceil(maxq * G / 128) = 2^20 * 8 * 32 workgroups; the call
+    # fails before any launch, so the aligned fake pointers are never read
+    fake = ctypes.c_void_p(1 << 20)
+    st = _prefill_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, qs=fake, S=1 << 20,
+                         total=1 << 20, Hq=8, Hkv=8, maxq=4096)
+    assert st == -1 and b"grid too large" in pa.lib().pa_last_error()
 
 
 def test_prefill_null_pointers_and_empty_batch():

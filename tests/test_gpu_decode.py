@@ -199,13 +199,15 @@ def test_full_size_sampled(device, name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("num_seqs", [1024, 1100])
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
-def test_more_sequences_than_the_balanced_schedule_holds(device, dtype):
-    """1100 sequences (the balanced schedule keeps its tables of at most
-    1024 in LDS): asking for it falls back to fixed partitions; every output
-    against the oracle, for the requested and the automatic schedule."""
+def test_balanced_schedule_sequence_limit(device, dtype, num_seqs):
+    """The balanced schedule keeps a tile prefix of at most 1024 sequences in
+    LDS: 1024 runs it with that table full, 1100 falls back to fixed
+    partitions.  Every output against the oracle, for the requested and the
+    automatic schedule."""
     rng = np.random.default_rng(21)
-    lens = rng.integers(0, 200, 1100).tolist()
+    lens = rng.integers(0, 200, num_seqs).tolist()
     x = synth.make_decode_inputs(lens, 16, 4, 128, 16, dtype="f16", seed=22,
                                  fill_unused=None if dtype == "i8" else float("nan"))
     if dtype == "i8":

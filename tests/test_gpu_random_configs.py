@@ -8,9 +8,11 @@ block size, head_dim, group).  Each case is checked against the fp64 oracle
 (max-abs error <= 5e-4) with every pool row outside the keys a query may
 see poisoned with NaN (for INT8 pools, their scales), so a read outside
 them fails the case.  The draws are seeded: a failing case id names its
-configuration exactly."""
+configuration exactly.  PA_RANDOM_DECODE_CASES / PA_RANDOM_PREFILL_CASES
+raise the number of draws (the defaults keep the suite to seconds)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -23,8 +25,8 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = 5e-4
-DECODE_CASES = 96
-PREFILL_CASES = 32
+DECODE_CASES = int(os.environ.get("PA_RANDOM_DECODE_CASES", 96))
+PREFILL_CASES = int(os.environ.get("PA_RANDOM_PREFILL_CASES", 32))
 HEADS = [(4, 4), (8, 8), (8, 4), (8, 2), (16, 2), (16, 4), (32, 4), (8, 1), (4, 1)]
 
 

@@ -1,0 +1,132 @@
+"""Seeded random block-manager traffic driving the GPU path, step by step.
+
+Each step takes one random operation — admit a sequence with a prompt,
+fork a live sequence, or free one — and then appends one token to a random
+subset of the live sequences.  Both sides replay it: the native block
+manager + pa_cache_write + pa_decode on the GPU, the oracle's block-manager
+model + cache write on the host.  Checked every step: identical block
+lists, slots and copy pairs; bit-identical pools; decode within 5e-4 of
+the oracle over the oracle's pool, and also of attention over each
+sequence's logical history (every K/V row it was given, in order, laid out
+contiguously), which does not depend on where the blocks were placed, on
+sharing, or on copy-on-write."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_153_amd as pa
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-4
+HQ, HKV, D = 8, 2, 128
+NB, STEPS, MAX_LIVE = 400, 40, 16
+
+
+def _contiguous(hist, order, bs):
+    """Pool and tables holding each sequence's history in fresh blocks."""
+    nblk = [-(-len(hist[s]) // bs) for s in order]
+    pool = np.zeros((max(1, sum(nblk)), 2, HKV, bs, D), dtype=np.float16)
+    tables = np.zeros((len(order), max(1, max(nblk))), dtype=np.int64)
+    first = 0
+    for i, s in enumerate(order):
+        for t, (k, v) in enumerate(hist[s]):
+            pool[first + t // bs, 0, :, t % bs] = k
+            pool[first + t // bs, 1, :, t % bs] = v
+        tables[i, :nblk[i]] = np.arange(first, first + nblk[i])
+        first += nblk[i]
+    lens = np.array([len(hist[s]) for s in order], dtype=np.int64)
+    return pool, tables, lens
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_block_manager_traffic(device, seed):
+    bs = [8, 16, 32][seed % 3]
+    kernel = ["valu", "mfma"][seed % 2]
+    print(f"random pipeline seed={seed} bs={bs} kernel={kernel}", flush=True)
+    rng = np.random.default_rng(300 + seed)
+    native, model = pa.BlockManager(NB, bs), oracle.BlockManagerModel(NB, bs)
+    pool0 = synth.normal((NB, 2, HKV, bs, D), torch.float16, synth._gen(10 + seed, "cpu"), "cpu")
+    pool_ref = pool0.numpy().copy()
+    pool_gpu = pool0.to(device)
+    hist, next_id, ops = {}, 0, {"admit": 0, "fork": 0, "free": 0, "cow": 0}
+
+    def write(slots, pairs, k, v):
+        nonlocal pool_ref
+        pool_ref = oracle.cache_write_ref(pool_ref, k.numpy(), v.numpy(),
+                                          np.array(slots, dtype=np.int64), cow_pairs=pairs)
+        pa.cache_write(k.to(device), v.to(device), pool_gpu,
+                       torch.tensor(slots, dtype=torch.int64, device=device),
+                       cow_pairs=(torch.tensor(pairs, dtype=torch.int32, device=device)
+                                  if pairs else None))
+
+    for step in range(STEPS):
+        live = sorted(hist)
+        op = rng.random()
+        if not live or (op < 0.35 and len(live) < MAX_LIVE):       # admit a prompt
+            n = int(rng.integers(1, 3 * bs + 5))
+            blocks = model.allocate(next_id, n)
+            assert native.allocate(next_id, n) == blocks
+            k, v = synth.rows(n, HKV, D, seed=1000 * seed + step)
+            write([blocks[t // bs] * bs + t % bs for t in range(n)], [], k, v)
+            hist[next_id] = [(k[t].numpy(), v[t].numpy()) for t in range(n)]
+            next_id += 1
+            ops["admit"] += 1
+        elif op < 0.6 and len(live) < MAX_LIVE:                    # fork a live sequence
+            parent = live[int(rng.integers(len(live)))]
+            native.fork(parent, next_id)
+            model.fork(parent, next_id)
+            hist[next_id] = list(hist[parent])
+            next_id += 1
+            ops["fork"] += 1
+        elif op < 0.8 and len(live) > 1:                            # free one
+            s = live[int(rng.integers(len(live)))]
+            native.free(s)
+            model.free(s)
+            del hist[s]
+            ops["free"] += 1
+
+        # one new token for a random subset, in a random order
+        live = sorted(hist)
+        batch = [s for s in live if rng.random() < 0.7] or live[:1]
+        batch = [batch[i] for i in rng.permutation(len(batch))]
+        slots_n, pairs_n = native.append_slots(batch)
+        want = [model.append_slot(s) for s in batch]
+        assert slots_n == [w[0] for w in want], step
+        pairs_m = [(w[1], w[2]) for w in want if w[1] >= 0]
+        assert pairs_n == pairs_m, step
+        ops["cow"] += len(pairs_n)
+        k, v = synth.rows(len(batch), HKV, D, seed=5000 + 1000 * seed + step)
+        write(slots_n, pairs_n, k, v)
+        for i, s in enumerate(batch):
+            hist[s].append((k[i].numpy(), v[i].numpy()))
+
+        # decode every live sequence
+        order = sorted(hist)
+        for s in order:
+            t_n, n_n = native.block_table(s)
+            t_m, n_m = model.block_table(s)
+            assert t_n == t_m and n_n == n_m == len(hist[s]), (step, s)
+        mb = max(len(model.block_table(s)[0]) for s in order)
+        rows, lens = native.block_tables(order, mb)
+        bt_m = np.array(rows, dtype=np.int64)
+        cl_m = np.array(lens, dtype=np.int64)
+        q = synth.normal((len(order), HQ, D), torch.float16, synth._gen(7000 + step, "cpu"), "cpu")
+        out = pa.decode(q.to(device), pool_gpu, torch.tensor(rows, dtype=torch.int32).to(device),
+                        torch.tensor(lens, dtype=torch.int32).to(device),
+                        max_context_len=int(cl_m.max()), kernel=kernel)
+        torch.cuda.synchronize()
+        assert np.array_equal(pool_gpu.cpu().numpy().view(np.uint16),
+                              pool_ref.view(np.uint16)), step
+        got = out.cpu().numpy().astype(np.float64)
+        want_pool = oracle.decode_ref(q.numpy(), pool_ref, bt_m, cl_m, D ** -0.5)
+        assert np.abs(got - want_pool).max() <= TOL, step
+        c_pool, c_tables, c_lens = _contiguous(hist, order, bs)
+        want_hist = oracle.decode_ref(q.numpy(), c_pool, c_tables, c_lens, D ** -0.5)
+        assert np.abs(got - want_hist).max() <= TOL, step
+    print(f"  ops {ops}, live at end {len(hist)}", flush=True)
+    assert ops["fork"] and ops["free"] and ops["cow"]   # the traffic exercised sharing
+    native.close()

@@ -9,7 +9,9 @@ lists, slots and copy pairs; bit-identical pools; decode within 5e-4 of
 the oracle over the oracle's pool, and also of attention over each
 sequence's logical history (every K/V row it was given, in order, laid out
 contiguously), which does not depend on where the blocks were placed, on
-sharing, or on copy-on-write."""
+sharing, or on copy-on-write.  Over an INT8 pool the copies move codes
+and scales together and the history holds each row as the oracle quantises
+it (code times scale)."""
 
 import numpy as np
 import pytest
@@ -29,7 +31,7 @@ NB, STEPS, MAX_LIVE = 400, 40, 16
 def _contiguous(hist, order, bs):
     """Pool and tables holding each sequence's history in fresh blocks."""
     nblk = [-(-len(hist[s]) // bs) for s in order]
-    pool = np.zeros((max(1, sum(nblk)), 2, HKV, bs, D), dtype=np.float16)
+    pool = np.zeros((max(1, sum(nblk)), 2, HKV, bs, D), dtype=np.float64)
     tables = np.zeros((len(order), max(1, max(nblk))), dtype=np.int64)
     first = 0
     for i, s in enumerate(order):
@@ -42,26 +44,48 @@ def _contiguous(hist, order, bs):
     return pool, tables, lens
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_random_block_manager_traffic(device, seed):
+def _history_rows(k, v, int8):
+    """Rows as the pool holds them: the f16 values, or code * scale."""
+    if not int8:
+        return [(k[t].numpy(), v[t].numpy()) for t in range(k.shape[0])]
+    kd = oracle.dequantize_ref(*oracle.quantize_rows_ref(k.numpy()))
+    vd = oracle.dequantize_ref(*oracle.quantize_rows_ref(v.numpy()))
+    return [(kd[t], vd[t]) for t in range(k.shape[0])]
+
+
+@pytest.mark.parametrize("seed,dtype", [(s, "f16") for s in range(6)] +
+                         [(s, "i8") for s in range(6, 10)])
+def test_random_block_manager_traffic(device, seed, dtype):
     bs = [8, 16, 32][seed % 3]
     kernel = ["valu", "mfma"][seed % 2]
-    print(f"random pipeline seed={seed} bs={bs} kernel={kernel}", flush=True)
+    int8 = dtype == "i8"
+    print(f"random pipeline seed={seed} bs={bs} kernel={kernel} {dtype}", flush=True)
     rng = np.random.default_rng(300 + seed)
     native, model = pa.BlockManager(NB, bs), oracle.BlockManagerModel(NB, bs)
-    pool0 = synth.normal((NB, 2, HKV, bs, D), torch.float16, synth._gen(10 + seed, "cpu"), "cpu")
-    pool_ref = pool0.numpy().copy()
-    pool_gpu = pool0.to(device)
+    g = synth._gen(10 + seed, "cpu")
+    if int8:
+        codes0 = torch.randint(-127, 128, (NB, 2, HKV, bs, D), generator=g, dtype=torch.int8)
+        scales0 = torch.rand((NB, HKV, 2, bs), generator=g) * 0.02 + 0.01
+        pool_ref = (codes0.numpy().copy(), scales0.numpy().copy())
+        pool_gpu, scales_gpu = codes0.to(device), scales0.to(device)
+    else:
+        pool0 = synth.normal((NB, 2, HKV, bs, D), torch.float16, g, "cpu")
+        pool_ref = pool0.numpy().copy()
+        pool_gpu, scales_gpu = pool0.to(device), None
     hist, next_id, ops = {}, 0, {"admit": 0, "fork": 0, "free": 0, "cow": 0}
 
     def write(slots, pairs, k, v):
         nonlocal pool_ref
-        pool_ref = oracle.cache_write_ref(pool_ref, k.numpy(), v.numpy(),
-                                          np.array(slots, dtype=np.int64), cow_pairs=pairs)
+        sl = np.array(slots, dtype=np.int64)
+        if int8:
+            pool_ref = oracle.cache_write_i8_ref(pool_ref[0], pool_ref[1], k.numpy(), v.numpy(),
+                                                 sl, cow_pairs=pairs)
+        else:
+            pool_ref = oracle.cache_write_ref(pool_ref, k.numpy(), v.numpy(), sl, cow_pairs=pairs)
         pa.cache_write(k.to(device), v.to(device), pool_gpu,
                        torch.tensor(slots, dtype=torch.int64, device=device),
                        cow_pairs=(torch.tensor(pairs, dtype=torch.int32, device=device)
-                                  if pairs else None))
+                                  if pairs else None), kv_scales=scales_gpu)
 
     for step in range(STEPS):
         live = sorted(hist)
@@ -72,7 +96,7 @@ def test_random_block_manager_traffic(device, seed):
             assert native.allocate(next_id, n) == blocks
             k, v = synth.rows(n, HKV, D, seed=1000 * seed + step)
             write([blocks[t // bs] * bs + t % bs for t in range(n)], [], k, v)
-            hist[next_id] = [(k[t].numpy(), v[t].numpy()) for t in range(n)]
+            hist[next_id] = _history_rows(k, v, int8)
             next_id += 1
             ops["admit"] += 1
         elif op < 0.6 and len(live) < MAX_LIVE:                    # fork a live sequence
@@ -101,8 +125,8 @@ def test_random_block_manager_traffic(device, seed):
         ops["cow"] += len(pairs_n)
         k, v = synth.rows(len(batch), HKV, D, seed=5000 + 1000 * seed + step)
         write(slots_n, pairs_n, k, v)
-        for i, s in enumerate(batch):
-            hist[s].append((k[i].numpy(), v[i].numpy()))
+        for s, row in zip(batch, _history_rows(k, v, int8)):
+            hist[s].append(row)
 
         # decode every live sequence
         order = sorted(hist)
@@ -117,12 +141,19 @@ def test_random_block_manager_traffic(device, seed):
         q = synth.normal((len(order), HQ, D), torch.float16, synth._gen(7000 + step, "cpu"), "cpu")
         out = pa.decode(q.to(device), pool_gpu, torch.tensor(rows, dtype=torch.int32).to(device),
                         torch.tensor(lens, dtype=torch.int32).to(device),
-                        max_context_len=int(cl_m.max()), kernel=kernel)
+                        max_context_len=int(cl_m.max()), kernel=kernel, kv_scales=scales_gpu)
         torch.cuda.synchronize()
-        assert np.array_equal(pool_gpu.cpu().numpy().view(np.uint16),
-                              pool_ref.view(np.uint16)), step
         got = out.cpu().numpy().astype(np.float64)
-        want_pool = oracle.decode_ref(q.numpy(), pool_ref, bt_m, cl_m, D ** -0.5)
+        if int8:
+            assert np.array_equal(pool_gpu.cpu().numpy(), pool_ref[0]), step
+            assert np.array_equal(scales_gpu.cpu().numpy().view(np.uint32),
+                                  pool_ref[1].view(np.uint32)), step
+            want_pool = oracle.decode_i8_ref(q.numpy(), pool_ref[0], pool_ref[1], bt_m, cl_m,
+                                             D ** -0.5)
+        else:
+            assert np.array_equal(pool_gpu.cpu().numpy().view(np.uint16),
+                                  pool_ref.view(np.uint16)), step
+            want_pool = oracle.decode_ref(q.numpy(), pool_ref, bt_m, cl_m, D ** -0.5)
         assert np.abs(got - want_pool).max() <= TOL, step
         c_pool, c_tables, c_lens = _contiguous(hist, order, bs)
         want_hist = oracle.decode_ref(q.numpy(), c_pool, c_tables, c_lens, D ** -0.5)

@@ -13,6 +13,8 @@ sharing, or on copy-on-write.  Over an INT8 pool the copies move codes
 and scales together and the history holds each row as the oracle quantises
 it (code times scale)."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -53,8 +55,14 @@ def _history_rows(k, v, int8):
     return [(kd[t], vd[t]) for t in range(k.shape[0])]
 
 
-@pytest.mark.parametrize("seed,dtype", [(s, "f16") for s in range(6)] +
-                         [(s, "i8") for s in range(6, 10)])
+def _cases():
+    """Seeds 0-5 over f16 pools, 6-9 over INT8; PA_RANDOM_PIPELINE_SEEDS = N
+    adds seeds 10 .. N-1, odd ones INT8."""
+    n = int(os.environ.get("PA_RANDOM_PIPELINE_SEEDS", 10))
+    return [(s, "f16" if s < 6 or (s >= 10 and s % 2 == 0) else "i8") for s in range(n)]
+
+
+@pytest.mark.parametrize("seed,dtype", _cases())
 def test_random_block_manager_traffic(device, seed, dtype):
     bs = [8, 16, 32][seed % 3]
     kernel = ["valu", "mfma"][seed % 2]

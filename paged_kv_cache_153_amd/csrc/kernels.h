@@ -58,6 +58,7 @@ struct PrefillArgs {
   const int32_t* qstart;    // [S + 1] first query row of each sequence
   int64_t num_blocks;
   int num_seqs;
+  int total_queries;        // rows of q and out: query_start entries are bounded by it
   int num_q_heads;
   int num_kv_heads;
   int max_blocks;

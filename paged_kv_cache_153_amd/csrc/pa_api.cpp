@@ -616,6 +616,7 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   a.qstart = query_start;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
+  a.total_queries = total_queries;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;

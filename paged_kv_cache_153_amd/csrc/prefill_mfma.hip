@@ -114,12 +114,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   lid /= (unsigned)a.qblocks;
   const int g = (int)(lid % (unsigned)a.num_kv_heads);
   const int s = (int)(lid / (unsigned)a.num_kv_heads);
+  // query rows [q0, q1) of this sequence: a chunk that is empty, runs
+  // backwards or leaves [0, total_queries) has no rows, so a bad query_start
+  // entry can never address q or out outside their buffers
   const int q0 = a.qstart[s];
-  const int T = a.qstart[s + 1] - q0;
+  const int q1 = a.qstart[s + 1];
+  if (q0 < 0 || q1 <= q0 || q1 > a.total_queries) return;  // the whole workgroup
+  const int T = q1 - q0;
   int n = a.cl[s];
   n = n < 0 ? 0 : (n > a.max_tokens ? a.max_tokens : n);
   const int wg_tok0 = qb * (COLS_WG / G);
-  if (T <= 0 || T > n || wg_tok0 >= T) return;  // the whole workgroup
+  if (T > n || wg_tok0 >= T) return;
   const int wg_last = min(T - 1, wg_tok0 + COLS_WG / G - 1);
   const int nsteps = (n - T + wg_last) / kKeys + 1;
 

@@ -11,6 +11,7 @@ import torch
 import oracle
 import paged_kv_cache_153_amd as pa
 import synth
+from tests.full_oracle import assert_every_row
 
 pytestmark = pytest.mark.gpu
 
@@ -164,37 +165,21 @@ def test_shared_prefix_shape_small(device, bs):
 
 
 # --------------------------------------------------------------------------
-# full workload sizes, default (benchmarked) launch, sampled outputs
+# full workload sizes, the benchmarked launch, every output row
 # --------------------------------------------------------------------------
-def _sampled_check(x_dev, out, samples):
-    """Oracle one (sequence, head) at a time on the host copy of that
-    sequence's blocks only."""
-    bs = x_dev.block_size
-    for s, h in samples:
-        n = int(x_dev.context_lens[s])
-        nblk = -(-n // bs)
-        ids = x_dev.block_tables[s, :nblk].long()
-        blocks = x_dev.kv_cache[ids].cpu().numpy()
-        q = x_dev.q[s:s + 1].cpu().numpy()
-        want = oracle.decode_ref(q, blocks, np.arange(nblk)[None], np.array([n]), x_dev.scale)
-        got = out[s, h].cpu().numpy().astype(np.float64)
-        err = np.abs(got - want[0, h]).max()
-        assert err <= TOL, (s, h, err)
-
-
-@pytest.mark.parametrize("name", ["llama7b_mha", "gqa7b", "llama70b"])
-def test_full_size_sampled(device, name):
-    print(f"full-size {name}", flush=True)
+@pytest.mark.parametrize("name,part", [("llama7b_mha", 0), ("gqa7b", 0), ("llama70b", 0),
+                                       ("llama70b", 512)])
+def test_full_size_every_row(device, name, part):
+    """The full 7B, GQA and 70B layers in the launch the benchmark times
+    (automatic schedule), and the 70B layer also as 512-token partitions
+    (64 per sequence) plus the log-sum-exp merge; every (sequence, head)
+    against the oracle."""
+    print(f"full-size {name} partition {part}", flush=True)
     x = synth.WORKLOADS[name](seed=0, device=device)
     out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
-                    max_context_len=int(x.context_lens.max()))
+                    max_context_len=int(x.context_lens.max()), partition_size=part)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    S, Hq = x.num_seqs, x.num_q_heads
-    rng = np.random.default_rng(0)
-    samples = [(0, 0), (S - 1, Hq - 1)] + [(int(rng.integers(S)), int(rng.integers(Hq)))
-                                           for _ in range(4)]
-    _sampled_check(x, out, samples)
+    assert_every_row(x, out, TOL)
     del x, out
     torch.cuda.empty_cache()
 
@@ -248,22 +233,17 @@ def test_one_very_long_context(device):
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
-def test_shared_prefix_full_size_sampled(device, bs):
+def test_shared_prefix_full_size_every_row(device, bs):
     """The shared-prefix workload at its full size (64 sequences over one
     512-token prefix, private suffixes U[1, 2048]) in the launch the
     benchmark uses for it: cached K/V loads, schedule chosen by the
-    library; sampled (sequence, head) pairs against the oracle."""
+    library; every (sequence, head) against the oracle."""
     print(f"full-size shared prefix bs={bs}", flush=True)
     x = synth.shared_prefix(seed=0, block_size=bs, device=device)
     out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
                     max_context_len=int(x.context_lens.max()), cached_kv=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    S, Hq = x.num_seqs, x.num_q_heads
-    rng = np.random.default_rng(bs)
-    samples = [(0, 0), (S - 1, Hq - 1)] + [(int(rng.integers(S)), int(rng.integers(Hq)))
-                                           for _ in range(4)]
-    _sampled_check(x, out, samples)
+    assert_every_row(x, out, TOL)
     del x, out
     torch.cuda.empty_cache()
 

@@ -135,3 +135,121 @@ def test_long_chunk_70b_heads_sampled(device, bs):
                                       np.array([0, 1]), x.scale)
             err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
             assert err <= TOL, (s, i, err)
+
+
+def test_query_start_outside_total_stays_inside_buffers(device, monkeypatch):
+    """query_start entries that leave [0, total_queries), run backwards or
+    go negative give their sequence no rows; the rows of the valid
+    sequences still match the oracle.  q and out are views into larger
+    buffers filled with a sentinel, so even a kernel that trusted the bad
+    entries would stay inside the allocations, and the guard rows show
+    whether it wrote there."""
+    monkeypatch.delenv("PA_CHECK", raising=False)      # no host-side validation
+    hq, hkv, d, bs = 8, 2, 64, 16
+    lens = [40, 30, 50, 20, 25, 30]
+    x, _, _ = make(lens, [1] * len(lens), hq, hkv, d, bs, seed=68)
+    total = 14
+    # sequences 0 and 1 are valid; 2 runs past total, 3 runs backwards, 4
+    # ends past total, 5 starts below 0
+    qs = np.array([0, 8, 14, 24, 20, 28, 2], np.int32)
+    qs_bad = qs.copy()
+    qs_bad[5] = -4                     # sequence 4: [20, -4); sequence 5: [-4, 2)
+    guard = 8                          # rows before the views: covers q0 = -4
+    rows = guard + 32
+    q_big = synth.normal((rows, hq, d), torch.float16, synth._gen(69, "cpu"), "cpu")
+    q_dev = q_big.to(device)
+    out_big = torch.full((rows, hq, d), 1234.5, dtype=torch.float32, device=device)
+    q_view, out_view = q_dev[guard:guard + total], out_big[guard:guard + total]
+    g = x.to(device)
+    for entries in (qs, qs_bad):
+        out_big.fill_(1234.5)
+        pa.prefill(q_view, g.kv_cache, g.block_tables, g.context_lens,
+                   torch.from_numpy(entries).to(device), scale=x.scale, max_query_len=10,
+                   out=out_view)
+        torch.cuda.synchronize()
+        got = out_big.cpu().numpy()
+        assert np.all(got[:guard] == 1234.5) and np.all(got[guard + total:] == 1234.5)
+        sub = synth.DecodeInputs("valid", x.q[:2], x.kv_cache, x.block_tables[:2],
+                                 x.context_lens[:2], x.scale, 0)
+        want = ref(sub, q_big[guard:guard + total], np.array([0, 8, 14], np.int32))
+        assert np.abs(got[guard:guard + total].astype(np.float64) - want).max() <= TOL
+
+
+# --------------------------------------------------------------------------
+# peaked scores: the softmax reference must move after the first step
+# --------------------------------------------------------------------------
+KEYS_PER_STEP = 32       # the kernel's key step; its reference moves only
+SLACK_LOG2 = 8.0         # when a score passes it by more than 2^8
+
+
+def _late_jumps(x, q, qstart):
+    """Count (query row, head) columns whose score, in log2 units, rises more
+    than 8 above the largest score of the first 32 keys at some later key
+    the column sees: each forces the kernel to rescale an accumulator that
+    already holds weight (computed from the inputs alone, in float64)."""
+    from oracle.attention import gather_sequence
+    bt, cl = x.block_tables.numpy(), x.context_lens.numpy()
+    hq, hkv = q.shape[1], x.kv_cache.shape[2]
+    G = hq // hkv
+    jumps = 0
+    for s in range(len(cl)):
+        n, q0, q1 = int(cl[s]), int(qstart[s]), int(qstart[s + 1])
+        T = q1 - q0
+        if T == 0:
+            continue
+        k, _ = gather_sequence(x.kv_cache.numpy(), bt[s], n)
+        k = k.astype(np.float64)
+        for i in range(T):
+            p = n - T + i
+            if p < KEYS_PER_STEP:
+                continue
+            for h in range(hq):
+                z = (k[:p + 1, h // G, :] @ q[q0 + i, h].double().numpy()) * x.scale / np.log(2)
+                if z[KEYS_PER_STEP:].max() > z[:KEYS_PER_STEP].max() + SLACK_LOG2:
+                    jumps += 1
+    return jumps
+
+
+def _ramp_keys(x, factor):
+    """Scale K row t of every sequence by 1 + factor * t / n (in float32,
+    rounded back to float16): later keys get ever larger scores, so the
+    reference moves again and again."""
+    bs = x.block_size
+    kv = x.kv_cache.float()
+    for s, n in enumerate(x.context_lens.tolist()):
+        for t in range(n):
+            b = int(x.block_tables[s, t // bs])
+            kv[b, 0, :, t % bs] *= 1.0 + factor * t / n
+    x.kv_cache.copy_(kv.to(x.kv_cache.dtype))
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 4), (32, 4)])
+@pytest.mark.parametrize("kind", ["scale1_std3", "ramp"])
+def test_peaked_scores_move_the_reference(device, bs, hq, hkv, kind):
+    """Scores far above the first step's (scale 1 with N(0, 3^2) values, or
+    keys whose norm grows along the context) make the kernel move its
+    softmax reference while earlier keys' weights are in the accumulators;
+    the rescale must keep every row equal to the oracle."""
+    lens = [300, 97, 700, 64]
+    chunks = [300, 40, 129, 33]          # a fresh prompt, short and long pasts
+    d = 64 if hq == 8 else 128
+    if kind == "scale1_std3":
+        x = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype="f16", seed=bs + hq,
+                                     std=3.0, scale=1.0, fill_unused=float("nan"))
+        g = synth._gen(bs + hq + 50, "cpu")
+        q = synth.normal((sum(chunks), hq, d), torch.float16, g, "cpu", 3.0)
+    else:
+        x = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype="f16", seed=bs + hq,
+                                     fill_unused=float("nan"))
+        _ramp_keys(x, 20.0)
+        g = synth._gen(bs + hq + 50, "cpu")
+        q = synth.normal((sum(chunks), hq, d), torch.float16, g, "cpu")
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    jumps = _late_jumps(x, q, qs)
+    print(f"  peaked {kind} bs={bs} {hq}/{hkv}: {jumps} late jumps", flush=True)
+    assert jumps >= 100                  # the inputs do force live rescales
+    want = ref(x, q, qs)
+    got = run(x, q, qs, device)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL

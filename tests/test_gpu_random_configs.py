@@ -4,7 +4,8 @@ group (MHA to MQA), a length mix with empty, one-token and block-boundary
 contexts, sliding window, schedule (auto, single pass, balanced, fixed
 partitions), kernel family, load policy, table width and the host bound on
 the lengths — and random causal prefill chunks (chunk lengths, pasts,
-block size, head_dim, group).  Each case is checked against the fp64 oracle
+block size, head_dim, group, value spread and softmax scale, so that peaked
+scores move the kernel's softmax reference mid-context).  Each case is checked against the fp64 oracle
 (max-abs error <= 5e-4) with every pool row outside the keys a query may
 see poisoned with NaN (for INT8 pools, their scales), so a read outside
 them fails the case.  The draws are seeded: a failing case id names its
@@ -148,6 +149,11 @@ def draw_prefill(case):
         chunks[0] = 1
         lens[0] = max(lens[0], 1)
     cfg["chunks"], cfg["lens"] = chunks, lens
+    # peaked scores too (scale 1, wide values): the kernel's softmax
+    # reference then moves with weight already accumulated
+    cfg["scale"] = None if rng.random() < 0.6 else float([1.0, rng.uniform(0.01, 0.3)][
+        rng.integers(0, 2)])
+    cfg["std"] = float([1.0, 0.5, 2.0, 3.0][rng.integers(0, 4)])
     return cfg
 
 
@@ -156,11 +162,12 @@ def test_random_prefill_config(device, case):
     cfg = draw_prefill(case)
     print(f"  prefill case {case}: {cfg}", flush=True)
     x = synth.make_decode_inputs(cfg["lens"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["bs"],
-                                 dtype="f16", seed=7000 + case, fill_unused=float("nan"))
+                                 dtype="f16", seed=7000 + case, std=cfg["std"],
+                                 scale=cfg["scale"], fill_unused=float("nan"))
     qstart = np.concatenate([[0], np.cumsum(cfg["chunks"])]).astype(np.int32)
     total = int(qstart[-1])
     q = synth.normal((total, cfg["hq"], cfg["d"]), torch.float16, synth._gen(7100 + case, "cpu"),
-                     "cpu")
+                     "cpu", cfg["std"])
     want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
                               x.context_lens.numpy(), qstart, x.scale)
     out = pa.prefill(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),

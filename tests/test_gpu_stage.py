@@ -2,12 +2,15 @@
 bookkeeping ([KVPA] §5.3: block tables are copied to the GPU for each
 attention call): the device copy is bit-exact for every size class, and two
 pinned buffers used alternately (as the decode step does) never hand back a
-stale copy."""
+stale copy.  pa_stage_and_write, the fused upload + cache write the
+benchmark step runs, leaves the pool (and INT8 scales) bit-exact against the
+oracle's cache write, with and without copy-on-write pairs."""
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_153_amd as pa
 
 pytestmark = pytest.mark.gpu
@@ -90,6 +93,61 @@ def test_stage_and_write_equals_the_two_calls(device, dtype, with_cow):
     assert torch.equal(g1.kv_cache, g2.kv_cache)
     if dtype == "i8":
         assert torch.equal(g1.kv_scales.view(torch.int32), g2.kv_scales.view(torch.int32))
+    # and both against the oracle's write of the same rows, slots and pairs
+    _assert_pool_is_oracle_write(x, k.cpu(), v.cpu(), slots, cow, g2)
+
+
+def _assert_pool_is_oracle_write(x, k, v, slots, cow, g):
+    """The device pool (and INT8 scales) of ``g`` equals, bit for bit, the
+    oracle's cache write applied to the host pool of ``x``."""
+    pairs = [] if cow is None else [tuple(p) for p in cow.tolist()]
+    if x.kv_scales is None:
+        want = oracle.cache_write_ref(x.kv_cache.numpy(), k.numpy(), v.numpy(),
+                                      slots.numpy(), pairs)
+        assert np.array_equal(g.kv_cache.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    else:
+        codes, scales = oracle.cache_write_i8_ref(x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                                  k.numpy(), v.numpy(), slots.numpy(), pairs)
+        assert np.array_equal(g.kv_cache.cpu().numpy(), codes)
+        assert np.array_equal(g.kv_scales.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_stage_and_write_bench_step_against_oracle(device, dtype):
+    """The fused call at the shape of one benchmark decode step of the
+    shared-prefix workload (64 sequences, 8 KV heads x 128, block 16): each
+    sequence's next slot from the native block manager, one copy-on-write of
+    a forked sequence's shared partial block, the slots and pairs read from
+    the pinned pack; pool (and scales) bit-exact against the oracle."""
+    import synth
+    S, hkv, d, bs = 64, 8, 128, 16
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 600, S - 1).tolist()
+    need = sum(-(-(n + 1) // bs) for n in lens) + 4
+    bm = pa.BlockManager(need, bs)
+    for s_, n in enumerate(lens):
+        bm.allocate(s_, n)
+    parent = next(s_ for s_, n in enumerate(lens) if n % bs)
+    bm.fork(parent, S - 1)                          # its append copies the shared block
+    x = synth.make_decode_inputs([16] * 2, 8, hkv, d, bs, dtype="f16", seed=32,
+                                 num_blocks=need)
+    if dtype == "i8":
+        x = synth.int8_pool(x, seed=33)
+    k, v = synth.rows(S, hkv, d, dtype="f16", seed=34)
+    pack = torch.zeros(2 * S + 2 * S + 128, dtype=torch.int32).pin_memory()
+    slots = pack[0:2 * S].view(torch.int64)
+    pairs = pack[2 * S:4 * S].view(S, 2)
+    ncow = bm.append_slots_into(torch.arange(S, dtype=torch.int64), slots, pairs)
+    assert ncow == 1
+    pack[4 * S:].copy_(torch.arange(128, dtype=torch.int32))
+    g = x.to(device)
+    dst = torch.zeros(pack.numel(), dtype=torch.int32, device=device)
+    pa.stage_and_write(dst, pack, k.to(device), v.to(device), g.kv_cache, slots,
+                       cow_pairs=pairs[:ncow], kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), pack)
+    _assert_pool_is_oracle_write(x, k, v, slots, pairs[:ncow], g)
+    bm.close()
 
 
 def test_stage_and_write_refuses_slots_inside_the_destination(device):

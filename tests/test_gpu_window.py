@@ -11,6 +11,7 @@ import torch
 import oracle
 import paged_kv_cache_153_amd as pa
 import synth
+from tests.full_oracle import assert_every_row
 
 pytestmark = pytest.mark.gpu
 
@@ -114,30 +115,14 @@ def test_window_at_least_context_equals_full_attention(device):
 
 
 @pytest.mark.parametrize("window", [4096, 1000])
-def test_window_full_size_llama70b_sampled(device, window):
-    """64 query / 8 KV heads, 16 x 32768 tokens, default launch; the oracle
-    takes sampled (sequence, head) pairs over the window's blocks only."""
+def test_window_full_size_llama70b_every_row(device, window):
+    """64 query / 8 KV heads, 16 x 32768 tokens, default launch; every
+    (sequence, head) against the oracle over the window's blocks."""
     print(f"full-size llama70b W={window}", flush=True)
     x = synth.llama70b(seed=0, device=device)
     out = pa.decode(x.q, x.kv_cache, x.block_tables, x.context_lens, scale=x.scale,
                     max_context_len=int(x.context_lens.max()), sliding_window=window)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    bs = x.block_size
-    rng = np.random.default_rng(1)
-    S, Hq = x.num_seqs, x.num_q_heads
-    samples = [(0, 0), (S - 1, Hq - 1)] + [(int(rng.integers(S)), int(rng.integers(Hq)))
-                                           for _ in range(4)]
-    for s, h in samples:
-        n = int(x.context_lens[s])
-        lo_blk = max(0, n - window) // bs
-        nblk = -(-n // bs) - lo_blk
-        ids = x.block_tables[s, lo_blk:lo_blk + nblk].long()
-        blocks = x.kv_cache[ids].cpu().numpy()
-        # the same window relative to the copied blocks: n' = n - lo_blk * bs
-        want = oracle.decode_ref(x.q[s:s + 1].cpu().numpy(), blocks, np.arange(nblk)[None],
-                                 np.array([n - lo_blk * bs]), x.scale, window=window)
-        err = np.abs(out[s, h].cpu().numpy().astype(np.float64) - want[0, h]).max()
-        assert err <= TOL, (s, h, err)
+    assert_every_row(x, out, TOL, window=window)
     del x, out
     torch.cuda.empty_cache()

@@ -19,8 +19,9 @@
  *     ABI.  pa_strerror() names a status; pa_last_error() gives the detail of
  *     the last failure on the calling thread.
  *   - Device pointers are raw HIP device addresses owned by the caller; the
- *     library never allocates, frees or retains device memory.  Host pointers
- *     are only read or written during the call.
+ *     library never allocates, frees or retains device memory, save the one
+ *     fixed array per GPU that pa_decode_static (2a) uses in place of a
+ *     workspace.  Host pointers are only read or written during the call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued on it and the call returns without waiting; a
  *     device-side fault surfaces at the caller's next synchronisation.
@@ -210,6 +211,31 @@ int pa_decode(float* out, const void* query, const void* kv_cache,
               int partition_size, int kernel, void* workspace,
               size_t workspace_bytes, size_t* workspace_needed, int dtype,
               void* stream);
+
+/* -------------------------------------------------------------------------
+ * 2a. Decode without a caller workspace — for callers that cannot allocate
+ *     device memory: code under stream capture, tight serving loops,
+ *     harnesses that forbid hipMalloc.
+ *
+ * pa_decode with the same arguments but the workspace ones, the same
+ * kernels and the same results (bit for bit, for the same schedule).  The
+ * split-context partials go to a device array of
+ * pa_decode_static_capacity() bytes (64 MiB) that the library holds on each
+ * GPU it runs on until the process ends; the call allocates and frees no
+ * memory.  A call whose partials need more returns PA_ERR_WORKSPACE before
+ * anything is enqueued; out == NULL only checks whether the call fits.  All
+ * calls on one GPU share that array: calls that overlap on a GPU (on other
+ * streams, or from other host threads without ordering) race; calls on one
+ * stream are ordered.  The array needs no clearing between calls.
+ * ------------------------------------------------------------------------- */
+int pa_decode_static(float* out, const void* query, const void* kv_cache,
+                     const float* kv_scales, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size,
+                     int max_blocks_per_seq, int max_context_len, int64_t num_blocks,
+                     float scale, int sliding_window, int partition_size, int kernel,
+                     int dtype, void* stream);
+size_t pa_decode_static_capacity(void);
 
 /* -------------------------------------------------------------------------
  * 2b. Multi-token queries: causal attention of a prefill chunk ([KV2P] §5.4

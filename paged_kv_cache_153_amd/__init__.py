@@ -58,6 +58,10 @@ _SIGNATURES = {
                              _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float, _c.c_int,
                              _c.c_int, _c.c_int, _P, _c.c_size_t, _c.POINTER(_c.c_size_t),
                              _c.c_int, _P]),
+    "pa_decode_static": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int,
+                                    _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64,
+                                    _c.c_float, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P]),
+    "pa_decode_static_capacity": (_c.c_size_t, []),
     "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
                               _c.c_int, _c.c_int, _P]),
@@ -318,6 +322,45 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
                            KERNELS[kernel] | (KV_CACHED if cached_kv else 0),
                            None if workspace is None else workspace.data_ptr(),
                            wbytes, None, dt, _stream(query.device, stream)))
+    return out
+
+
+def decode_static(out, query, kv_cache, block_tables, context_lens, scale=None,
+                  max_context_len=None, partition_size=0, kernel="auto", stream=None,
+                  cached_kv=False, sliding_window=0, kv_scales=None):
+    """``decode`` for callers that cannot allocate device memory: the caller
+    passes ``out`` [S, Hq, D] float32, and the split-context partials go to
+    the library's own per-GPU array (``pa_decode_static``; raises with
+    PA_ERR_WORKSPACE when they need more than its
+    ``pa_decode_static_capacity()`` bytes).  Calls that overlap on one GPU
+    share that array and race."""
+    torch = _torch()
+    _need_cuda(out, query, kv_cache, block_tables, context_lens)
+    nb, two, hkv, bs, d = kv_cache.shape
+    s, hq, dq = query.shape
+    if two != 2 or dq != d:
+        raise ValueError("query/kv_cache shape mismatch")
+    q_dtype = torch.float16 if kv_cache.dtype == torch.int8 else kv_cache.dtype
+    if query.dtype != q_dtype:
+        raise TypeError("query must have the pool's dtype (float16 for an int8 pool)")
+    sp = _scales_ptr(kv_cache, kv_scales)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise TypeError("block_tables must be int32 [S, MB]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (s,):
+        raise TypeError("context_lens must be int32 [S]")
+    if out.dtype != torch.float32 or out.shape != (s, hq, d):
+        raise TypeError("out must be float32 [S, Hq, D]")
+    mb = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = mb * bs
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib().pa_decode_static(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(), sp,
+                                  block_tables.data_ptr(), context_lens.data_ptr(), s, hq, hkv, d,
+                                  bs, mb, int(max_context_len), nb, float(scale),
+                                  int(sliding_window), int(partition_size),
+                                  KERNELS[kernel] | (KV_CACHED if cached_kv else 0),
+                                  _dtype_code(kv_cache), _stream(query.device, stream)))
     return out
 
 

@@ -19,7 +19,12 @@ Printed: one JSON line.  ``value`` is the whole-step KV-read throughput
 (algorithmic K+V bytes the decode reads / wall time per step); ``roofline``
 is the decode call alone (HIP events on its stream) against the 8 TB/s HBM
 peak; ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of
-the same step on this host.
+the same step on this host; ``cache_write_us`` is the upload + cache write
+(+ copy-on-write) launch timed on its own in further steps.  The default
+run (the 7B layer) adds ``workloads``: one compact record for each other
+workload of the benchmark set (GQA, 70B with automatic and 512-token
+partitions, shared prefix at block 8/16/32, tiny), the INT8 pools and a
+GQA prefill chunk.
 """
 
 from __future__ import annotations
@@ -125,38 +130,64 @@ class StepEvent:
             b.release()
 
 
-def source_fingerprint():
-    """sha256 (first 16 hex) over the device sources and the dispatch code, in
+# Sources each kernel's code and launch depend on (csrc/): a committed
+# counter profile stays valid while these files hash to its fingerprint.
+_DECODE_COMMON = ["decode_epilogue.h", "decode_schedule.h", "device_common.h", "kernels.h",
+                  "merge.hip", "pa_api.cpp"]
+KERNEL_SOURCES = {
+    "decode_valu": ["decode_valu.hip"] + _DECODE_COMMON,
+    "decode_mfma": ["decode_mfma.hip"] + _DECODE_COMMON,
+    "decode_valu_i8": ["decode_valu_i8.hip"] + _DECODE_COMMON,
+    "decode_mfma_i8": ["decode_mfma_i8.hip"] + _DECODE_COMMON,
+    "prefill_mfma": ["prefill_mfma.hip", "device_common.h", "kernels.h", "pa_api.cpp"],
+}
+
+
+def source_fingerprint(files):
+    """sha256 (first 16 hex) over the named csrc/ files, concatenated in
     name order: the key under which measured counter figures stay valid."""
-    import glob
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_153_amd", "csrc")
-    files = sorted(f for f in glob.glob(os.path.join(csrc, "*"))
-                   if f.endswith((".hip", ".h")) or f.endswith("pa_api.cpp"))
     h = hashlib.sha256()
-    for f in files:
-        with open(f, "rb") as fh:
+    for f in sorted(files):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, mode="decode"):
-    """HBM bytes per decode (or prefill) dispatch from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when
-    there is none for this workload or the kernels changed since it was
-    taken."""
-    import glob
-    pattern = f"decode_*_{workload}.md" if mode == "decode" else f"prefill_*_prefill_{workload}.md"
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", pattern))):
+def measured_traffic_ratio(kernel, profile_key):
+    """(HBM bytes / algorithmic bytes, profile file) for one dispatch of
+    ``kernel``, from the committed rocprofv3 counter summary
+    ``profiles/<kernel>_<key>.md`` (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or (None, None) when there is none or the kernel's
+    sources changed since it was taken.  The bench scales the ratio by its
+    own algorithmic bytes per launch, so the figure matches the line's step
+    count and lengths."""
+    for path in [os.path.join(ROOT, "profiles", f"{kernel}_{profile_key}.md")]:
+        if not os.path.exists(path):
+            continue
         fields = {}
         for line in open(path):
             if " = " in line:
                 k, v = line.split(" = ", 1)
                 fields[k.strip()] = v.strip()
-        if "traffic_bytes_per_dispatch" not in fields:
+        files = fields.get("kernel_source_files", "").split()
+        if "traffic_ratio" not in fields or not files:
             continue
-        if fields.get("kernel_source_fingerprint") == source_fingerprint():
-            return int(fields["traffic_bytes_per_dispatch"])
+        if fields.get("kernel_source_fingerprint") == source_fingerprint(files):
+            return float(fields["traffic_ratio"]), os.path.basename(path)
+    return None, None
+
+
+def cpu_model():
+    """The host CPU's model name (first ``model name`` of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
     return None
 
 
@@ -321,6 +352,7 @@ class Step:
                             pa.I8 if self.int8 else pa.F32 if w["dtype"] == "f32" else pa.F16,
                             torch.cuda.current_stream(dev).cuda_stream)
         self.k = 0
+        self.host_s = []         # host bookkeeping time per step (block manager, tables)
         self.kv_bytes = []       # algorithmic decode bytes per step
         self.ctx_tokens = []
         self.ncow = []
@@ -364,13 +396,20 @@ class Step:
             return int(np.minimum(ln, self.window).sum())
         return int(ln.sum())
 
-    def run(self, timed_events=None):
+    def run(self, timed_events=None, write_events=None):
+        """One decode step.  ``timed_events`` (a pair) brackets the decode
+        call; ``write_events`` (a pair) brackets the upload + cache write
+        (copy-on-write launch included)."""
         torch, pa = self.torch, self.pa
         buf = self.bufs[self.k % 2]
         fence = buf.pop("fence", None) or buf["event"]
         fence.synchronize()                 # its previous upload has left pinned memory
+        t_host = time.perf_counter()
         ncow = self.host_step(buf)
         maxlen = int(buf["lens"].numpy().max())
+        self.host_s.append(time.perf_counter() - t_host)
+        if write_events is not None:
+            write_events[0].record()
         # the C calls take arguments prepared once per buffer (the binding's
         # checks would add host time to every step)
         if self.upload == "fused":   # upload + K/V scatter in one launch
@@ -379,12 +418,14 @@ class Step:
             if rc != 0:
                 raise pa.PAError(rc, pa.lib().pa_last_error().decode())
             # the pinned buffer may be refilled once this upload has run: in a
-            # timed step the event after the decode marks that (one queue
-            # marker fewer per step), otherwise a marker of its own
-            if timed_events is None:
-                buf["event"].record()
-            else:
+            # timed step an event recorded after it anyway marks that (one
+            # queue marker fewer per step), otherwise a marker of its own
+            if timed_events is not None:
                 buf["fence"] = timed_events[1]
+            elif write_events is not None:
+                buf["fence"] = write_events[1]
+            else:
+                buf["event"].record()
         else:
             if self.upload == "kernel":
                 rc = pa.lib().pa_stage_from_host(*buf["stage_args"])
@@ -396,6 +437,8 @@ class Step:
             pa.cache_write(self.new_k, self.new_v, self.pool, self.d_slots,
                            cow_pairs=self.d_pairs[:ncow] if ncow else None,
                            kv_scales=self.kv_scales)
+        if write_events is not None:
+            write_events[1].record()
         if timed_events is not None:
             timed_events[0].record()
         rc = pa.lib().pa_decode(*self.decode_pre, maxlen, *self.decode_post)
@@ -538,7 +581,7 @@ def stream_ceiling(dev, tile_bytes=4096, nbytes=4 << 30, reps=5):
     loads."""
     import ctypes
     import torch
-    probe = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_153_amd", "libpa_probe.so"))
+    probe = ctypes.CDLL(os.path.join(ROOT, "bench_probe", "libpa_probe.so"))
     probe.pa_probe_read_linear.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     probe.pa_probe_read_tiles_sized.argtypes = [
@@ -610,19 +653,23 @@ def parity_sample(st, samples=3):
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, AMD specification
 
 
-def prefill_bench(args, dev):
+def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parity=True,
+                  cpu=True):
     """Chunked-prefill attention: each step writes a chunk of new K/V rows per
     sequence (pa_cache_write) and runs causal multi-token attention over the
     paged cache (pa_prefill).  Flops counted: 4 * D per (query, head, key
-    attended), the q.K and P.V products."""
+    attended), the q.K and P.V products.  Returns the result line."""
     import torch
     import numpy as np
     import paged_kv_cache_153_amd as pa
     import synth
-    w = WORKLOADS[args.workload]
+    workload = workload or args.workload
+    steps = steps or args.steps
+    warmup = args.warmup if warmup is None else warmup
+    w = WORKLOADS[workload]
     S, Hq, Hkv, D = args.seqs or 8, w["Hq"], w["Hkv"], w["D"]
     bs = args.block_size or w["bs"]
-    n, T = args.context or 4096, args.chunk
+    n, T = args.context or (8192 if workload == "llama70b" else 4096), args.chunk
     if w["dtype"] != "f16" or T > n:
         raise SystemExit("prefill needs a float16 workload and chunk <= context")
     x = synth.make_decode_inputs([n] * S, Hq, Hkv, D, bs, dtype="f16", seed=args.seed,
@@ -649,20 +696,20 @@ def prefill_bench(args, dev):
         if ev:
             ev[1].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(StepEvent(), StepEvent()) for _ in range(args.steps)]
+    ev = [(StepEvent(), StepEvent()) for _ in range(steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    att_s = sum(a.elapsed_time(b) for a, b in ev) / args.steps / 1e3
+    att_s = sum(a.elapsed_time(b) for a, b in ev) / steps / 1e3
     StepEvent.release_all(ev)
     tflops = flops / att_s / 1e12
     parity = None
-    if not args.no_parity:
+    if check_parity:
         import oracle
         rng = np.random.default_rng(0)
         errs = []
@@ -676,14 +723,18 @@ def prefill_bench(args, dev):
                                           np.array([n - T + i + 1]), np.array([0, 1]), x.scale)
                 errs.append(float(np.abs(out[row].cpu().numpy() - want[0]).max()))
         parity = max(errs)
-    log(f"[bench] prefill step {wall / args.steps * 1e6:.1f} us, attention {att_s * 1e6:.1f} us, "
+    log(f"[bench] prefill step {wall / steps * 1e6:.1f} us, attention {att_s * 1e6:.1f} us, "
         f"{tflops:.1f} TFLOP/s")
+    # HBM bytes the kernel must move at least: every K/V row of the
+    # contexts once, the queries, the outputs
+    unique = S * n * Hkv * 2 * D * 2 + S * T * Hq * D * (2 + 4)
+    ratio, prof = measured_traffic_ratio("prefill_mfma", f"prefill_{workload}")
     res = {
         "metric": "chunked-prefill attention TFLOP/s (q.K and P.V, useful flops)",
-        "value": round(flops * args.steps / wall / 1e12, 2),
+        "value": round(flops * steps / wall / 1e12, 2),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0, std^2) K/V/Q; no weights)",
         "config": {"workload": f"{w['desc']}: {S} seqs, chunk {T} at context {n} (past {n - T})",
@@ -696,13 +747,132 @@ def prefill_bench(args, dev):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     # HBM bytes per pa_prefill dispatch (rocprofv3, committed
-                     # profile) for the configuration it was taken on
-                     "traffic": measured_traffic(args.workload, "prefill")
-                     if (S, T, n, bs, args.seed) == (8, 512, 4096, w["bs"], 0) else None},
-        "cpu_baseline": None if args.no_cpu_baseline else prefill_cpu_baseline(q, x, S, T, n),
+                     # HBM bytes per pa_prefill dispatch: the committed counter
+                     # profile's ratio to the unique bytes, times this line's
+                     "traffic": round(ratio * unique) if ratio else None},
+        "traffic_profile": prof,
+        "cpu_baseline": prefill_cpu_baseline(q, x, S, T, n) if cpu else None,
     }
-    print(json.dumps(res), flush=True)
+    del x, q, new_k, new_v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+# The other workloads the default run also measures (one compact record
+# each, after the headline): the remaining configurations of the method's
+# benchmark set, the INT8 pools and a chunked prefill.
+EXTRA_DECODE = [
+    # (key, workload, overrides)
+    ("tiny", "tiny", {}),
+    ("gqa7b", "gqa7b", {}),
+    ("llama70b", "llama70b", {}),
+    ("llama70b_p512", "llama70b", {"partition": 512}),
+    ("shared_prefix_bs8", "shared_prefix", {"block_size": 8}),
+    ("shared_prefix_bs16", "shared_prefix", {"block_size": 16}),
+    ("shared_prefix_bs32", "shared_prefix", {"block_size": 32}),
+    ("llama7b_mha_i8", "llama7b_mha", {"kv_dtype": "i8"}),
+    ("gqa7b_i8", "gqa7b", {"kv_dtype": "i8"}),
+    ("llama70b_i8", "llama70b", {"kv_dtype": "i8"}),
+]
+EXTRA_PREFILL = ["gqa7b"]
+
+
+def measure_decode(args, dev, name, block_size=None, partition=0, kv_dtype="f16", window=0,
+                   context=0, kernel="auto", kv_loads="auto", prefix_cache=False,
+                   upload="fused", steps=None, warmup=None, parity=True, write_steps=None):
+    """Warm-up steps, then ``steps`` timed steps (decode call bracketed by
+    HIP events), then ``write_steps`` steps with the upload + cache write
+    bracketed instead.  Returns (Step, metrics)."""
+    import torch
+    steps = steps or args.steps
+    warmup = args.warmup if warmup is None else warmup
+    write_steps = min(steps, 20) if write_steps is None else write_steps
+    st = Step(name, block_size, args.seed, warmup + steps + write_steps, kernel, partition, dev,
+              context=context, window=window, kv_dtype=kv_dtype, kv_loads=kv_loads,
+              prefix_cache=prefix_cache, upload=upload)
+    log(f"[bench] {name}: warmup {warmup} steps")
+    for _ in range(warmup):
+        st.run()
+    torch.cuda.synchronize()
+    st.kv_bytes.clear()
+    st.ctx_tokens.clear()
+    st.ncow.clear()
+    st.host_s.clear()
+    ev = [(StepEvent(), StepEvent()) for _ in range(steps)]
+    log(f"[bench] {name}: timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st.run(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    StepEvent.release_all(ev)
+    for b in st.bufs:            # the released events no longer fence the buffers
+        b.pop("fence", None)
+    m = {"steps": steps, "warmup": warmup, "wall": wall,
+         "kv_bytes": sum(st.kv_bytes), "tokens": sum(st.ctx_tokens),
+         "ncow": sum(st.ncow), "host_us": sum(st.host_s) / steps * 1e6}
+    m["dec_avg_s"] = sum(dec_ms) / len(dec_ms) / 1e3
+    m["dec_med_s"] = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
+    m["achieved"] = m["kv_bytes"] / steps / m["dec_avg_s"] / 1e9
+    m["value"] = m["kv_bytes"] / wall / 1e9
+    m["parity"] = parity_sample(st) if parity else None
+    if write_steps:
+        wev = [(StepEvent(), StepEvent()) for _ in range(write_steps)]
+        for i in range(write_steps):
+            st.run(write_events=wev[i])
+        torch.cuda.synchronize()
+        w_ms = [a.elapsed_time(b) for a, b in wev]
+        StepEvent.release_all(wev)
+        for b in st.bufs:
+            b.pop("fence", None)
+        m["write_us"] = sum(w_ms) / len(w_ms) * 1e3
+    else:
+        m["write_us"] = None
+    log(f"[bench] {name}: step {wall / steps * 1e6:.1f} us, decode {m['dec_avg_s'] * 1e6:.1f} us, "
+        f"{m['achieved']:.1f} GB/s decode, {m['value']:.1f} GB/s whole step")
+    return st, m
+
+
+def decode_kernel_name(st, kernel):
+    """Family of the decode kernel a Step's launches use (as the library's
+    automatic choice picks it: matrix cores for f16 / INT8 with G >= 4)."""
+    g = st.Hq // st.Hkv
+    if kernel == "auto":
+        kernel = "mfma" if st.w["dtype"] != "f32" and g >= 4 else "valu"
+    return f"decode_{kernel}" + ("_i8" if st.int8 else "")
+
+
+def extra_line(args, dev, key, name, kw):
+    """One compact record for a further workload at the default launch."""
+    import torch
+    st, m = measure_decode(args, dev, name, steps=args.steps, warmup=args.warmup,
+                           parity=not args.no_parity, **kw)
+    ratio, prof = measured_traffic_ratio(decode_kernel_name(st, "auto"), key)
+    per_launch = m["kv_bytes"] / m["steps"]
+    rec = {
+        "workload": st.w["desc"] + (f" (block {st.bs})" if kw.get("block_size") else "")
+        + (", INT8 pool" if st.int8 else "")
+        + (f", {kw['partition']}-token partitions" if kw.get("partition") else ""),
+        "kernel": decode_kernel_name(st, "auto"),
+        "partition": kw.get("partition", 0),
+        "decode_us": round(m["dec_avg_s"] * 1e6, 2),
+        "decode_GBps": round(m["achieved"], 1),
+        "hbm_frac": round(m["achieved"] / HBM_PEAK_GBPS, 4),
+        "decode_seq_ctx_tokens_per_s": round(m["tokens"] / m["steps"] / m["dec_avg_s"], 1),
+        "whole_step_GBps": round(m["value"], 1),
+        "ms_per_step": round(m["wall"] / m["steps"] * 1e3, 4),
+        "cache_write_us": round(m["write_us"], 2) if m["write_us"] else None,
+        "host_bookkeeping_us": round(m["host_us"], 2),
+        "cow_pairs_per_step": round(m["ncow"] / m["steps"], 3),
+        "parity_max_abs_err": m["parity"],
+        "traffic": round(ratio * per_launch) if ratio else None,
+        "traffic_profile": prof,
+    }
+    del st
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -739,6 +909,11 @@ def main():
                     help="sliding window: attend to the last W tokens (0 = whole context)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured HBM read ceiling (libpa_probe.so)")
+    ap.add_argument("--extras", default="auto", choices=["auto", "all", "none"],
+                    help="also measure the other workloads (GQA, 70B with automatic and "
+                         "512-token partitions, shared prefix at block 8/16/32, tiny, INT8 "
+                         "pools, a GQA prefill chunk) in one compact record each; auto = only "
+                         "when the headline is the default 7B launch")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -756,57 +931,40 @@ def main():
     pa.lib()
     dev = torch.device("cuda:0")
     if args.mode == "prefill":
-        prefill_bench(args, dev)
+        print(json.dumps(prefill_bench(args, dev, check_parity=not args.no_parity,
+                                       cpu=not args.no_cpu_baseline)), flush=True)
         return
     if args.calibrate_copy:
         print(json.dumps(calibrate_copy(dev)), flush=True)
         return
-    st = Step(args.workload, args.block_size, args.seed, args.warmup + args.steps, args.kernel,
-              args.partition, dev, context=args.context, window=args.window,
-              kv_dtype=args.kv_dtype, kv_loads=args.kv_loads, prefix_cache=args.prefix_cache,
-              upload=args.upload)
-    step_fn = st.run
-    log(f"[bench] warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step_fn()
-    torch.cuda.synchronize()
-    st.kv_bytes.clear()
-    st.ctx_tokens.clear()
-    st.ncow.clear()
-    ev = [(StepEvent(), StepEvent()) for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step_fn(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    StepEvent.release_all(ev)
-    for b in st.bufs:            # the released events no longer fence the buffers
-        b.pop("fence", None)
-    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
-    dec_med_s = sorted(dec_ms)[len(dec_ms) // 2] / 1e3
-    total_bytes = sum(st.kv_bytes)
-    total_tokens = sum(st.ctx_tokens)
-    step_s = wall / args.steps
-    value = total_bytes / wall / 1e9
-    achieved = total_bytes / args.steps / dec_avg_s / 1e9
-    log(f"[bench] step {step_s * 1e6:.1f} us, decode {dec_avg_s * 1e6:.1f} us, "
-        f"{achieved:.1f} GB/s decode, {value:.1f} GB/s whole step")
-
-    parity = None if args.no_parity else parity_sample(st)
+    st, m = measure_decode(args, dev, args.workload, block_size=args.block_size,
+                           partition=args.partition, kv_dtype=args.kv_dtype, window=args.window,
+                           context=args.context, kernel=args.kernel, kv_loads=args.kv_loads,
+                           prefix_cache=args.prefix_cache, upload=args.upload,
+                           parity=not args.no_parity)
+    steps = args.steps
+    step_s = m["wall"] / steps
+    dec_avg_s = m["dec_avg_s"]
+    achieved = m["achieved"]
     # bytes of one K (or V) tile of one KV head: the unit the decode reads
     tile_bytes = 2048 if st.bs * st.D * st.elem <= 2048 else 4096
-    ceiling = None if args.no_ceiling else stream_ceiling(dev, tile_bytes)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(st)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(st)
+        cpu["cpu_model"] = cpu_model()
+    key = (args.workload + ("_i8" if st.int8 else "")
+           + (f"_w{args.window}" if args.window else "")
+           + (f"_bs{args.block_size}" if args.block_size else "")
+           + (f"_p{args.partition}" if args.partition else ""))
+    kernel_name = decode_kernel_name(st, args.kernel)
+    ratio, prof = measured_traffic_ratio(kernel_name, key)
     w = st.w
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(m["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
@@ -818,7 +976,7 @@ def main():
             "workload": w["desc"] + (f" (block {st.bs})" if args.block_size else ""),
             "num_seqs": st.S, "num_q_heads": st.Hq, "num_kv_heads": st.Hkv, "head_dim": st.D,
             "block_size": st.bs, "pool_blocks": st.num_blocks,
-            "mean_key_tokens": round(total_tokens / args.steps / st.S, 1),
+            "mean_key_tokens": round(m["tokens"] / steps / st.S, 1),
             "kernel": args.kernel, "partition": args.partition, "seed": args.seed,
             "context_override": args.context or None,
             "sliding_window": args.window or None,
@@ -829,32 +987,54 @@ def main():
                        "dma": "DMA copy (torch copy_)"}[st.upload],
             "step": "block-manager append + tables H2D + pa_cache_write (+COW) + pa_decode",
         },
-        "hbm_frac_whole_step": round(value / HBM_PEAK_GBPS, 4),
-        "seq_ctx_tokens_per_s": round(total_tokens / wall, 1),
+        "hbm_frac_whole_step": round(m["value"] / HBM_PEAK_GBPS, 4),
+        "seq_ctx_tokens_per_s": round(m["tokens"] / m["wall"], 1),
+        "decode_kernel": kernel_name,
         "decode_us": round(dec_avg_s * 1e6, 2),
-        "decode_us_median": round(dec_med_s * 1e6, 2),
-        "decode_seq_ctx_tokens_per_s": round(total_tokens / args.steps / dec_avg_s, 1),
-        "cow_pairs_per_step": round(sum(st.ncow) / args.steps, 3),
+        "decode_us_median": round(m["dec_med_s"] * 1e6, 2),
+        "decode_seq_ctx_tokens_per_s": round(m["tokens"] / steps / dec_avg_s, 1),
+        "cache_write_us": round(m["write_us"], 2) if m["write_us"] else None,
+        "host_bookkeeping_us": round(m["host_us"], 2),
+        "cow_pairs_per_step": round(m["ncow"] / steps, 3),
         "prefix_cache": st.prefix_info,
-        "parity_max_abs_err": parity,
-        "measured_read_ceiling": ceiling,
-        "decode_frac_of_tile_ceiling": (
-            round(achieved / ceiling[f"random_{tile_bytes // 1024}KiB_tile_read_GBps"], 4)
-            if ceiling else None),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(args.workload + ("_i8" if st.int8 else "")
-                                        + (f"_w{args.window}" if args.window else ""))
-            # only for the configuration the profile was taken on
-            if (args.kernel, args.partition, args.context, args.block_size, args.kv_loads,
-                args.seed) == ("auto", 0, 0, None, "auto", 0) else None,
-        },
-        "cpu_baseline": cpu,
+        "parity_max_abs_err": m["parity"],
     }
+    res["roofline"] = {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        # HBM bytes per decode launch: the committed counter profile's
+        # ratio to the algorithmic bytes, times this line's algorithmic bytes
+        "traffic": round(ratio * m["kv_bytes"] / steps) if ratio else None,
+    }
+    res["traffic_profile"] = prof
+    res["cpu_baseline"] = cpu
+    del st
+    torch.cuda.empty_cache()
+    ceiling = None if args.no_ceiling else stream_ceiling(dev, tile_bytes)
+    res["measured_read_ceiling"] = ceiling
+    res["decode_frac_of_tile_ceiling"] = (
+        round(achieved / ceiling[f"random_{tile_bytes // 1024}KiB_tile_read_GBps"], 4)
+        if ceiling else None)
+    default_launch = (args.workload, args.block_size, args.partition, args.kv_dtype, args.window,
+                      args.context, args.kernel, args.kv_loads, args.prefix_cache,
+                      args.upload) == ("llama7b_mha", None, 0, "f16", 0, 0, "auto", "auto",
+                                       False, "fused")
+    if args.extras == "all" or (args.extras == "auto" and default_launch):
+        extra = {}
+        for k, name, kw in EXTRA_DECODE:
+            extra[k] = extra_line(args, dev, k, name, kw)
+        for name in EXTRA_PREFILL:
+            r = prefill_bench(args, dev, workload=name, steps=args.steps, warmup=args.warmup,
+                              check_parity=not args.no_parity, cpu=False)
+            extra[f"prefill_{name}"] = {
+                "workload": r["config"]["workload"], "kernel": "prefill_mfma",
+                "attention_us": r["attention_us"], "tflops": r["roofline"]["achieved"],
+                "mfma_frac": r["roofline"]["frac"], "parity_max_abs_err": r["parity_max_abs_err"],
+                "traffic": r["roofline"]["traffic"], "traffic_profile": r["traffic_profile"]}
+        res["workloads"] = extra
     print(json.dumps(res), flush=True)
 
 

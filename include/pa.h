@@ -13,6 +13,8 @@
  *   [KVPA]  "KV Cache与PagedAttention深度解析：vLLM内存管理革命" (iopencloud.com)
  *   [KV2P]  "KV Cache从原理到实战：大模型推理内存管理演进与优化" (xnwp.cn)
  *   [NANO]  the zwxr.cn nano-vllm walkthrough (untitled in the extract)
+ *   [INFRA] "大模型 (LLM) 推理加速核心技术解析：从 KV Cache 到 PagedAttention
+ *           实战" (jsqmd.com)
  *
  * Conventions for every call:
  *   - Return value is a pa_status (0 = PA_OK).  No C++ exception crosses the

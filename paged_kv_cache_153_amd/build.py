@@ -18,8 +18,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-PROBE_SRC = os.path.join(HERE, "probe", "stream_read.hip")
-PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
 ARCH = "gfx950"
 
 # Packed FP32 arithmetic is disabled for all device code; hipcc's host pass
@@ -45,8 +43,6 @@ def sources():
 
 def _compile(src, verbose):
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    if src == PROBE_SRC:
-        obj = os.path.join(OBJ, "probe_" + os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -72,14 +68,6 @@ def build(verbose=False, jobs=None):
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
-    # the bandwidth probe used by bench.py for the measured ceiling
-    pobj = _compile(PROBE_SRC, verbose)
-    tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, pobj],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"probe link failed\n{r.stdout}{r.stderr}")
-    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

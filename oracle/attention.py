@@ -50,6 +50,12 @@ its scores span past + T keys; the plain reading is the mask aligned to the
 end (each query sees all past tokens and the chunk tokens up to itself),
 which for T = 1 is the decode case and for n = T is the square mask.
 
+With a sliding window of W tokens (the remedy [KV2P] §7.2 names for long
+contexts) each query sees only the last W tokens up to and including its own
+position: keys ``max(0, p + 1 - W) <= t <= p``.  Reading: the decode's window
+(the last W of the n cached tokens, the newest included) applied at every
+query position of the chunk, so T = 1 is the windowed decode.
+
 Split-context partials
 ----------------------
 The pages merge block results with decay factors ([KVPA] §7.2 running max /
@@ -124,15 +130,18 @@ def decode_ref(q, kv_cache, block_tables, context_lens, scale, window=0):
     return out
 
 
-def prefill_ref(q, kv_cache, block_tables, context_lens, query_start, scale):
+def prefill_ref(q, kv_cache, block_tables, context_lens, query_start, scale, window=0):
     """Causal attention of multi-token queries over a paged cache.
 
     q:            [total_q, Hq, D], the queries of sequence s are rows
                   ``query_start[s] .. query_start[s+1]-1`` (T_s of them)
     context_lens: [S], n_s, counting the chunk (n_s >= T_s)
     query_start:  [S+1] increasing, query_start[0] = 0
+    window:       0 = every earlier key; W > 0 = only the last W tokens up
+                  to the query's own position
     returns       [total_q, Hq, D] float64: row ``query_start[s] + i`` is the
-                  attention of query i over keys t <= n_s - T_s + i
+                  attention of query i over keys t <= p = n_s - T_s + i
+                  (and t > p - W under a window)
     """
     q = np.asarray(q)
     total, num_q_heads, head_dim = q.shape
@@ -152,10 +161,11 @@ def prefill_ref(q, kv_cache, block_tables, context_lens, query_start, scale):
         v = v.astype(np.float64)
         for i in range(T):
             p = n - T + i
+            lo = max(0, p + 1 - window) if window > 0 else 0
             for h in range(num_q_heads):
                 g = h // group
-                out[q0 + i, h] = _attend(q[q0 + i, h].astype(np.float64), k[:p + 1, g, :],
-                                         v[:p + 1, g, :], scale)
+                out[q0 + i, h] = _attend(q[q0 + i, h].astype(np.float64), k[lo:p + 1, g, :],
+                                         v[lo:p + 1, g, :], scale)
     return out
 
 

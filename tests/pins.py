@@ -604,3 +604,46 @@ def chunked_equals_whole(prefill, seed=13):
     a = prefill(q[:t1], pool, tables, np.array([t1]), np.array([0, t1]), 0.2)
     b = prefill(q[t1:], pool, tables, np.array([n]), np.array([0, n - t1]), 0.2)
     return bool(np.allclose(np.concatenate([a, b]), whole, rtol=0, atol=1e-12))
+
+
+def prefill_window_is_banded_sdpa(prefill, window, seed=14):
+    """Under a window of W tokens each chunk equals SDPA on its contiguous
+    K/V with a band mask: key t is allowed for the query at position p when
+    p - W < t <= p (the causal mask cut to the last W tokens)."""
+    rng = np.random.default_rng(seed)
+    lens, chunks, hq, hkv, d, bs = (40, 17, 64, 9), (40, 5, 20, 1), 8, 2, 16, 8
+    ks = [rng.standard_normal((n, hkv, d)) for n in lens]
+    vs = [rng.standard_normal((n, hkv, d)) for n in lens]
+    pool, tables = _scatter(ks, vs, bs, seed)
+    qstart = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((int(qstart[-1]), hq, d))
+    out = prefill(q, pool, tables, np.array(lens), qstart, 0.3, window=window)
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        kt = torch.from_numpy(ks[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vs[s]).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        qt = torch.from_numpy(q[qstart[s]:qstart[s + 1]]).permute(1, 0, 2)      # [Hq, T, D]
+        pos = (n - T + torch.arange(T))[:, None]
+        t = torch.arange(n)[None, :]
+        allowed = (t <= pos) & (t > pos - window)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed,
+                                                               scale=0.3)
+        if not np.allclose(out[qstart[s]:qstart[s + 1]], ref.permute(1, 0, 2).numpy(),
+                           rtol=0, atol=1e-12):
+            return False
+    return True
+
+
+def prefill_window_one_is_own_value_row(prefill):
+    """W = 1: every query sees only its own token, so its output is that
+    token's V row, exactly."""
+    rng = np.random.default_rng(15)
+    kv = rng.standard_normal((6, 2, 1, 4, 8))
+    bt = np.array([[5, 2, 0]])
+    q = rng.standard_normal((4, 2, 8))
+    out = prefill(q, kv, bt, np.array([10]), np.array([0, 4]), 0.7, window=1)
+    for i in range(4):
+        p = 10 - 4 + i
+        row = kv[bt[0, p // 4], 1, 0, p % 4]
+        if not (np.array_equal(out[i, 0], row) and np.array_equal(out[i, 1], row)):
+            return False
+    return True

@@ -320,7 +320,7 @@ def test_prefix_pins_pass_the_model():
 # multi-token (causal) mutants
 # --------------------------------------------------------------------------
 def prefill_mutant(mistake):
-    def prefill(q, kv, bt, cl, qstart, scale):
+    def prefill(q, kv, bt, cl, qstart, scale, window=0):
         q = np.asarray(q, dtype=np.float64)
         total, hq, d = q.shape
         hkv, bs = kv.shape[2], kv.shape[3]
@@ -340,10 +340,15 @@ def prefill_mutant(mistake):
                 if mistake == "strict":
                     p -= 1
                 p = max(p, 0)
+                lo = max(0, p + 1 - window) if window > 0 else 0
+                if mistake == "window_off_by_one" and window > 0:
+                    lo = max(0, p - window)
+                if mistake == "window_from_context_end" and window > 0:
+                    lo = min(p, max(0, n - window))     # the decode's window for every query
                 for h in range(hq):
-                    z = scale * (k[:p + 1, h // G] @ q[q0 + i, h])
+                    z = scale * (k[lo:p + 1, h // G] @ q[q0 + i, h])
                     w = np.exp(z - z.max())
-                    out[q0 + i, h] = (w @ v[:p + 1, h // G]) / w.sum()
+                    out[q0 + i, h] = (w @ v[lo:p + 1, h // G]) / w.sum()
         return out
     return prefill
 
@@ -361,3 +366,18 @@ def test_prefill_pins_catch(mistake):
 def test_prefill_pins_pass_clean_copy():
     assert not _prefill_pins_fail(prefill_mutant(None))
     assert not _prefill_pins_fail(oracle.prefill_ref)
+
+
+def _prefill_window_pins_fail(f):
+    ok = all(pins.prefill_window_is_banded_sdpa(f, w) for w in (1, 3, 16, 39))
+    return not (ok and pins.prefill_window_one_is_own_value_row(f))
+
+
+@pytest.mark.parametrize("mistake", ["window_off_by_one", "window_from_context_end"])
+def test_prefill_window_pins_catch(mistake):
+    assert _prefill_window_pins_fail(prefill_mutant(mistake))
+
+
+def test_prefill_window_pins_pass_clean_copy():
+    assert not _prefill_window_pins_fail(prefill_mutant(None))
+    assert not _prefill_window_pins_fail(oracle.prefill_ref)

@@ -320,3 +320,37 @@ def test_prefill_first_query_of_fresh_prompt_is_its_value_row():
     q = rng.standard_normal((5, 2, 8))
     out = oracle.prefill_ref(q, kv, np.array([[2, 0]]), np.array([5]), np.array([0, 5]), 1.0)
     assert np.array_equal(out[0, 0], kv[2, 1, 0, 0]) and np.array_equal(out[0, 1], kv[2, 1, 0, 0])
+
+
+# sliding window on multi-token queries ([KV2P] §7.2 applied per query)
+@pytest.mark.parametrize("window", [1, 3, 16, 39, 100])
+def test_prefill_window_is_banded_sdpa(window):
+    assert _pins.prefill_window_is_banded_sdpa(oracle.prefill_ref, window)
+
+
+def test_prefill_window_one_is_own_value_row():
+    assert _pins.prefill_window_one_is_own_value_row(oracle.prefill_ref)
+
+
+def test_prefill_window_single_token_is_windowed_decode():
+    """T = 1 per sequence under a window is the windowed decode, exactly."""
+    rng = np.random.default_rng(16)
+    kv = rng.standard_normal((12, 2, 2, 8, 16))
+    bt = np.array([[3, 1, 7], [4, 0, 11]])
+    lens = np.array([20, 9])
+    q = rng.standard_normal((2, 4, 16))
+    for w in (1, 5, 9, 19, 50):
+        assert np.array_equal(oracle.prefill_ref(q, kv, bt, lens, np.array([0, 1, 2]), 0.5,
+                                                 window=w),
+                              oracle.decode_ref(q, kv, bt, lens, 0.5, window=w))
+
+
+def test_prefill_window_at_least_context_is_plain_causal():
+    rng = np.random.default_rng(17)
+    kv = rng.standard_normal((10, 2, 2, 8, 16))
+    bt = np.array([[3, 1, 7, 9], [4, 0, 2, 5]])
+    lens, qs = np.array([30, 12]), np.array([0, 10, 22])
+    q = rng.standard_normal((22, 4, 16))
+    full = oracle.prefill_ref(q, kv, bt, lens, qs, 0.4)
+    assert np.array_equal(oracle.prefill_ref(q, kv, bt, lens, qs, 0.4, window=30), full)
+    assert not np.allclose(oracle.prefill_ref(q, kv, bt, lens, qs, 0.4, window=29), full)

@@ -521,7 +521,7 @@ def cpu_baseline(st, budget_s=20.0, cap_wall_s=8.0):
                        f"{wall:.2f} s wall; {toks / wall:.4g} seq*ctx tokens/s")
 
 
-def prefill_cpu_baseline(q, x, S, T, n, budget_s=20.0, cap_wall_s=8.0, rows=16):
+def prefill_cpu_baseline(q, x, S, T, n, budget_s=20.0, cap_wall_s=8.0, rows=16, window=0):
     """Time the fp64 oracle (prefill_ref) on the host cores: groups of
     ``rows`` consecutive query rows of the step's first sequences, each group
     the last ``rows`` tokens of a context ending at its last row (host copies
@@ -549,7 +549,7 @@ def prefill_cpu_baseline(q, x, S, T, n, budget_s=20.0, cap_wall_s=8.0, rows=16):
         blocks, qs = host[s_]
         ctx = n - T + i0 + rows                 # the group is the last `rows` tokens
         return oracle.prefill_ref(qs[i0:i0 + rows], blocks, np.arange(blocks.shape[0])[None],
-                                  np.array([ctx]), np.array([0, rows]), x.scale)
+                                  np.array([ctx]), np.array([0, rows]), x.scale, window=window)
 
     done, flops = 0, 0.0
     with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
@@ -559,7 +559,8 @@ def prefill_cpu_baseline(q, x, S, T, n, budget_s=20.0, cap_wall_s=8.0, rows=16):
             for f in [ex.submit(one, it) for it in batch]:
                 f.result()
             for s_, i0 in batch:
-                keys = sum(n - T + i + 1 for i in range(i0, i0 + rows))
+                keys = sum(min(n - T + i + 1, window) if window > 0 else n - T + i + 1
+                           for i in range(i0, i0 + rows))
                 flops += 4.0 * D * Hq * keys
             done += len(batch)
             wall = time.perf_counter() - t0
@@ -684,7 +685,9 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
                          dtype=torch.int64, device=dev)
     qstart = torch.arange(0, S * T + 1, T, dtype=torch.int32, device=dev)
     out = torch.empty((S * T, Hq, D), dtype=torch.float32, device=dev)
-    keys = S * (T * (n - T) + T * (T + 1) // 2)
+    win = args.window
+    # keys attended per query at position p: p + 1, or at most the window
+    keys = S * sum(min(p + 1, win) if win > 0 else p + 1 for p in range(n - T, n))
     flops = 4.0 * D * Hq * keys
 
     def step(ev=None):
@@ -692,7 +695,7 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
         if ev:
             ev[0].record()
         pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens, qstart, scale=x.scale,
-                   max_query_len=T, out=out)
+                   max_query_len=T, out=out, sliding_window=win)
         if ev:
             ev[1].record()
 
@@ -720,14 +723,16 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
                 row = s_ * T + i
                 want = oracle.prefill_ref(q[row:row + 1].cpu().numpy(), blocks,
                                           np.arange(blocks.shape[0])[None],
-                                          np.array([n - T + i + 1]), np.array([0, 1]), x.scale)
+                                          np.array([n - T + i + 1]), np.array([0, 1]), x.scale,
+                                          window=win)
                 errs.append(float(np.abs(out[row].cpu().numpy() - want[0]).max()))
         parity = max(errs)
     log(f"[bench] prefill step {wall / steps * 1e6:.1f} us, attention {att_s * 1e6:.1f} us, "
         f"{tflops:.1f} TFLOP/s")
     # HBM bytes the kernel must move at least: every K/V row of the
     # contexts once, the queries, the outputs
-    unique = S * n * Hkv * 2 * D * 2 + S * T * Hq * D * (2 + 4)
+    rows_read = min(n, T + win - 1) if win > 0 else n     # keys some query of a chunk sees
+    unique = S * rows_read * Hkv * 2 * D * 2 + S * T * Hq * D * (2 + 4)
     ratio, prof = measured_traffic_ratio("prefill_mfma", f"prefill_{workload}")
     res = {
         "metric": "chunked-prefill attention TFLOP/s (q.K and P.V, useful flops)",
@@ -737,7 +742,9 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
         "ms_per_step": round(wall / steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic (seeded N(0, std^2) K/V/Q; no weights)",
-        "config": {"workload": f"{w['desc']}: {S} seqs, chunk {T} at context {n} (past {n - T})",
+        "config": {"workload": f"{w['desc']}: {S} seqs, chunk {T} at context {n} (past {n - T})"
+                               + (f", sliding window {win}" if win > 0 else ""),
+                   "sliding_window": win or None,
                    "num_seqs": S, "chunk": T, "context": n, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "step": "pa_cache_write (chunk rows) + pa_prefill"},
@@ -751,7 +758,7 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
                      # profile's ratio to the unique bytes, times this line's
                      "traffic": round(ratio * unique) if ratio else None},
         "traffic_profile": prof,
-        "cpu_baseline": prefill_cpu_baseline(q, x, S, T, n) if cpu else None,
+        "cpu_baseline": prefill_cpu_baseline(q, x, S, T, n, window=win) if cpu else None,
     }
     del x, q, new_k, new_v, out
     torch.cuda.empty_cache()

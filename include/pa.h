@@ -250,7 +250,10 @@ size_t pa_decode_static_capacity(void);
  * position p = n_s - T_s + i and attends to keys t <= p:
  *   out[row, h, :] = sum_{t <= p} softmax_t(scale * q[row,h,:] . K_t) V_t,
  * with the paging and grouping of pa_decode.  T_s = 1 is the decode case;
- * T_s = n_s is an ordinary causal prefill.  Accumulation and output float32.
+ * T_s = n_s is an ordinary causal prefill.  With sliding_window = W > 0 a
+ * query sees only the last W tokens up to its own position, p - W < t <= p
+ * ([KV2P] §7.2, the decode's window at every query position); rows before
+ * every query's window are not read.  Accumulation and output float32.
  *
  *   out            device, [total_queries, num_q_heads, head_dim] float32
  *   query          device, [total_queries, num_q_heads, head_dim] binary16
@@ -262,10 +265,13 @@ size_t pa_decode_static_capacity(void);
  *   max_query_len  host bound on every T_s (sizes the grid)
  *   scale          > 0 and finite (the kernel takes the running max on the
  *                  raw scores); PA_ERR_INVALID_ARG otherwise
+ *   sliding_window 0 = every earlier key; W > 0 = the last W tokens up to
+ *                  the query; < 0 is PA_ERR_INVALID_ARG
  *   kernel         PA_KERNEL_AUTO or PA_KERNEL_MFMA (PA_KV_CACHED is accepted
  *                  and has no effect: every K/V row is read by several
  *                  query blocks, so the prefill always uses cached loads)
- * Sequences with T_s > n_s produce no output rows.  Supported: dtype
+ * Sequences with T_s > n_s, or whose rows leave [0, total_queries), produce
+ * no output rows.  Supported: dtype
  * PA_F16; head_dim 64 or 128; block_size 8, 16 or 32; G in {1, 2, 4, 8}.
  * num_seqs * num_kv_heads * ceil(max_query_len * G / 128) workgroups above
  * 2^24 - 1 return PA_ERR_INVALID_ARG.
@@ -275,8 +281,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
                const int32_t* query_start, int num_seqs, int total_queries,
                int num_q_heads, int num_kv_heads, int head_dim,
                int block_size, int max_blocks_per_seq, int max_query_len,
-               int64_t num_blocks, float scale, int kernel, int dtype,
-               void* stream);
+               int64_t num_blocks, float scale, int sliding_window, int kernel,
+               int dtype, void* stream);
 
 /* -------------------------------------------------------------------------
  * 3. Host block manager ([KVPA] §5.1-§5.3, §8.2; [KV2P] §6.2; [NANO] §2.3,

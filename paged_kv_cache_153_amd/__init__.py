@@ -64,7 +64,7 @@ _SIGNATURES = {
     "pa_decode_static_capacity": (_c.c_size_t, []),
     "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
-                              _c.c_int, _c.c_int, _P]),
+                              _c.c_int, _c.c_int, _c.c_int, _P]),
     "pa_stage_from_host": (_c.c_int, [_P, _P, _c.c_int64, _P]),
     "pa_stage_and_write": (_c.c_int, [_P, _P, _c.c_int64, _P, _P, _P, _P, _P, _c.c_int64, _P,
                                       _c.c_int64, _c.c_int64, _c.c_int, _c.c_int, _c.c_int,
@@ -365,16 +365,16 @@ def decode_static(out, query, kv_cache, block_tables, context_lens, scale=None,
 
 
 def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None,
-            max_query_len=None, out=None, stream=None):
+            max_query_len=None, out=None, stream=None, sliding_window=0):
     """Causal attention of multi-token query chunks over the paged cache.
 
     query [total_q, Hq, D] float16 (the chunks of all sequences, in order),
     kv_cache [NB, 2, Hkv, bs, D] float16 with the chunks' K/V already written,
     block_tables [S, MB] int32, context_lens [S] int32 (chunks included),
     query_start [S + 1] int32.  Query i of sequence s attends to the keys up
-    to its own position n_s - T_s + i.  Returns ``out`` [total_q, Hq, D]
-    float32.  ``max_query_len`` is a host bound on the chunk lengths (default
-    total_q).
+    to its own position n_s - T_s + i (with ``sliding_window`` W > 0, only
+    the last W of them).  Returns ``out`` [total_q, Hq, D] float32.
+    ``max_query_len`` is a host bound on the chunk lengths (default total_q).
     """
     torch = _torch()
     _need_cuda(query, kv_cache, block_tables, context_lens, query_start, out)
@@ -401,7 +401,7 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
                             block_tables.data_ptr(), context_lens.data_ptr(),
                             query_start.data_ptr(), s, total, hq, hkv, d, bs,
                             block_tables.shape[1], int(max_query_len), nb, float(scale),
-                            0, F16, _stream(query.device, stream)))
+                            int(sliding_window), 0, F16, _stream(query.device, stream)))
     return out
 
 

@@ -65,6 +65,7 @@ struct PrefillArgs {
   int max_tokens;           // MB * BS
   int qblocks;              // workgroups per (sequence, KV head)
   float scale_log2;
+  int window;               // > 0: a query sees the last `window` tokens up to itself
 };
 int prefill_columns_per_workgroup();
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,

@@ -573,8 +573,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int num_seqs, int total_queries, int num_q_heads,
                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-               int max_query_len, int64_t num_blocks, float scale, int kernel, int dtype,
-               void* stream_) {
+               int max_query_len, int64_t num_blocks, float scale, int sliding_window,
+               int kernel, int dtype, void* stream_) {
   pa::clear_error();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   if (dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "prefill needs an f16 pool");
@@ -583,6 +583,7 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
       num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARG, "sizes out of range");
   if (num_q_heads % num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_q_heads % num_kv_heads");
+  if (sliding_window < 0) return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0");
   const int group = num_q_heads / num_kv_heads;
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim");
   if (block_size != 8 && block_size != 16 && block_size != 32)
@@ -627,6 +628,7 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   if ((long long)num_seqs * a.qblocks * num_kv_heads > pa::kMaxGridWorkgroups)
     return fail(PA_ERR_INVALID_ARG, "grid too large");
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.window = sliding_window;
   const int rc = pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);
   if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));

@@ -5,8 +5,9 @@
 // chunked prefill) has its K/V written to the cache first; query i sits at
 // position p = n - T + i and attends to the keys t <= p (the causal mask of
 // [INFRA] "大模型 (LLM) 推理加速核心技术解析" §2, aligned to the end of the
-// context).  Addressing is the paged one of the decode ([KVPA] "KV Cache与
-// PagedAttention深度解析" §4.3): token t is row t % BS of block
+// context); under a sliding window of W tokens ([KV2P] §7.2) only to
+// p - W < t <= p.  Addressing is the paged one of the decode ([KVPA] "KV
+// Cache与PagedAttention深度解析" §4.3): token t is row t % BS of block
 // block_tables[s, t / BS].
 //
 // Columns are (query token, head) pairs of one KV head, head fastest; a wave
@@ -126,18 +127,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const int wg_tok0 = qb * (COLS_WG / G);
   if (T > n || wg_tok0 >= T) return;
   const int wg_last = min(T - 1, wg_tok0 + COLS_WG / G - 1);
+  // the workgroup's keys: from the first window start of its columns (0
+  // without a window) to its last column's position; steps are absolute
+  const int win = a.window;
+  const int wg_lo = win > 0 ? max(0, n - T + wg_tok0 + 1 - win) : 0;
+  const int st0 = wg_lo / kKeys;
   const int nsteps = (n - T + wg_last) / kKeys + 1;
 
   // this wave's columns: token w_tok0 + (16 cb + col) / G, head col % G
   const int w_tok0 = wg_tok0 + w * TOK_W;
   const int w_pmax = w_tok0 < T ? n - T + min(T - 1, w_tok0 + TOK_W - 1) : -1;
   const int w_pmin = w_tok0 + TOK_W - 1 < T ? n - T + w_tok0 : -1;
+  // keys below the window start of the wave's last column need the mask
+  const int w_lomax = win > 0 && w_pmax >= 0 ? max(0, w_pmax + 1 - win) : 0;
   const int hh = col % G;
-  int tok[CB], p_col[CB];
+  int tok[CB], p_col[CB], lo_col[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     tok[cb] = w_tok0 + (16 * cb + col) / G;
     p_col[cb] = tok[cb] < T ? n - T + tok[cb] : -1;  // last key the column sees
+    lo_col[cb] = win > 0 ? max(0, p_col[cb] + 1 - win) : 0;  // and its first
   }
 
   // ---- q as the B operand: lane (quad, col), chunk 4j + quad of its row -----
@@ -162,20 +171,22 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const int lrow = lane / CPR;
   const int lch = lane % CPR;
 
-  // Step sl goes to buffer sl % kBufs.  Wave w's round j fills rows
+  // Step sl goes to buffer (sl - st0) % kBufs.  Wave w's round j fills rows
   // (4 j + w) * RPW .. + RPW - 1 of the K and the V tile: lane l lands at
   // byte 16 l of that 1 KiB piece, i.e. row + l / CPR, physical chunk
   // l % CPR, so it loads logical chunk (l % CPR) ^ (row & (CPR - 1)).  Rows
-  // past the context load row n - 1 instead (finite; their weights are 0).
-  // Steps past the last re-read it, so every step issues the same loads and
-  // the wait counts stay fixed.
+  // past the context load row n - 1 instead, rows before the workgroup's
+  // first key load row wg_lo (finite; their weights are 0): a piece's RPW
+  // rows, clamped into [wg_lo, n - 1], still lie in one block, and rows no
+  // column sees are never read.  Steps past the last re-read it, so every
+  // step issues the same loads and the wait counts stay fixed.
   constexpr int LPS = 2 * ROUNDS;  // loads per lane per step
   int ids[ROUNDS];
   auto fetch_ids = [&](int sl) {
     const int sd = min(sl, nsteps - 1);
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
-      const int k0 = min(sd * kKeys + (j * kWaves + w) * RPW, n - 1);
+      const int k0 = min(max(sd * kKeys + (j * kWaves + w) * RPW, wg_lo), n - 1);
       const int lb = k0 / BS;  // wave-uniform: the piece's rows share a block
       const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
       ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     for (int j = 0; j < ROUNDS; ++j) {
       const int piece = j * kWaves + w;
       const int r = piece * RPW + lrow;
-      const int key = min(sd * kKeys + r, n - 1);
+      const int key = min(max(sd * kKeys + r, wg_lo), n - 1);
       const int c = lch ^ (r & (CPR - 1));
       const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D);
       load_lds16(src + c * 16, &lds[b][0][piece * 1024]);            // K: swizzled
@@ -259,7 +270,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       else
         vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + r * (2 * D) + col * 8);
     }
-    const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n;
+    const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n ||
+                      st * kKeys < w_lomax;
     float y[CB][8];  // raw scores; in log2 units they are cs * y
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int t = st * kKeys + (k >> 2) * 16 + 4 * quad + (k & 3);
-          if (t > p_col[cb]) y[cb][k] = -INFINITY;
+          if (t > p_col[cb] || t < lo_col[cb]) y[cb][k] = -INFINITY;
         }
       }
       const float lm = cs * fmaxf(fmaxf(fmaxf(y[cb][0], y[cb][1]), fmaxf(y[cb][2], y[cb][3])),
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     }
   };
 
-  // ---- steps 0 .. nsteps - 1 ----------------------------------------------
+  // ---- steps st0 .. nsteps - 1 --------------------------------------------
   // Iteration st: wait until step st + 1 has landed (own loads, then the
   // barrier for everyone's), issue step st + kAhead into the buffer step
   // st - 1 used, then run q.K of step st + 1 on the matrix cores while the
@@ -365,13 +377,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  fetch_ids(0);
-  issue(0, I0{});
-  fetch_ids(1);
-  issue(1, I1{});
-  fetch_ids(2);
-  issue(2, I2{});
-  fetch_ids(3);
+  fetch_ids(st0);
+  issue(st0, I0{});
+  fetch_ids(st0 + 1);
+  issue(st0 + 1, I1{});
+  fetch_ids(st0 + 2);
+  issue(st0 + 2, I2{});
+  fetch_ids(st0 + 3);
   vm_wait(std::integral_constant<int, 2 * LPS>{});
   barrier();
   float4_t sc[CB][2];
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       }
     }
   };
-  for (int st = 0; st < nsteps; st += kBufs) {  // fixed buffers in each trip
+  for (int st = st0; st < nsteps; st += kBufs) {  // fixed buffers in each trip
     step(st, I0{});
     if (st + 1 < nsteps) step(st + 1, I1{});
     if (st + 2 < nsteps) step(st + 2, I2{});

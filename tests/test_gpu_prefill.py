@@ -253,3 +253,105 @@ def test_peaked_scores_move_the_reference(device, bs, hq, hkv, kind):
     got = run(x, q, qs, device)
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= TOL
+
+
+# --------------------------------------------------------------------------
+# sliding window ([KV2P] §7.2 at every query position)
+# --------------------------------------------------------------------------
+def poison_before_windows(x, chunks, window):
+    """NaN in every pool row of sequence s before the window of its first
+    query, t < max(0, n - T - W + 1): no query of the chunk may read them
+    (the blocks of different sequences are disjoint in these inputs)."""
+    bs = x.block_size
+    for s, (n, T) in enumerate(zip(x.context_lens.tolist(), chunks)):
+        lo = max(0, n - T - window + 1) if T else n
+        for t0 in range(0, lo, bs):
+            b = int(x.block_tables[s, t0 // bs])
+            x.kv_cache[b, :, :, :min(bs, lo - t0)] = float("nan")
+
+
+@pytest.mark.parametrize("window", [1, 7, 32, 100, 333])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 8), (128, 16, 4), (128, 32, 4)])
+def test_window_ragged_chunks(device, window, bs, d, hq, hkv):
+    lens = [1, 17, 40, 100, 33, 300, 64, 700]
+    chunks = [1, 17, 9, 100, 1, 37, 64, 129]
+    x, q, qs = make(lens, chunks, hq, hkv, d, bs, seed=window + bs + hq)
+    poison_before_windows(x, chunks, window)
+    print(f"  prefill window={window} bs={bs} d={d} {hq}/{hkv}", flush=True)
+    want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                              x.context_lens.numpy(), qs, x.scale, window=window)
+    assert np.isfinite(want).all()
+    got = run(x, q, qs, device, sliding_window=window)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL
+
+
+def test_window_one_is_each_querys_value_row(device):
+    """W = 1: each query weighs its own token alone, so its output is that
+    token's V row (to float32 rounding: the kernel's softmax reference is a
+    rounded product, so the lone weight is 2^7 only to within an ulp)."""
+    lens, chunks = [40, 100, 16], [40, 7, 16]
+    x, q, qs = make(lens, chunks, 16, 4, 128, 16, seed=81)
+    got = run(x, q, qs, device, sliding_window=1)
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        for i in range(T):
+            p = n - T + i
+            b = int(x.block_tables[s, p // 16])
+            for h in range(16):
+                row = x.kv_cache[b, 1, h // 4, p % 16].double().numpy()
+                assert np.abs(got[qs[s] + i, h] - row).max() <= 1e-5, (s, i, h)
+
+
+def test_window_at_least_context_equals_plain_causal(device):
+    lens, chunks = [37, 160, 511, 512], [37, 20, 100, 1]
+    x, q, qs = make(lens, chunks, 32, 8, 128, 16, seed=82)
+    a = run(x, q, qs, device)
+    b = run(x, q, qs, device, sliding_window=512)
+    c = run(x, q, qs, device, sliding_window=100000)
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert np.abs(a - ref(x, q, qs)).max() <= TOL
+
+
+def test_window_single_token_chunks_match_windowed_decode(device):
+    x, q, qs = make([50, 7, 129, 1000], [1, 1, 1, 1], 32, 8, 128, 16, seed=83)
+    for w in (1, 16, 100):
+        got = run(x, q, qs, device, sliding_window=w)
+        dec = pa.decode(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
+                        x.context_lens.to(device), scale=x.scale, partition_size=-1,
+                        sliding_window=w)
+        torch.cuda.synchronize()
+        assert np.abs(got - dec.cpu().numpy()).max() <= 1e-5
+        want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                                  x.context_lens.numpy(), qs, x.scale, window=w)
+        assert np.abs(got - want).max() <= TOL
+
+
+@pytest.mark.parametrize("window", [1024, 4096])
+def test_window_long_chunk_70b_heads(device, window):
+    """A 1536-token chunk at context 6000 and a fresh 2000-token prompt, 64 q
+    / 8 KV heads, windows shorter and longer than the chunk; rows before
+    every window poisoned; sampled rows (first, last and random) against
+    the oracle."""
+    lens, chunks = [6000, 2000], [1536, 2000]
+    x = synth.make_decode_inputs(lens, 64, 8, 128, 16, dtype="f16", seed=84, device=device,
+                                 fill_unused=float("nan"))
+    poison_before_windows(x, chunks, window)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = synth.normal((int(qs[-1]), 64, 128), torch.float16, synth._gen(85, device), device)
+    out = pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=max(chunks),
+                     sliding_window=window)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(window)
+    for s in range(2):
+        n, T = lens[s], chunks[s]
+        nblk = -(-n // 16)
+        blocks = x.kv_cache[x.block_tables[s, :nblk].long()].cpu().numpy()
+        for i in [0, T - 1] + rng.integers(0, T, 6).tolist():
+            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
+                                      np.arange(nblk)[None], np.array([n - T + i + 1]),
+                                      np.array([0, 1]), x.scale, window=window)
+            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
+            assert err <= TOL, (s, i, err)

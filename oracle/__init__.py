@@ -28,7 +28,8 @@ Modules:
 * ``block_manager``  — a dict/list model of the host block manager.
 * ``kv_size``        — closed forms for KV-cache sizes and block counts.
 * ``quant``          — INT8 KV cache with one scale per 128-element group:
-                       quantise on write, decode over the dequantised pool.
+                       quantise on write, decode and prefill over the
+                       dequantised pool.
 
 Every function in these modules is pinned by a ``-m "not gpu"`` test against
 something other than itself (closed forms, worked examples printed on the
@@ -39,7 +40,8 @@ pages, library routines on contiguous data, invariants).  No function is
 from .attention import decode_ref, gather_sequence, split_ref, merge_ref, prefill_ref
 from .cache import cache_write_ref
 from .block_manager import BlockManagerModel, BlockManagerError
-from .quant import (quantize_rows_ref, dequantize_ref, cache_write_i8_ref, decode_i8_ref)
+from .quant import (quantize_rows_ref, dequantize_ref, cache_write_i8_ref, decode_i8_ref,
+                    prefill_i8_ref)
 from . import kv_size
 
 __all__ = [
@@ -56,4 +58,5 @@ __all__ = [
     "dequantize_ref",
     "cache_write_i8_ref",
     "decode_i8_ref",
+    "prefill_i8_ref",
 ]

@@ -27,14 +27,16 @@ Readings (the pages give no formula)
   ``x / scale`` are correctly rounded float32 divisions of the float16 inputs
   widened to float32.  Dequantisation and everything after it is float64.
 * Decode over an INT8 cache is decode attention over the dequantised cache:
-  quantisation changes which values are stored, not what is computed.
+  quantisation changes which values are stored, not what is computed.  The
+  same holds for multi-token (chunked prefill) queries, which the page also
+  runs over the cache ([KV2P] §5.4).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode_ref
+from .attention import decode_ref, prefill_ref
 
 QMAX = 127
 
@@ -95,3 +97,12 @@ def decode_i8_ref(q, kv_codes, kv_scales, block_tables, context_lens, scale, win
     per_row = np.swapaxes(np.asarray(kv_scales), 1, 2)    # -> [NB, 2, Hkv, bs], as the codes
     return decode_ref(q, dequantize_ref(kv_codes, per_row), block_tables, context_lens, scale,
                       window=window)
+
+
+def prefill_i8_ref(q, kv_codes, kv_scales, block_tables, context_lens, query_start, scale,
+                   window=0):
+    """Causal multi-token attention (``attention.prefill_ref``) over the
+    dequantised INT8 pool (float64); scales [NB, Hkv, 2, bs]."""
+    per_row = np.swapaxes(np.asarray(kv_scales), 1, 2)    # -> [NB, 2, Hkv, bs], as the codes
+    return prefill_ref(q, dequantize_ref(kv_codes, per_row), block_tables, context_lens,
+                       query_start, scale, window=window)

@@ -647,3 +647,44 @@ def prefill_window_one_is_own_value_row(prefill):
         if not (np.array_equal(out[i, 0], row) and np.array_equal(out[i, 1], row)):
             return False
     return True
+
+
+def i8_prefill_is_masked_sdpa_on_dequantised(prefill_i8, window=0, seed=18):
+    """Chunked prefill over the INT8 pool equals SDPA over the dequantised
+    contiguous K/V of each sequence with the end-aligned causal mask (cut to
+    the last W tokens under a window), the codes and scales read through a
+    random table: codes [block, K|V, head, row], scales [block, head, K|V,
+    row]."""
+    rng = np.random.default_rng(seed)
+    lens, chunks, hq, hkv, d, bs = (40, 17, 64, 9), (40, 5, 20, 1), 8, 2, 16, 8
+    nbs = [-(-n // bs) for n in lens]
+    nb = sum(nbs) + 2
+    codes = rng.integers(-127, 128, (nb, 2, hkv, bs, d)).astype(np.int8)
+    scales = rng.uniform(0.001, 0.05, (nb, hkv, 2, bs)).astype(np.float32)
+    perm = rng.permutation(nb)
+    tables = np.full((len(lens), max(nbs)), -1)
+    pos = 0
+    for s, k in enumerate(nbs):
+        tables[s, :k] = perm[pos:pos + k]
+        pos += k
+    qstart = np.concatenate([[0], np.cumsum(chunks)])
+    q = rng.standard_normal((int(qstart[-1]), hq, d))
+    out = prefill_i8(q, codes, scales, tables, np.array(lens), qstart, 0.3, window=window)
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        t = np.arange(n)
+        blk = tables[s][t // bs]
+        kk = codes[blk, 0, :, t % bs, :].astype(np.float64) * scales[blk, :, 0, t % bs][..., None]
+        vv = codes[blk, 1, :, t % bs, :].astype(np.float64) * scales[blk, :, 1, t % bs][..., None]
+        kt = torch.from_numpy(kk).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        vt = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(hq // hkv, dim=0)
+        qt = torch.from_numpy(q[qstart[s]:qstart[s + 1]]).permute(1, 0, 2)
+        p = (n - T + torch.arange(T))[:, None]
+        allowed = torch.arange(n)[None, :] <= p
+        if window > 0:
+            allowed &= torch.arange(n)[None, :] > p - window
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed,
+                                                               scale=0.3)
+        if not np.allclose(out[qstart[s]:qstart[s + 1]], ref.permute(1, 0, 2).numpy(),
+                           rtol=0, atol=1e-12):
+            return False
+    return True

@@ -381,3 +381,24 @@ def test_prefill_window_pins_catch(mistake):
 def test_prefill_window_pins_pass_clean_copy():
     assert not _prefill_window_pins_fail(prefill_mutant(None))
     assert not _prefill_window_pins_fail(oracle.prefill_ref)
+
+
+def i8_prefill_mutant(mistake):
+    """The INT8 prefill as the dequantised pool's prefill, with a planted
+    mistake in how the scales are read."""
+    def prefill(q, codes, scales, bt, cl, qstart, scale, window=0):
+        sc = np.asarray(scales)
+        if mistake == "scales_swapped":            # K and V scales exchanged
+            sc = sc[:, :, ::-1, :]
+        per_row = np.swapaxes(sc, 1, 2)
+        if mistake == "scales_as_codes_layout":    # [NB, 2, Hkv, bs] read as [NB, Hkv, 2, bs]
+            per_row = sc.reshape(sc.shape[0], sc.shape[2], sc.shape[1], sc.shape[3])
+        return oracle.prefill_ref(q, oracle.dequantize_ref(codes, per_row), bt, cl, qstart,
+                                  scale, window=window)
+    return prefill
+
+
+@pytest.mark.parametrize("mistake", ["scales_swapped", "scales_as_codes_layout"])
+def test_i8_prefill_pins_catch(mistake):
+    assert not pins.i8_prefill_is_masked_sdpa_on_dequantised(i8_prefill_mutant(mistake))
+    assert pins.i8_prefill_is_masked_sdpa_on_dequantised(i8_prefill_mutant(None))

@@ -84,3 +84,23 @@ def test_i8_decode_close_to_fp16_decode():
     a = oracle.decode_ref(args[0], kv, *args[1:])
     b = oracle.decode_i8_ref(args[0], codes, np.swapaxes(scales, 1, 2), *args[1:])
     assert np.abs(a - b).max() < 0.05 and not np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("window", [0, 1, 6, 30])
+def test_i8_prefill_is_masked_sdpa_on_dequantised_contiguous(window):
+    assert pins.i8_prefill_is_masked_sdpa_on_dequantised(oracle.prefill_i8_ref, window)
+
+
+def test_i8_prefill_single_token_is_i8_decode():
+    """T = 1 per sequence is the INT8 decode, exactly (with and without a
+    window)."""
+    rng = np.random.default_rng(19)
+    codes = rng.integers(-127, 128, (12, 2, 2, 8, 16)).astype(np.int8)
+    scales = rng.uniform(0.01, 0.1, (12, 2, 2, 8)).astype(np.float32)
+    bt = np.array([[3, 1, 7], [4, 0, 11]])
+    lens = np.array([20, 9])
+    q = rng.standard_normal((2, 4, 16))
+    for w in (0, 4, 15):
+        assert np.array_equal(
+            oracle.prefill_i8_ref(q, codes, scales, bt, lens, np.array([0, 1, 2]), 0.5, window=w),
+            oracle.decode_i8_ref(q, codes, scales, bt, lens, 0.5, window=w))

@@ -138,8 +138,11 @@ KERNEL_SOURCES = {
     "decode_valu": ["decode_valu.hip"] + _DECODE_COMMON,
     "decode_mfma": ["decode_mfma.hip"] + _DECODE_COMMON,
     "decode_valu_i8": ["decode_valu_i8.hip"] + _DECODE_COMMON,
-    "decode_mfma_i8": ["decode_mfma_i8.hip"] + _DECODE_COMMON,
-    "prefill_mfma": ["prefill_mfma.hip", "device_common.h", "kernels.h", "pa_api.cpp"],
+    "decode_mfma_i8": ["decode_mfma_i8.hip", "i8_codes.h"] + _DECODE_COMMON,
+    "prefill_mfma": ["prefill_mfma.hip", "prefill_common.h", "device_common.h", "kernels.h",
+                     "pa_api.cpp"],
+    "prefill_mfma_i8": ["prefill_mfma_i8.hip", "prefill_common.h", "i8_codes.h",
+                        "device_common.h", "kernels.h", "pa_api.cpp"],
 }
 
 
@@ -675,6 +678,9 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
         raise SystemExit("prefill needs a float16 workload and chunk <= context")
     x = synth.make_decode_inputs([n] * S, Hq, Hkv, D, bs, dtype="f16", seed=args.seed,
                                  device=dev, std=w["std"])
+    int8 = args.kv_dtype == "i8"
+    if int8:
+        x = synth.int8_pool(x)
     g = synth._gen(args.seed + 7, dev)
     q = synth.normal((S * T, Hq, D), torch.float16, g, dev, w["std"])
     new_k = synth.normal((S * T, Hkv, D), torch.float16, g, dev, w["std"])
@@ -691,11 +697,11 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
     flops = 4.0 * D * Hq * keys
 
     def step(ev=None):
-        pa.cache_write(new_k, new_v, x.kv_cache, slots)
+        pa.cache_write(new_k, new_v, x.kv_cache, slots, kv_scales=x.kv_scales)
         if ev:
             ev[0].record()
         pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens, qstart, scale=x.scale,
-                   max_query_len=T, out=out, sliding_window=win)
+                   max_query_len=T, out=out, sliding_window=win, kv_scales=x.kv_scales)
         if ev:
             ev[1].record()
 
@@ -719,12 +725,14 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
         for s_ in (0, S - 1):
             ids = x.block_tables[s_, :-(-n // bs)].long()
             blocks = x.kv_cache[ids].cpu().numpy()
+            scl = x.kv_scales[ids].cpu().numpy() if int8 else None
             for i in (0, T - 1, int(rng.integers(T))):
                 row = s_ * T + i
-                want = oracle.prefill_ref(q[row:row + 1].cpu().numpy(), blocks,
-                                          np.arange(blocks.shape[0])[None],
-                                          np.array([n - T + i + 1]), np.array([0, 1]), x.scale,
-                                          window=win)
+                args_ = (q[row:row + 1].cpu().numpy(), blocks)
+                rest = (np.arange(blocks.shape[0])[None], np.array([n - T + i + 1]),
+                        np.array([0, 1]), x.scale)
+                want = (oracle.prefill_i8_ref(*args_, scl, *rest, window=win) if int8 else
+                        oracle.prefill_ref(*args_, *rest, window=win))
                 errs.append(float(np.abs(out[row].cpu().numpy() - want[0]).max()))
         parity = max(errs)
     log(f"[bench] prefill step {wall / steps * 1e6:.1f} us, attention {att_s * 1e6:.1f} us, "
@@ -732,19 +740,23 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
     # HBM bytes the kernel must move at least: every K/V row of the
     # contexts once, the queries, the outputs
     rows_read = min(n, T + win - 1) if win > 0 else n     # keys some query of a chunk sees
-    unique = S * rows_read * Hkv * 2 * D * 2 + S * T * Hq * D * (2 + 4)
-    ratio, prof = measured_traffic_ratio("prefill_mfma", f"prefill_{workload}")
+    row_bytes = 2 * D + 8 if int8 else 2 * D * 2           # K + V of one (token, KV head)
+    unique = S * rows_read * Hkv * row_bytes + S * T * Hq * D * (2 + 4)
+    kname = "prefill_mfma_i8" if int8 else "prefill_mfma"
+    ratio, prof = measured_traffic_ratio(kname, f"prefill_{workload}" + ("_i8" if int8 else ""))
     res = {
         "metric": "chunked-prefill attention TFLOP/s (q.K and P.V, useful flops)",
         "value": round(flops * steps / wall / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(wall / steps * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8" if int8 else "f16",
         "data": "synthetic (seeded N(0, std^2) K/V/Q; no weights)",
         "config": {"workload": f"{w['desc']}: {S} seqs, chunk {T} at context {n} (past {n - T})"
                                + (f", sliding window {win}" if win > 0 else ""),
                    "sliding_window": win or None,
+                   "kv_cache": "int8 codes + f32 row scales" if int8 else "f16",
                    "num_seqs": S, "chunk": T, "context": n, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": bs,
                    "step": "pa_cache_write (chunk rows) + pa_prefill"},
@@ -758,7 +770,8 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
                      # profile's ratio to the unique bytes, times this line's
                      "traffic": round(ratio * unique) if ratio else None},
         "traffic_profile": prof,
-        "cpu_baseline": prefill_cpu_baseline(q, x, S, T, n, window=win) if cpu else None,
+        "cpu_baseline": (prefill_cpu_baseline(q, x, S, T, n, window=win)
+                         if cpu and not int8 else None),
     }
     del x, q, new_k, new_v, out
     torch.cuda.empty_cache()

@@ -257,7 +257,10 @@ size_t pa_decode_static_capacity(void);
  *
  *   out            device, [total_queries, num_q_heads, head_dim] float32
  *   query          device, [total_queries, num_q_heads, head_dim] binary16
- *   kv_cache       device, binary16 pool as for pa_cache_write
+ *   kv_cache       device, binary16 or PA_I8 pool as for pa_cache_write
+ *   kv_scales      PA_I8: the row scales written by pa_cache_write ([KV2P]
+ *                  §5.2; K_t and V_t are then code * scale of their rows);
+ *                  NULL otherwise
  *   block_tables   device, [num_seqs, max_blocks_per_seq] int32
  *   context_lens   device, [num_seqs] int32, T_s <= n_s <= max_blocks * bs
  *   query_start    device, [num_seqs + 1] int32, non-decreasing, from 0 to
@@ -272,12 +275,14 @@ size_t pa_decode_static_capacity(void);
  *                  query blocks, so the prefill always uses cached loads)
  * Sequences with T_s > n_s, or whose rows leave [0, total_queries), produce
  * no output rows.  Supported: dtype
- * PA_F16; head_dim 64 or 128; block_size 8, 16 or 32; G in {1, 2, 4, 8}.
+ * PA_F16 or PA_I8; head_dim 64 or 128; block_size 8, 16 or 32; G in
+ * {1, 2, 4, 8}.
  * num_seqs * num_kv_heads * ceil(max_query_len * G / 128) workgroups above
  * 2^24 - 1 return PA_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
 int pa_prefill(float* out, const void* query, const void* kv_cache,
-               const int32_t* block_tables, const int32_t* context_lens,
+               const float* kv_scales, const int32_t* block_tables,
+               const int32_t* context_lens,
                const int32_t* query_start, int num_seqs, int total_queries,
                int num_q_heads, int num_kv_heads, int head_dim,
                int block_size, int max_blocks_per_seq, int max_query_len,

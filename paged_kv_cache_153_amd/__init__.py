@@ -62,7 +62,7 @@ _SIGNATURES = {
                                     _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64,
                                     _c.c_float, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P]),
     "pa_decode_static_capacity": (_c.c_size_t, []),
-    "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+    "pa_prefill": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                               _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_float,
                               _c.c_int, _c.c_int, _c.c_int, _P]),
     "pa_stage_from_host": (_c.c_int, [_P, _P, _c.c_int64, _P]),
@@ -365,7 +365,7 @@ def decode_static(out, query, kv_cache, block_tables, context_lens, scale=None,
 
 
 def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None,
-            max_query_len=None, out=None, stream=None, sliding_window=0):
+            max_query_len=None, out=None, stream=None, sliding_window=0, kv_scales=None):
     """Causal attention of multi-token query chunks over the paged cache.
 
     query [total_q, Hq, D] float16 (the chunks of all sequences, in order),
@@ -375,6 +375,8 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
     to its own position n_s - T_s + i (with ``sliding_window`` W > 0, only
     the last W of them).  Returns ``out`` [total_q, Hq, D] float32.
     ``max_query_len`` is a host bound on the chunk lengths (default total_q).
+    An int8 ``kv_cache`` needs its row scales ``kv_scales`` (written by
+    ``cache_write``).
     """
     torch = _torch()
     _need_cuda(query, kv_cache, block_tables, context_lens, query_start, out)
@@ -383,8 +385,9 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
     s = block_tables.shape[0]
     if two != 2 or dq != d:
         raise ValueError("query/kv_cache shape mismatch")
-    if query.dtype != torch.float16 or kv_cache.dtype != torch.float16:
-        raise TypeError("prefill takes float16 query and pool")
+    if query.dtype != torch.float16 or kv_cache.dtype not in (torch.float16, torch.int8):
+        raise TypeError("prefill takes a float16 query and a float16 or int8 pool")
+    sp = _scales_ptr(kv_cache, kv_scales)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or \
             query_start.dtype != torch.int32 or context_lens.shape != (s,) or \
             query_start.shape != (s + 1,):
@@ -397,11 +400,12 @@ def prefill(query, kv_cache, block_tables, context_lens, query_start, scale=None
         out = torch.empty((total, hq, d), dtype=torch.float32, device=query.device)
     elif out.dtype != torch.float32 or out.shape != (total, hq, d):
         raise TypeError("out must be float32 [total_q, Hq, D]")
-    _check(lib().pa_prefill(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(),
+    _check(lib().pa_prefill(out.data_ptr(), query.data_ptr(), kv_cache.data_ptr(), sp,
                             block_tables.data_ptr(), context_lens.data_ptr(),
                             query_start.data_ptr(), s, total, hq, hkv, d, bs,
                             block_tables.shape[1], int(max_query_len), nb, float(scale),
-                            int(sliding_window), 0, F16, _stream(query.device, stream)))
+                            int(sliding_window), 0, _dtype_code(kv_cache),
+                            _stream(query.device, stream)))
     return out
 
 

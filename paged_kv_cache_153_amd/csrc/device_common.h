@@ -150,6 +150,13 @@ __device__ __forceinline__ void load_lds16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 #endif
 }
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes
+// land at byte 4 l of `dst`.
+__device__ __forceinline__ void load_lds4(const void* src, void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+#endif
+}
 
 // Max over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
 // rows), result in all four.  v_permlane32_swap exchanges the upper half of
@@ -172,6 +179,15 @@ __device__ __forceinline__ float rows4_max(float x) {
   float c = fmaxf(a, b), d = c;
   permlane16_swap(c, d);
   return fmaxf(c, d);
+}
+
+// Sum over the same four lanes, result in all four.
+__device__ __forceinline__ float rows4_sum(float x) {
+  float a = x, b = x;
+  permlane32_swap(a, b);
+  float c = a + b, d = c;
+  permlane16_swap(c, d);
+  return c + d;
 }
 
 // True when any lane of the wave has `pred` set (wave-uniform).

@@ -52,7 +52,8 @@ struct DecodeArgs {
 struct PrefillArgs {
   float* out;               // [total_q, Hq, D]
   const void* q;            // [total_q, Hq, D] f16
-  const void* kv;           // [NB, 2, Hkv, BS, D] f16
+  const void* kv;           // [NB, 2, Hkv, BS, D] f16 (or int8 codes)
+  const float* kv_scales;   // INT8 pool: [NB, Hkv, 2, BS] row scales; else null
   const int32_t* bt;        // [S, MB]
   const int32_t* cl;        // [S] context lengths, chunk included
   const int32_t* qstart;    // [S + 1] first query row of each sequence
@@ -70,6 +71,9 @@ struct PrefillArgs {
 int prefill_columns_per_workgroup();
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream);
+// INT8 pool (codes + row scales; query in f16).
+int launch_prefill_mfma_i8(const PrefillArgs& a, int head_dim, int block_size, int group,
+                           hipStream_t stream);
 
 // Each returns 0 on success, 1 if the (dtype, D, BS, G) combination has no
 // instantiation, or 2 if the launch failed (hipGetLastError has the code).

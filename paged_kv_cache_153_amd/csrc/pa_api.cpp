@@ -569,7 +569,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   return PA_OK;
 }
 
-int pa_prefill(float* out, const void* query, const void* kv_cache,
+int pa_prefill(float* out, const void* query, const void* kv_cache, const float* kv_scales,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int num_seqs, int total_queries, int num_q_heads,
                int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
@@ -577,7 +577,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
                int kernel, int dtype, void* stream_) {
   pa::clear_error();
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-  if (dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "prefill needs an f16 pool");
+  if (dtype != PA_F16 && dtype != PA_I8)
+    return fail(PA_ERR_UNSUPPORTED, "prefill needs an f16 or INT8 pool");
   if (num_seqs < 0 || total_queries < 0 || max_query_len < 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
       num_blocks <= 0)
@@ -602,6 +603,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
     return fail(PA_ERR_INVALID_ARG, "null device pointer");
   if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache))
     return fail(PA_ERR_INVALID_ARG, "out/query/kv_cache must be 16-byte aligned");
+  if (dtype == PA_I8 ? (!kv_scales || !aligned16(kv_scales)) : kv_scales != nullptr)
+    return fail(PA_ERR_INVALID_ARG, "kv_scales: 16-byte aligned for INT8 pools, NULL otherwise");
   if (pa::check_mode()) {
     if (int st = pa::check_prefill_arrays(block_tables, context_lens, query_start, num_seqs,
                                           total_queries, max_query_len, max_blocks_per_seq,
@@ -612,6 +615,7 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
   a.out = out;
   a.q = query;
   a.kv = kv_cache;
+  a.kv_scales = kv_scales;
   a.bt = block_tables;
   a.cl = context_lens;
   a.qstart = query_start;
@@ -629,7 +633,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache,
     return fail(PA_ERR_INVALID_ARG, "grid too large");
   a.scale_log2 = scale * 1.4426950408889634f;
   a.window = sliding_window;
-  const int rc = pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);
+  const int rc = dtype == PA_I8 ? pa::launch_prefill_mfma_i8(a, head_dim, block_size, group, stream)
+                                : pa::launch_prefill_mfma(a, head_dim, block_size, group, stream);
   if (rc == 1) return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (rc == 2) return fail(PA_ERR_HIP, hipGetErrorString(hipGetLastError()));
   return PA_OK;

@@ -40,46 +40,24 @@
 // the row, so that the 16 lanes that read one chunk of 16 different K rows
 // hit distinct banks; V rows are plain, since the lanes of a quad read one V
 // row whole (measured: an XOR swizzle by row there costs a two-way conflict).
-#include "device_common.h"
-#include "kernels.h"
+#include "prefill_common.h"
 
 #include <type_traits>
 
 namespace pa {
 namespace {
 
-// The softmax reference m of a column moves only when a score exceeds it by
-// more than kSlack (log2 units), so most steps skip the cross-lane max and
-// the rescale.  Weights are exp2(y - m + kPLog) <= 2^(kSlack + kPLog) = 2^15,
-// inside fp16 range for the hi/lo split.
-constexpr float kSlack = 8.f;
-constexpr float kPLog = 7.f;
-constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kKeys = 32;           // keys per step: two 16-key MFMA tiles
-constexpr int kBufs = 4;            // LDS step buffers
-constexpr int kAhead = 3;           // steps in flight ahead of the one computed
-
-template <int D>
-struct VRow;  // per-lane share of one V row: 16 bytes (D=128) or 8 bytes (D=64)
-template <>
-struct VRow<128> {
-  using type = u32x4_t;
-};
-template <>
-struct VRow<64> {
-  using type = u32x2_t;
-};
-
-// Byte offset of 16-byte chunk c of row r in an LDS step tile.
-template <int D>
-__device__ __forceinline__ uint32_t tile_off(int r, int c) {
-  constexpr int CPR = D / 8;  // chunks per row
-  return (uint32_t)(r * (2 * D) + ((c ^ (r & (CPR - 1))) << 4));
-}
+using prefill::kAhead;
+using prefill::kBufs;
+using prefill::kKeys;
+using prefill::kPLog;
+using prefill::kSlack;
+using prefill::kWaves;
+using prefill::tile_off;
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int CB = 2;  // 16-column blocks per wave
+  constexpr int CB = prefill::kCB;  // 16-column blocks per wave
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KS = D / 32;                 // 16x16x32 steps of q.K
   constexpr int NE = D / 16;                 // P.V blocks of 16 output rows
@@ -90,9 +68,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   static_assert(ROUNDS >= 1 && BS % RPW == 0, "a wave's load rows lie in one block");
   constexpr int TILE = kKeys * 2 * D;        // bytes of one K or V step tile
   constexpr int COLS_W = 16 * CB;            // columns per wave
-  constexpr int COLS_WG = kWaves * COLS_W;   // columns per workgroup
   constexpr int TOK_W = COLS_W / G;          // query tokens per wave
-  using vrow_t = typename VRow<D>::type;
+  using vrow_t = typename prefill::VRow<D>::type;
 
   // [buffer][K|V]: step st lives in buffer st % kBufs; its rows arrive by
   // direct global->LDS loads issued kAhead steps before it is used
@@ -103,36 +80,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const int quad = lane >> 4;
   const int col = lane & 15;
 
-  // ---- workgroup -> (sequence, KV head, column block) ----------------------
-  // Workgroups go to the 8 XCDs round robin.  Renumbered so that each XCD
-  // takes a contiguous range, every column block of one (sequence, KV head)
-  // runs on the XCD whose L2 holds that head's K/V; within a pair the
-  // latest tokens (the most keys) start first.
-  const unsigned nwg = gridDim.x, bid = blockIdx.x;
-  const unsigned per = nwg / 8u, rem = nwg % 8u, xcd = bid % 8u;
-  unsigned lid = xcd * per + (xcd < rem ? xcd : rem) + bid / 8u;
-  const int qb = a.qblocks - 1 - (int)(lid % (unsigned)a.qblocks);
-  lid /= (unsigned)a.qblocks;
-  const int g = (int)(lid % (unsigned)a.num_kv_heads);
-  const int s = (int)(lid / (unsigned)a.num_kv_heads);
-  // query rows [q0, q1) of this sequence: a chunk that is empty, runs
-  // backwards or leaves [0, total_queries) has no rows, so a bad query_start
-  // entry can never address q or out outside their buffers
-  const int q0 = a.qstart[s];
-  const int q1 = a.qstart[s + 1];
-  if (q0 < 0 || q1 <= q0 || q1 > a.total_queries) return;  // the whole workgroup
-  const int T = q1 - q0;
-  int n = a.cl[s];
-  n = n < 0 ? 0 : (n > a.max_tokens ? a.max_tokens : n);
-  const int wg_tok0 = qb * (COLS_WG / G);
-  if (T > n || wg_tok0 >= T) return;
-  const int wg_last = min(T - 1, wg_tok0 + COLS_WG / G - 1);
-  // the workgroup's keys: from the first window start of its columns (0
-  // without a window) to its last column's position; steps are absolute
+  // ---- workgroup -> (sequence, KV head, query block) and its keys ----------
+  prefill::Work wk;
+  if (!prefill::workgroup_work<G>(a, wk)) return;  // the whole workgroup
+  const int s = wk.s, g = wk.g, q0 = wk.q0, T = wk.T, n = wk.n;
+  const int wg_tok0 = wk.wg_tok0, wg_lo = wk.wg_lo, st0 = wk.st0, nsteps = wk.nsteps;
   const int win = a.window;
-  const int wg_lo = win > 0 ? max(0, n - T + wg_tok0 + 1 - win) : 0;
-  const int st0 = wg_lo / kKeys;
-  const int nsteps = (n - T + wg_last) / kKeys + 1;
 
   // this wave's columns: token w_tok0 + (16 cb + col) / G, head col % G
   const int w_tok0 = wg_tok0 + w * TOK_W;
@@ -463,7 +416,7 @@ int by_block(const PrefillArgs& a, int block_size, int group, hipStream_t stream
 
 }  // namespace
 
-int prefill_columns_per_workgroup() { return kWaves * 32; }
+int prefill_columns_per_workgroup() { return prefill::kColsWG; }
 
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream) {

@@ -350,11 +350,13 @@ def test_native_prefix_cache_rejects_bad_use():
 
 
 def _prefill_status(**kw):
-    args = dict(out=None, query=None, kv=None, bt=None, cl=None, qs=None, S=2, total=8, Hq=8,
+    args = dict(out=None, query=None, kv=None, sc=None, bt=None, cl=None, qs=None, S=2, total=8,
+                Hq=8,
                 Hkv=2, D=128, bs=16, MB=4, maxq=4, NB=16, scale=0.1, window=0, kernel=0,
                 dtype=1)
     args.update(kw)
-    return pa.lib().pa_prefill(args["out"], args["query"], args["kv"], args["bt"], args["cl"],
+    return pa.lib().pa_prefill(args["out"], args["query"], args["kv"], args["sc"], args["bt"],
+                               args["cl"],
                                args["qs"], args["S"], args["total"], args["Hq"], args["Hkv"],
                                args["D"], args["bs"], args["MB"], args["maxq"], args["NB"],
                                args["scale"], args["window"], args["kernel"], args["dtype"],
@@ -362,7 +364,7 @@ def _prefill_status(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=0), -2), (dict(dtype=2), -2), (dict(kernel=1), -2), (dict(D=96), -2),
+    (dict(dtype=0), -2), (dict(dtype=3), -2), (dict(kernel=1), -2), (dict(D=96), -2),
     (dict(bs=24), -2), (dict(Hq=6), -2), (dict(Hq=7), -1), (dict(kernel=0x200), -1),
     (dict(NB=0), -1), (dict(S=-1), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
     (dict(scale=float("inf")), -1), (dict(scale=float("nan")), -1), (dict(window=-1), -1),
@@ -383,6 +385,11 @@ def test_prefill_rejects_a_grid_beyond_one_launch():
 def test_prefill_null_pointers_and_empty_batch():
     fake = ctypes.c_void_p(1 << 20)
     assert _prefill_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, qs=None) == -1
+    # an INT8 pool needs its scales; an f16 pool takes none (checked before any launch)
+    assert _prefill_status(out=fake, query=fake, kv=fake, bt=fake, cl=fake, qs=fake,
+                           dtype=2) == -1
+    assert _prefill_status(out=fake, query=fake, kv=fake, sc=fake, bt=fake, cl=fake, qs=fake,
+                           dtype=1) == -1
     assert _prefill_status(S=0) == 0 and _prefill_status(total=0) == 0
 
 

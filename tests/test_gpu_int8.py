@@ -188,3 +188,146 @@ def test_full_size_every_row(device, name):
     assert_every_row(x, out, TOL)
     del x, out
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# chunked prefill over an INT8 pool ([KV2P] §5.2 cache, §5.4 chunked prefill)
+# --------------------------------------------------------------------------
+def _i8_prefill_inputs(lens, chunks, hq, hkv, d, bs, seed, window=0, scale=None, code_std=1.0):
+    """An INT8 pool whose scales are NaN outside every context and before
+    every query's window, and f16 queries of the chunks."""
+    base = synth.make_decode_inputs(lens, hq, hkv, d, bs, dtype="f16", seed=seed, scale=scale,
+                                    std=code_std)
+    x = synth.int8_pool(base, fill_unused=float("nan"))
+    if window:
+        for s, (n, T) in enumerate(zip(lens, chunks)):
+            lo = max(0, n - T - window + 1) if T else n
+            for t0 in range(0, lo, bs):
+                b = int(x.block_tables[s, t0 // bs])
+                x.kv_scales[b, :, :, :min(bs, lo - t0)] = float("nan")
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = synth.normal((int(qs[-1]), hq, d), torch.float16, synth._gen(seed + 50, "cpu"), "cpu",
+                     code_std)
+    return x, q, qs
+
+
+def _i8_prefill(x, q, qs, device, window=0):
+    g = x.to(device)
+    out = pa.prefill(q.to(device), g.kv_cache, g.block_tables, g.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale,
+                     max_query_len=max(1, int(np.diff(qs).max())), sliding_window=window,
+                     kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _i8_prefill_ref(x, q, qs, window=0):
+    return oracle.prefill_i8_ref(q.numpy(), x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                 x.block_tables.numpy(), x.context_lens.numpy(), qs, x.scale,
+                                 window=window)
+
+
+@pytest.mark.parametrize("window", [0, 7, 100])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 8), (64, 16, 2), (128, 16, 4), (128, 32, 4)])
+def test_prefill_ragged_chunks(device, window, bs, d, hq, hkv):
+    lens = [1, 17, 40, 100, 33, 300, 64, 500]
+    chunks = [1, 17, 9, 100, 1, 37, 64, 129]
+    x, q, qs = _i8_prefill_inputs(lens, chunks, hq, hkv, d, bs, seed=bs + d + hq + window,
+                                  window=window)
+    print(f"  i8 prefill W={window} bs={bs} d={d} {hq}/{hkv}", flush=True)
+    want = _i8_prefill_ref(x, q, qs, window)
+    assert np.isfinite(want).all()
+    got = _i8_prefill(x, q, qs, device, window)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL
+
+
+def test_prefill_single_token_chunks_match_i8_decode(device):
+    x, q, qs = _i8_prefill_inputs([50, 7, 129, 700], [1, 1, 1, 1], 32, 8, 128, 16, seed=91)
+    got = _i8_prefill(x, q, qs, device)
+    g = x.to(device)
+    dec = pa.decode(q.to(device), g.kv_cache, g.block_tables, g.context_lens, scale=x.scale,
+                    partition_size=-1, kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    assert np.abs(got - dec.cpu().numpy()).max() <= 1e-5
+    assert np.abs(got - _i8_prefill_ref(x, q, qs)).max() <= TOL
+
+
+def test_prefill_peaked_scores_move_the_reference(device):
+    """Scale 1 and wide values: later keys pass the first step's scores by
+    far more than 2^8, so the kernel rescales live accumulators; every row
+    against the oracle."""
+    lens, chunks = [300, 97, 700], [300, 40, 129]
+    x, q, qs = _i8_prefill_inputs(lens, chunks, 32, 4, 128, 16, seed=92, scale=1.0,
+                                  code_std=3.0)
+    k = oracle.dequantize_ref(x.kv_cache.numpy()[:, 0], x.kv_scales.numpy()[:, :, 0])
+    jumps = 0
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        t = np.arange(n)
+        blk = x.block_tables.numpy()[s][t // 16]
+        ks = k[blk, :, t % 16, :]                       # [n, Hkv, D]
+        for i in range(0, T, 7):
+            p = n - T + i
+            if p < 32:
+                continue
+            for h in range(0, 32, 5):
+                z = ks[:p + 1, h // 8] @ q[qs[s] + i, h].double().numpy() / np.log(2)
+                jumps += int(z[32:].max() > z[:32].max() + 8)
+    assert jumps >= 20
+    got = _i8_prefill(x, q, qs, device)
+    assert np.isfinite(got).all()
+    assert np.abs(got - _i8_prefill_ref(x, q, qs)).max() <= TOL
+
+
+def test_prefill_after_cache_write_of_the_chunk(device):
+    """The chunk's rows are quantised into the pool by pa_cache_write, then
+    attended to by pa_prefill; the oracle takes the same f16 rows through its
+    own quantiser and prefill."""
+    lens, chunks, bs = [200, 64, 333], [50, 64, 1], 16
+    x, q, qs = _i8_prefill_inputs(lens, chunks, 16, 4, 128, bs, seed=93)
+    rows = int(qs[-1])
+    k, v = synth.rows(rows, 4, 128, dtype="f16", seed=94)
+    bt = x.block_tables.numpy()
+    slots = []
+    for s, (n, T) in enumerate(zip(lens, chunks)):
+        for p in range(n - T, n):
+            slots.append(int(bt[s, p // bs]) * bs + p % bs)
+    slots = torch.tensor(slots, dtype=torch.int64)
+    codes, scales = oracle.cache_write_i8_ref(x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                              k.numpy(), v.numpy(), slots.numpy())
+    want = oracle.prefill_i8_ref(q.numpy(), codes, scales, bt, np.array(lens), qs, x.scale)
+    g = x.to(device)
+    pa.cache_write(k.to(device), v.to(device), g.kv_cache, slots.to(device),
+                   kv_scales=g.kv_scales)
+    out = pa.prefill(q.to(device), g.kv_cache, g.block_tables, g.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=64,
+                     kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy().astype(np.float64) - want).max() <= TOL
+
+
+@pytest.mark.parametrize("window", [0, 1024])
+def test_prefill_long_chunk_70b_heads_sampled(device, window):
+    """A 1536-token chunk at context 3000 and a fresh 700-token prompt, 64 q /
+    8 KV heads over an INT8 pool; sampled rows against the oracle."""
+    lens, chunks = [3000, 700], [1536, 700]
+    x, q, qs = _i8_prefill_inputs(lens, chunks, 64, 8, 128, 16, seed=95, window=window)
+    g = x.to(device)
+    out = pa.prefill(q.to(device), g.kv_cache, g.block_tables, g.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=1536,
+                     sliding_window=window, kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(window)
+    for s in range(2):
+        n, T = lens[s], chunks[s]
+        nblk = -(-n // 16)
+        ids = x.block_tables[s, :nblk].long()
+        for i in [0, T - 1] + rng.integers(0, T, 4).tolist():
+            want = oracle.prefill_i8_ref(q[qs[s] + i:qs[s] + i + 1].numpy(),
+                                         x.kv_cache[ids].numpy(), x.kv_scales[ids].numpy(),
+                                         np.arange(nblk)[None], np.array([n - T + i + 1]),
+                                         np.array([0, 1]), x.scale, window=window)
+            assert np.abs(got[qs[s] + i] - want[0]).max() <= TOL, (s, i)

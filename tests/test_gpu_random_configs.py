@@ -5,7 +5,8 @@ contexts, sliding window, schedule (auto, single pass, balanced, fixed
 partitions), kernel family, load policy, table width and the host bound on
 the lengths — and random causal prefill chunks (chunk lengths, pasts,
 block size, head_dim, group, value spread and softmax scale, so that peaked
-scores move the kernel's softmax reference mid-context, and sliding window).  Each case is checked against the fp64 oracle
+scores move the kernel's softmax reference mid-context, sliding window, and
+f16 or INT8 pool).  Each case is checked against the fp64 oracle
 (max-abs error <= 5e-4) with every pool row outside the keys a query may
 see poisoned with NaN (for INT8 pools, their scales), so a read outside
 them fails the case.  The draws are seeded: a failing case id names its
@@ -155,6 +156,7 @@ def draw_prefill(case):
         rng.integers(0, 2)])
     cfg["std"] = float([1.0, 0.5, 2.0, 3.0][rng.integers(0, 4)])
     cfg["window"] = 0 if rng.random() < 0.6 else int(rng.integers(1, 1000))
+    cfg["i8"] = bool(rng.random() < 0.3)
     return cfg
 
 
@@ -169,19 +171,31 @@ def test_random_prefill_config(device, case):
     total = int(qstart[-1])
     q = synth.normal((total, cfg["hq"], cfg["d"]), torch.float16, synth._gen(7100 + case, "cpu"),
                      "cpu", cfg["std"])
+    if cfg["i8"]:       # an INT8 pool: scales of rows outside every context NaN
+        x = synth.int8_pool(x, fill_unused=float("nan"))
     if cfg["window"]:   # rows before every query's window: never read
         bs = cfg["bs"]
+        poisoned = x.kv_scales if cfg["i8"] else None
         for s, (n, T) in enumerate(zip(cfg["lens"], cfg["chunks"])):
             lo = max(0, n - T - cfg["window"] + 1) if T else n
             for t0 in range(0, lo, bs):
                 b = int(x.block_tables[s, t0 // bs])
-                x.kv_cache[b, :, :, :min(bs, lo - t0)] = float("nan")
-    want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
-                              x.context_lens.numpy(), qstart, x.scale, window=cfg["window"])
-    out = pa.prefill(q.to(device), x.kv_cache.to(device), x.block_tables.to(device),
-                     x.context_lens.to(device), torch.from_numpy(qstart).to(device),
+                if poisoned is None:
+                    x.kv_cache[b, :, :, :min(bs, lo - t0)] = float("nan")
+                else:
+                    poisoned[b, :, :, :min(bs, lo - t0)] = float("nan")
+    if cfg["i8"]:
+        want = oracle.prefill_i8_ref(q.numpy(), x.kv_cache.numpy(), x.kv_scales.numpy(),
+                                     x.block_tables.numpy(), x.context_lens.numpy(), qstart,
+                                     x.scale, window=cfg["window"])
+    else:
+        want = oracle.prefill_ref(q.numpy(), x.kv_cache.numpy(), x.block_tables.numpy(),
+                                  x.context_lens.numpy(), qstart, x.scale, window=cfg["window"])
+    g = x.to(device)
+    out = pa.prefill(q.to(device), g.kv_cache, g.block_tables, g.context_lens,
+                     torch.from_numpy(qstart).to(device),
                      scale=x.scale, max_query_len=max(1, max(cfg["chunks"])),
-                     sliding_window=cfg["window"])
+                     sliding_window=cfg["window"], kv_scales=g.kv_scales)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all(), cfg

@@ -73,3 +73,56 @@ def assert_every_row(x, out, tol, window=0):
     s, h = np.unravel_index(int(np.argmax(err)), err.shape)
     assert err[s, h] <= tol, (int(s), int(h), float(err[s, h]))
     return float(err.max())
+
+
+def every_prefill_row(x, q, qstart, window=0, rows=16):
+    """Oracle output [total_q, Hq, D] float64 of a chunked prefill (``x`` and
+    ``q`` on the device; an INT8 pool when ``x.kv_scales`` is set): each
+    sequence's blocks are copied to host memory once, and its chunk is cut
+    into groups of ``rows`` query rows, each the last rows of a context that
+    ends at its last row, computed in a pool of worker threads."""
+    from threadpoolctl import threadpool_limits
+
+    bs = x.block_size
+    lens = x.context_lens.tolist()
+    host = []
+    for s, n in enumerate(lens):
+        nblk = -(-n // bs)
+        ids = x.block_tables[s, :nblk].long()
+        host.append((x.kv_cache[ids].cpu().numpy(),
+                     None if x.kv_scales is None else x.kv_scales[ids].cpu().numpy()))
+    qh = q.cpu().numpy()
+    jobs = []
+    for s, n in enumerate(lens):
+        q0, q1 = int(qstart[s]), int(qstart[s + 1])
+        T = q1 - q0
+        for i0 in range(0, T, rows):
+            jobs.append((s, n, T, q0, i0, min(T, i0 + rows)))
+
+    def one(job):
+        s, n, T, q0, i0, i1 = job
+        blocks, scales = host[s]
+        args = (np.arange(blocks.shape[0])[None], np.array([n - T + i1]),
+                np.array([0, i1 - i0]), x.scale)
+        if scales is None:
+            return oracle.prefill_ref(qh[q0 + i0:q0 + i1], blocks, *args, window=window)
+        return oracle.prefill_i8_ref(qh[q0 + i0:q0 + i1], blocks, scales, *args, window=window)
+
+    out = np.zeros(qh.shape)
+    with threadpool_limits(1), ThreadPoolExecutor(_workers()) as ex:
+        for job, res in zip(jobs, ex.map(one, jobs)):
+            s, n, T, q0, i0, i1 = job
+            out[q0 + i0:q0 + i1] = res
+    return out
+
+
+def assert_every_prefill_row(x, q, qstart, out, tol, window=0):
+    """Every row of ``out`` (device, [total_q, Hq, D]) within ``tol`` of the
+    oracle; names the worst (row, head) on failure."""
+    want = every_prefill_row(x, q, qstart, window)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max(axis=2)
+    r, h = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert err[r, h] <= tol, (int(r), int(h), float(err[r, h]))
+    return float(err.max())

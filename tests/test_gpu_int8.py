@@ -18,7 +18,7 @@ import torch
 import oracle
 import paged_kv_cache_153_amd as pa
 import synth
-from tests.full_oracle import assert_every_row
+from tests.full_oracle import assert_every_prefill_row, assert_every_row
 
 pytestmark = pytest.mark.gpu
 
@@ -308,9 +308,9 @@ def test_prefill_after_cache_write_of_the_chunk(device):
 
 
 @pytest.mark.parametrize("window", [0, 1024])
-def test_prefill_long_chunk_70b_heads_sampled(device, window):
+def test_prefill_long_chunk_70b_heads_every_row(device, window):
     """A 1536-token chunk at context 3000 and a fresh 700-token prompt, 64 q /
-    8 KV heads over an INT8 pool; sampled rows against the oracle."""
+    8 KV heads over an INT8 pool: every row against the oracle."""
     lens, chunks = [3000, 700], [1536, 700]
     x, q, qs = _i8_prefill_inputs(lens, chunks, 64, 8, 128, 16, seed=95, window=window)
     g = x.to(device)
@@ -318,16 +318,17 @@ def test_prefill_long_chunk_70b_heads_sampled(device, window):
                      torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=1536,
                      sliding_window=window, kv_scales=g.kv_scales)
     torch.cuda.synchronize()
-    got = out.cpu().numpy().astype(np.float64)
-    assert np.isfinite(got).all()
-    rng = np.random.default_rng(window)
-    for s in range(2):
-        n, T = lens[s], chunks[s]
-        nblk = -(-n // 16)
-        ids = x.block_tables[s, :nblk].long()
-        for i in [0, T - 1] + rng.integers(0, T, 4).tolist():
-            want = oracle.prefill_i8_ref(q[qs[s] + i:qs[s] + i + 1].numpy(),
-                                         x.kv_cache[ids].numpy(), x.kv_scales[ids].numpy(),
-                                         np.arange(nblk)[None], np.array([n - T + i + 1]),
-                                         np.array([0, 1]), x.scale, window=window)
-            assert np.abs(got[qs[s] + i] - want[0]).max() <= TOL, (s, i)
+    assert_every_prefill_row(g, q, qs, out, TOL, window=window)
+
+
+def test_prefill_gqa_chunk_every_row(device):
+    """The benchmarked prefill (8 x 512-token chunks at context 4096, 32 q /
+    8 KV heads) over an INT8 pool: every row against the oracle."""
+    lens, chunks = [4096] * 8, [512] * 8
+    x, q, qs = _i8_prefill_inputs(lens, chunks, 32, 8, 128, 16, seed=96)
+    g = x.to(device)
+    out = pa.prefill(q.to(device), g.kv_cache, g.block_tables, g.context_lens,
+                     torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=512,
+                     kv_scales=g.kv_scales)
+    torch.cuda.synchronize()
+    assert_every_prefill_row(g, q, qs, out, TOL)

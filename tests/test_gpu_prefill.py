@@ -2,7 +2,8 @@
 [KV2P] §5.4; causal mask for T > 1, [INFRA] §2) against the fp64 oracle,
 max-abs error <= 5e-4: ragged chunk lengths and pasts, every block size,
 head_dim and group size, chunks equal to whole prompts, T = 1 against the
-decode, and a 7B-shaped chunk on sampled outputs.  Pool rows past every
+decode, and the benchmarked 7B-shaped chunk and long 70B-head chunks on every
+output row.  Pool rows past every
 context hold NaN, so a kernel that weighs one fails."""
 
 import numpy as np
@@ -12,6 +13,7 @@ import torch
 import oracle
 import paged_kv_cache_153_amd as pa
 import synth
+from tests.full_oracle import assert_every_prefill_row
 
 pytestmark = pytest.mark.gpu
 
@@ -86,8 +88,9 @@ def test_empty_and_overlong_chunks_write_nothing(device):
     assert np.abs(out.cpu().numpy() - ref(x, q, qs)).max() <= TOL
 
 
-def test_llama7b_gqa_chunk_sampled(device):
-    """8 sequences x 512-token chunks at context 4096, 32 q / 8 KV heads."""
+def test_llama7b_gqa_chunk_every_row(device):
+    """8 sequences x 512-token chunks at context 4096, 32 q / 8 KV heads (the
+    benchmarked prefill): every row against the oracle."""
     lens, chunks = [4096] * 8, [512] * 8
     x = synth.make_decode_inputs(lens, 32, 8, 128, 16, dtype="f16", seed=64, device=device)
     qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
@@ -95,25 +98,14 @@ def test_llama7b_gqa_chunk_sampled(device):
     out = pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens,
                      torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=512)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    rng = np.random.default_rng(0)
-    for s in (0, 7, int(rng.integers(8))):
-        ids = x.block_tables[s, :256].long()
-        blocks = x.kv_cache[ids].cpu().numpy()
-        rows = [0, 511] + rng.integers(0, 512, 3).tolist()
-        for i in rows:
-            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
-                                      np.arange(256)[None], np.array([4096 - 512 + i + 1]),
-                                      np.array([0, 1]), x.scale)
-            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
-            assert err <= TOL, (s, i, err)
+    assert_every_prefill_row(x, q, qs, out, TOL)
 
 
 @pytest.mark.parametrize("bs", [8, 32])
-def test_long_chunk_70b_heads_sampled(device, bs):
+def test_long_chunk_70b_heads_every_row(device, bs):
     """A 1536-token chunk at context 3000 and a fresh 700-token prompt, 64 q /
-    8 KV heads (many query blocks per (sequence, KV head)); sampled rows,
-    including the first and last of each chunk, against the oracle."""
+    8 KV heads (many query blocks per (sequence, KV head)): every row against
+    the oracle."""
     lens, chunks = [3000, 700], [1536, 700]
     x = synth.make_decode_inputs(lens, 64, 8, 128, bs, dtype="f16", seed=66 + bs, device=device,
                                  fill_unused=float("nan"))
@@ -122,19 +114,7 @@ def test_long_chunk_70b_heads_sampled(device, bs):
     out = pa.prefill(q, x.kv_cache, x.block_tables, x.context_lens,
                      torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=max(chunks))
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    rng = np.random.default_rng(bs)
-    for s in range(2):
-        n, T = lens[s], chunks[s]
-        nblk = -(-n // bs)
-        ids = x.block_tables[s, :nblk].long()
-        blocks = x.kv_cache[ids].cpu().numpy()
-        for i in [0, T - 1] + rng.integers(0, T, 4).tolist():
-            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
-                                      np.arange(nblk)[None], np.array([n - T + i + 1]),
-                                      np.array([0, 1]), x.scale)
-            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
-            assert err <= TOL, (s, i, err)
+    assert_every_prefill_row(x, q, qs, out, TOL)
 
 
 def test_query_start_outside_total_stays_inside_buffers(device, monkeypatch):
@@ -331,8 +311,7 @@ def test_window_single_token_chunks_match_windowed_decode(device):
 def test_window_long_chunk_70b_heads(device, window):
     """A 1536-token chunk at context 6000 and a fresh 2000-token prompt, 64 q
     / 8 KV heads, windows shorter and longer than the chunk; rows before
-    every window poisoned; sampled rows (first, last and random) against
-    the oracle."""
+    every window poisoned; every row against the oracle."""
     lens, chunks = [6000, 2000], [1536, 2000]
     x = synth.make_decode_inputs(lens, 64, 8, 128, 16, dtype="f16", seed=84, device=device,
                                  fill_unused=float("nan"))
@@ -343,15 +322,4 @@ def test_window_long_chunk_70b_heads(device, window):
                      torch.from_numpy(qs).to(device), scale=x.scale, max_query_len=max(chunks),
                      sliding_window=window)
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    rng = np.random.default_rng(window)
-    for s in range(2):
-        n, T = lens[s], chunks[s]
-        nblk = -(-n // 16)
-        blocks = x.kv_cache[x.block_tables[s, :nblk].long()].cpu().numpy()
-        for i in [0, T - 1] + rng.integers(0, T, 6).tolist():
-            want = oracle.prefill_ref(q[qs[s] + i:qs[s] + i + 1].cpu().numpy(), blocks,
-                                      np.arange(nblk)[None], np.array([n - T + i + 1]),
-                                      np.array([0, 1]), x.scale, window=window)
-            err = np.abs(out[qs[s] + i].cpu().numpy().astype(np.float64) - want[0]).max()
-            assert err <= TOL, (s, i, err)
+    assert_every_prefill_row(x, q, qs, out, TOL, window=window)

@@ -376,8 +376,14 @@ int pa_bm_ref_count(const pa_bm* bm, int32_t block);
  * ------------------------------------------------------------------------- */
 
 /* Turn the prefix cache on; only on a manager that holds no sequence.
- * protect_hits >= 0. */
-int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits);
+ * protect_hits >= 0: blocks with at least that many hits are evicted last
+ * (0 = plain LRU).  admit_after >= 1: a full block enters the cache only at
+ * the admit_after-th registration of its key (its tokens and position), so
+ * prompts seen once do not push out reused ones ([KV2P] §4.3, cache
+ * pollution); keys below the threshold are remembered for at most
+ * num_blocks keys, the least recently seen forgotten first.  1 caches at the
+ * first registration.  Errors: PA_ERR_INVALID_ARG. */
+int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits, int admit_after);
 
 /* Admit a new sequence with prompt `tokens` [n] (host int32): its leading
  * full blocks that are cached are reused (one more reference each), the rest
@@ -396,12 +402,14 @@ int pa_bm_record_tokens(pa_bm* bm, int64_t seq, const int32_t* tokens,
 
 /* Cache the sequence's full blocks whose token ids are known and whose K/V
  * the caller has written (call after the write).  A block whose key is
- * already cached under another block stays private.  *newly_cached (may be
- * NULL) receives the number of blocks added. */
+ * already cached under another block, or whose key has not yet reached the
+ * admission threshold, stays private.  *newly_cached (may be NULL) receives
+ * the number of blocks added. */
 int pa_bm_register(pa_bm* bm, int64_t seq, int64_t* newly_cached);
 
-/* out[6]: cached blocks, evictable blocks, lookups, reused (hit) blocks,
- * missed full blocks, evictions. */
+/* out[7]: cached blocks, evictable blocks, lookups, reused (hit) blocks,
+ * missed full blocks, evictions, registrations held back by the admission
+ * threshold. */
 int pa_bm_prefix_stats(const pa_bm* bm, int64_t* out);
 
 /* ------------------------------------------------------------------------- */

@@ -69,10 +69,20 @@ chunk hash to the block, reuse only full blocks).
   (removed from the cache): the least recently released one, taking blocks
   with at least ``protect_hits`` hits last ([KV2P] §4.3: protect frequently
   reused prefixes against one-off requests; 0 = plain LRU).
+* Admission threshold ``admit_after`` ([KV2P] §4.3, the other remedy for
+  cache pollution: a prefix seen fewer times than a minimum does not enter
+  the cache).  Reading: a full block is cached at registration only once its
+  key (the chain hash, i.e. its tokens and position) has been registered
+  ``admit_after`` times; the earlier copies stay private.  The keys still
+  below the threshold and their counts are kept for at most ``num_blocks``
+  keys, the one seen least recently dropped first.  1 (the default) caches
+  at the first registration.
 * With the cache on, ``free`` counts free plus evictable blocks.
 """
 
 from __future__ import annotations
+
+from collections import OrderedDict
 
 FNV_OFFSET = 0xCBF29CE484222325
 FNV_PRIME = 0x100000001B3
@@ -117,6 +127,8 @@ class BlockManagerModel:
         # prefix cache
         self.cache_on = False
         self.protect_hits = 0
+        self.admit_after = 1
+        self.sightings = OrderedDict()   # key -> registrations, least recent first
         self.cache = {}        # hash -> block
         self.block_key = {}    # cached block -> (hash, parent hash, tokens)
         self.hits = [0] * self.num_blocks
@@ -124,7 +136,8 @@ class BlockManagerModel:
         self.clock = 0
         self.tokens = {}       # seq -> known token ids (a prefix of its tokens)
         self.registered = {}   # seq -> leading blocks already in the cache chain
-        self.counters = {"lookups": 0, "hit_blocks": 0, "miss_blocks": 0, "evictions": 0}
+        self.counters = {"lookups": 0, "hit_blocks": 0, "miss_blocks": 0, "evictions": 0,
+                         "held_back": 0}
 
     # -- helpers -----------------------------------------------------------
     def _need(self, seq):
@@ -232,11 +245,16 @@ class BlockManagerModel:
         del self.registered[seq]
 
     # -- prefix cache ------------------------------------------------------
-    def enable_prefix_cache(self, protect_hits=0):
-        if self.tables or protect_hits < 0:
+    def enable_prefix_cache(self, protect_hits=0, admit_after=1):
+        if self.tables or protect_hits < 0 or admit_after < 1:
             raise BlockManagerError("invalid", "enable the prefix cache on an empty manager")
         self.cache_on = True
         self.protect_hits = int(protect_hits)
+        self.admit_after = int(admit_after)
+
+    def _admission_capacity(self):
+        """Keys below the admission threshold remembered at most."""
+        return self.num_blocks
 
     def _chain(self, seq, upto):
         """Hashes of the sequence's first ``upto`` full blocks."""
@@ -301,6 +319,14 @@ class BlockManagerModel:
             b = self.tables[seq][i]
             h = hashes[i]
             if h not in self.cache and b not in self.block_key:
+                if self.admit_after > 1:
+                    seen = self.sightings.pop(h, 0) + 1
+                    if seen < self.admit_after:      # below the threshold: stays private
+                        self.sightings[h] = seen
+                        while len(self.sightings) > self._admission_capacity():
+                            self.sightings.popitem(last=False)
+                        self.counters["held_back"] += 1
+                        continue
                 parent = hashes[i - 1] if i else 0
                 toks = self.tokens[seq][i * self.block_size:(i + 1) * self.block_size]
                 self.cache[h] = b
@@ -310,10 +336,11 @@ class BlockManagerModel:
         return added
 
     def prefix_stats(self):
-        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions)."""
+        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions,
+        registrations held back by the admission threshold)."""
         c = self.counters
         return (len(self.block_key), len(self.evictable), c["lookups"], c["hit_blocks"],
-                c["miss_blocks"], c["evictions"])
+                c["miss_blocks"], c["evictions"], c["held_back"])
 
     # -- queries -----------------------------------------------------------
     def block_table(self, seq):

@@ -79,7 +79,7 @@ _SIGNATURES = {
     "pa_bm_append_slots": (_c.c_int, [_P, _P, _c.c_int, _P, _P,
                                       _c.POINTER(_c.c_int)]),
     "pa_bm_free": (_c.c_int, [_P, _c.c_int64]),
-    "pa_bm_enable_prefix_cache": (_c.c_int, [_P, _c.c_int]),
+    "pa_bm_enable_prefix_cache": (_c.c_int, [_P, _c.c_int, _c.c_int]),
     "pa_bm_allocate_prompt": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int64, _I64P]),
     "pa_bm_record_tokens": (_c.c_int, [_P, _c.c_int64, _I32P, _c.c_int64]),
     "pa_bm_register": (_c.c_int, [_P, _c.c_int64, _I64P]),
@@ -526,8 +526,8 @@ class BlockManager:
         return r
 
     # -- prefix cache --------------------------------------------------------
-    def enable_prefix_cache(self, protect_hits=0):
-        _check(lib().pa_bm_enable_prefix_cache(self._h, int(protect_hits)))
+    def enable_prefix_cache(self, protect_hits=0, admit_after=1):
+        _check(lib().pa_bm_enable_prefix_cache(self._h, int(protect_hits), int(admit_after)))
 
     def allocate_prompt(self, seq, tokens):
         """Admit a prompt (token ids); returns (block table, cached_tokens)."""
@@ -548,7 +548,8 @@ class BlockManager:
         return added.value
 
     def prefix_stats(self):
-        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions)."""
-        out = (ctypes.c_int64 * 6)()
+        """(cached, evictable, lookups, hit_blocks, miss_blocks, evictions,
+        held_back)."""
+        out = (ctypes.c_int64 * 7)()
         _check(lib().pa_bm_prefix_stats(self._h, out))
         return tuple(out)

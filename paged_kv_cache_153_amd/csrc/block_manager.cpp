@@ -25,10 +25,15 @@
 // takes a reference on each; the rest gets fresh blocks.  A cached block whose
 // count reaches 0 stays cached but evictable; fresh blocks come from the free
 // pool first, then by evicting the least recently released evictable block,
-// blocks with at least protect_hits hits last.
+// blocks with at least protect_hits hits last.  With admit_after > 1 a full
+// block enters the cache only at the admit_after-th registration of its key
+// (the other remedy [KV2P] §4.3 gives for a cache polluted by one-off
+// prompts); the keys still below that count are remembered for at most
+// num_blocks keys, the one seen least recently forgotten first.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <list>
 #include <new>
 #include <set>
 #include <tuple>
@@ -59,6 +64,11 @@ struct pa_bm {
   // prefix cache
   bool cache_on = false;
   int protect_hits = 0;
+  int admit_after = 1;
+  // keys registered fewer than admit_after times: (key, count), least
+  // recently seen first, and where each key sits in that list
+  std::list<std::pair<uint64_t, int>> sightings;
+  std::unordered_map<uint64_t, std::list<std::pair<uint64_t, int>>::iterator> sighting_at;
   std::unordered_map<uint64_t, int32_t> cache;
   std::vector<Key> keys;
   std::vector<int64_t> hits;
@@ -66,7 +76,29 @@ struct pa_bm {
   std::vector<uint64_t> ev_clock;
   std::vector<int> ev_prot;
   uint64_t clock = 0;
-  int64_t lookups = 0, hit_blocks = 0, miss_blocks = 0, evictions = 0;
+  int64_t lookups = 0, hit_blocks = 0, miss_blocks = 0, evictions = 0, held_back = 0;
+
+  // Counts one more registration of key h; true once it reaches admit_after
+  // (the key is then forgotten here: it enters the cache).
+  bool admit(uint64_t h) {
+    if (admit_after <= 1) return true;
+    int seen = 1;
+    auto at = sighting_at.find(h);
+    if (at != sighting_at.end()) {
+      seen += at->second->second;
+      sightings.erase(at->second);
+      sighting_at.erase(at);
+    }
+    if (seen >= admit_after) return true;
+    sightings.emplace_back(h, seen);
+    sighting_at[h] = std::prev(sightings.end());
+    while ((int64_t)sightings.size() > num_blocks) {
+      sighting_at.erase(sightings.front().first);
+      sightings.pop_front();
+    }
+    ++held_back;
+    return false;
+  }
 
   int64_t available() const { return (int64_t)free_list.size() + (int64_t)evictable.size(); }
 
@@ -402,13 +434,14 @@ int pa_bm_stats(const pa_bm* bm, int64_t* num_free, int64_t* num_used, int64_t* 
   return PA_OK;
 }
 
-int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits) {
+int pa_bm_enable_prefix_cache(pa_bm* bm, int protect_hits, int admit_after) {
   pa::clear_error();
   if (!bm) return fail(PA_ERR_INVALID_ARG, "null block manager");
-  if (!bm->seqs.empty() || protect_hits < 0)
+  if (!bm->seqs.empty() || protect_hits < 0 || admit_after < 1)
     return fail(PA_ERR_INVALID_ARG, "enable the prefix cache on an empty manager");
   bm->cache_on = true;
   bm->protect_hits = protect_hits;
+  bm->admit_after = admit_after;
   return PA_OK;
 }
 
@@ -490,7 +523,7 @@ int pa_bm_register(pa_bm* bm, int64_t seq, int64_t* newly_cached) {
       const uint64_t h = block_hash(parent, blk, bs);
       if (i >= s.registered) {
         const int32_t b = s.blocks[i];
-        if (!bm->cache.count(h) && !bm->keys[b].cached) {
+        if (!bm->cache.count(h) && !bm->keys[b].cached && bm->admit(h)) {
           pa_bm::Key& k = bm->keys[b];
           k.tokens.assign(blk, blk + bs);
           k.hash = h;
@@ -521,6 +554,7 @@ int pa_bm_prefix_stats(const pa_bm* bm, int64_t* out) {
   out[3] = bm->hit_blocks;
   out[4] = bm->miss_blocks;
   out[5] = bm->evictions;
+  out[6] = bm->held_back;
   return PA_OK;
 }
 

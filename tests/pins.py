@@ -688,3 +688,62 @@ def i8_prefill_is_masked_sdpa_on_dequantised(prefill_i8, window=0, seed=18):
                            rtol=0, atol=1e-12):
             return False
     return True
+
+
+def admission_threshold_keeps_one_shot_prompts_out(cls):
+    """[KV2P] §4.3: with a minimum of two registrations before a block enters
+    the cache, a prompt seen once stays private, a prompt seen twice is
+    cached and hit by the third request, and a flood of one-shot prompts
+    cannot evict it; the same flood with the threshold at 1 does."""
+    bs, nb = 4, 12
+    hot = list(range(100, 108))                         # two full blocks
+    shots = [[1000 + 8 * k + j for j in range(8)] for k in range(20)]
+    results = []
+    for admit in (2, 1):
+        m = cls(nb, bs)
+        m.enable_prefix_cache(0, admit)
+        seq = 0
+        for _ in range(2):                               # the hot prompt, twice
+            m.allocate_prompt(seq, hot)
+            m.register(seq)
+            m.free(seq)
+            seq += 1
+            if admit == 2 and _ == 0 and m.prefix_stats()[0] != 0:
+                return False                             # cached after one sighting
+        cached_after_two = m.prefix_stats()[0]
+        for toks in shots:                               # one-shot flood
+            m.allocate_prompt(seq, toks)
+            m.register(seq)
+            m.free(seq)
+            seq += 1
+        _, cached = m.allocate_prompt(seq, hot)
+        results.append((cached_after_two, cached, m.prefix_stats()[6]))
+    (c2, hit2, held2), (c1, hit1, held1) = results
+    return c2 == 2 and hit2 == 8 and held2 == 2 + 2 * len(shots) and hit1 == 0 and held1 == 0
+
+
+def admission_table_is_bounded(cls):
+    """Keys below the threshold are remembered for at most num_blocks keys,
+    the least recently seen dropped first: a key seen once, then pushed out
+    by num_blocks other keys, starts counting again."""
+    bs, nb = 2, 6
+
+    def seen(m, seq, toks):
+        m.allocate_prompt(seq, toks)
+        m.register(seq)
+        m.free(seq)
+
+    m = cls(nb, bs)
+    m.enable_prefix_cache(0, 2)
+    seen(m, 0, [7, 7])
+    for k in range(nb - 1):                              # room for the first key
+        seen(m, 1 + k, [50 + k, 50 + k])
+    seen(m, 10, [7, 7])                                  # second sighting: cached
+    kept = m.prefix_stats()[0] == 1
+    m = cls(nb, bs)
+    m.enable_prefix_cache(0, 2)
+    seen(m, 0, [7, 7])
+    for k in range(nb):                                  # one more: the first is dropped
+        seen(m, 1 + k, [50 + k, 50 + k])
+    seen(m, 10, [7, 7])
+    return kept and m.prefix_stats()[0] == 0

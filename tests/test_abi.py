@@ -270,11 +270,11 @@ PREFIX_OPS = st.lists(st.tuples(st.sampled_from(["prompt", "register", "decode",
 
 @settings(max_examples=120, deadline=None)
 @given(ops=PREFIX_OPS, bs=st.sampled_from([2, 4, 8]), nb=st.integers(4, 40),
-       protect=st.integers(0, 2), seed=st.integers(0, 3))
-def test_native_prefix_cache_matches_model(ops, bs, nb, protect, seed):
+       protect=st.integers(0, 2), admit=st.integers(1, 3), seed=st.integers(0, 3))
+def test_native_prefix_cache_matches_model(ops, bs, nb, protect, admit, seed):
     ref, bm = BlockManagerModel(nb, bs), pa.BlockManager(nb, bs)
-    ref.enable_prefix_cache(protect)
-    bm.enable_prefix_cache(protect)
+    ref.enable_prefix_cache(protect, admit)
+    bm.enable_prefix_cache(protect, admit)
     prompts = _prompts(seed)
     for op, a, b, n in ops:
         if op == "prompt":
@@ -322,6 +322,31 @@ def test_native_prefix_cache_matches_model(ops, bs, nb, protect, seed):
     bm.close()
 
 
+@pytest.mark.parametrize("pin", ["system_prompt_stored_once", "position_matters",
+                                 "multi_turn_reuses_full_blocks", "lru_spares_referenced_blocks",
+                                 "protection_keeps_hot_prefix",
+                                 "admission_threshold_keeps_one_shot_prompts_out",
+                                 "admission_table_is_bounded"])
+def test_native_prefix_cache_passes_the_pins(pin):
+    from tests import pins
+
+    class NamedSeqs:
+        """The native manager with sequences named by strings, as some pins
+        name them (the library takes int64 ids)."""
+
+        def __init__(self, nb, bs):
+            self.bm, self.ids = pa.BlockManager(nb, bs), {}
+
+        def __getattr__(self, name):
+            f = getattr(self.bm, name)
+            if not callable(f):
+                return f
+            return lambda *args, **kw: f(*[self.ids.setdefault(x, len(self.ids))
+                                           if isinstance(x, str) else x for x in args], **kw)
+
+    assert getattr(pins, pin)(NamedSeqs)
+
+
 def test_native_prefix_cache_rejects_bad_use():
     bm = pa.BlockManager(8, 4)
     with pytest.raises(pa.PAError) as e:
@@ -332,6 +357,10 @@ def test_native_prefix_cache_rejects_bad_use():
         bm.enable_prefix_cache()
     assert e.value.status == -1            # not empty
     bm.free(5)
+    for bad in ((-1, 1), (0, 0)):
+        with pytest.raises(pa.PAError) as e:
+            bm.enable_prefix_cache(*bad)   # negative protection, threshold below 1
+        assert e.value.status == -1
     bm.enable_prefix_cache()
     bm.allocate_prompt(0, [1, 2, 3, 4, 5])
     with pytest.raises(pa.PAError) as e:

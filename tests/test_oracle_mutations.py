@@ -262,8 +262,20 @@ class MostRecentEviction(BlockManagerModel):
 
 
 class NoProtection(BlockManagerModel):
-    def enable_prefix_cache(self, protect_hits=0):
-        super().enable_prefix_cache(0)
+    def enable_prefix_cache(self, protect_hits=0, admit_after=1):
+        super().enable_prefix_cache(0, admit_after)
+
+
+class AdmitsOneEarly(BlockManagerModel):
+    """The admission threshold applied as 'at least admit_after - 1'."""
+
+    def enable_prefix_cache(self, protect_hits=0, admit_after=1):
+        super().enable_prefix_cache(protect_hits, max(1, admit_after - 1))
+
+
+class UnboundedAdmissionTable(BlockManagerModel):
+    def _admission_capacity(self):
+        return 1 << 40
 
 
 class CachesPartialBlocks(BlockManagerModel):
@@ -291,7 +303,9 @@ class NoReferenceOnHit(BlockManagerModel):
 
 PREFIX_PINS = [pins.system_prompt_stored_once, pins.position_matters,
                pins.multi_turn_reuses_full_blocks, pins.lru_spares_referenced_blocks,
-               pins.protection_keeps_hot_prefix]
+               pins.protection_keeps_hot_prefix,
+               pins.admission_threshold_keeps_one_shot_prompts_out,
+               pins.admission_table_is_bounded]
 
 
 def _prefix_pins_fail(cls):
@@ -307,7 +321,8 @@ def _prefix_pins_fail(cls):
 
 
 @pytest.mark.parametrize("cls", [PositionFreeMatch, MostRecentEviction, NoProtection,
-                                 CachesPartialBlocks, NoReferenceOnHit])
+                                 CachesPartialBlocks, NoReferenceOnHit, AdmitsOneEarly,
+                                 UnboundedAdmissionTable])
 def test_prefix_pins_catch(cls):
     assert _prefix_pins_fail(cls), cls.__name__
 

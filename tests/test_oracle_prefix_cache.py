@@ -37,6 +37,14 @@ def test_protection_keeps_hot_prefix():
     assert pins.protection_keeps_hot_prefix(BlockManagerModel)
 
 
+def test_admission_threshold_keeps_one_shot_prompts_out():
+    assert pins.admission_threshold_keeps_one_shot_prompts_out(BlockManagerModel)
+
+
+def test_admission_table_is_bounded():
+    assert pins.admission_table_is_bounded(BlockManagerModel)
+
+
 def test_prefix_cache_needs_empty_manager_and_is_off_by_default():
     m = BlockManagerModel(8, 4)
     try:

@@ -158,6 +158,42 @@ __device__ __forceinline__ void load_lds4(const void* src, void* dst) {
 #endif
 }
 
+// v_max3_f32 as written: the max of three values that are never NaN (the
+// plain fmaxf adds an operand-quieting op per input).
+__device__ __forceinline__ float max3_nonan(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// The fp16 parts of two weights: hi = both rounded toward zero and packed
+// (v_cvt_pkrtz), lo = what hi misses, p - hi in fp32 rounded to nearest fp16,
+// packed the same way.  The lo part comes from one mixed-precision FMA per
+// value (-hi * 1 + p with hi read as fp16, result written to one half):
+// hi + lo keeps ~21 bits of each weight.
+__device__ __forceinline__ void split_f16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(lo)
+      : "v"(hi), "v"(p0), "v"(p1));
+}
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  In each group of 16
+// lanes, the four 16-bit values that lanes 4r .. 4r + 3 address form row r
+// of a 4 x 16 matrix, and lane i receives column i: element r of its result
+// is value i % 4 of the piece that lane 4r + i / 4 addresses.  It turns rows
+// stored in LDS into the per-lane columns a matrix-core operand needs.
+__device__ __forceinline__ half4_t lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) i16x4_t*)(p)));
+#else
+  return half4_t{};
+#endif
+}
+
 // Max over the four lanes c, c + 16, c + 32, c + 48 (the four 16-lane
 // rows), result in all four.  v_permlane32_swap exchanges the upper half of
 // one register with the lower half of the other, v_permlane16_swap the odd

@@ -68,7 +68,8 @@ struct PrefillArgs {
   float scale_log2;
   int window;               // > 0: a query sees the last `window` tokens up to itself
 };
-int prefill_columns_per_workgroup();
+int prefill_columns_per_workgroup();     // f16 pools
+int prefill_i8_columns_per_workgroup();  // INT8 pools
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream);
 // INT8 pool (codes + row scales; query in f16).

@@ -627,7 +627,8 @@ int pa_prefill(float* out, const void* query, const void* kv_cache, const float*
   a.max_blocks = max_blocks_per_seq;
   a.max_tokens = (int)max_tokens_ll;
   const long long cols = (long long)max_query_len * group;
-  const int per_wg = pa::prefill_columns_per_workgroup();
+  const int per_wg = dtype == PA_I8 ? pa::prefill_i8_columns_per_workgroup()
+                                    : pa::prefill_columns_per_workgroup();
   a.qblocks = (int)((cols + per_wg - 1) / per_wg);
   if ((long long)num_seqs * a.qblocks * num_kv_heads > pa::kMaxGridWorkgroups)
     return fail(PA_ERR_INVALID_ARG, "grid too large");

@@ -23,12 +23,10 @@ namespace prefill {
 // inside fp16 range for the hi/lo split.
 constexpr float kSlack = 8.f;
 constexpr float kPLog = 7.f;
-constexpr int kWaves = 4;   // waves per workgroup
 constexpr int kKeys = 32;   // keys per step: two 16-key MFMA tiles
 constexpr int kBufs = 4;    // LDS buffers of raw step tiles
 constexpr int kAhead = 3;   // steps in flight ahead of the one computed
 constexpr int kCB = 2;      // 16-column blocks per wave
-constexpr int kColsWG = kWaves * 16 * kCB;  // columns per workgroup
 
 // Byte offset of 16-byte chunk c of row r in a 16-bit K step tile (rows of
 // 2D bytes): chunks are XOR-swizzled by the row, so the 16 lanes that read
@@ -68,7 +66,7 @@ struct Work {
 // [0, total_queries) (so a bad query_start entry can never address q or out
 // outside their buffers), one longer than its context, or a query block past
 // its end.
-template <int G>
+template <int G, int COLS>  // COLS: columns per workgroup
 __device__ __forceinline__ bool workgroup_work(const PrefillArgs& a, Work& wk) {
   const unsigned nwg = gridDim.x, bid = blockIdx.x;
   const unsigned per = nwg / 8u, rem = nwg % 8u, xcd = bid % 8u;
@@ -83,9 +81,9 @@ __device__ __forceinline__ bool workgroup_work(const PrefillArgs& a, Work& wk) {
   wk.T = q1 - wk.q0;
   int n = a.cl[wk.s];
   wk.n = n < 0 ? 0 : (n > a.max_tokens ? a.max_tokens : n);
-  wk.wg_tok0 = wk.qb * (kColsWG / G);
+  wk.wg_tok0 = wk.qb * (COLS / G);
   if (wk.T > wk.n || wk.wg_tok0 >= wk.T) return false;
-  wk.wg_last = min(wk.T - 1, wk.wg_tok0 + kColsWG / G - 1);
+  wk.wg_last = min(wk.T - 1, wk.wg_tok0 + COLS / G - 1);
   // keys: from the first window start of the columns (0 without a window)
   // to the last column's position; steps are absolute
   wk.wg_lo = a.window > 0 ? max(0, wk.n - wk.T + wk.wg_tok0 + 1 - a.window) : 0;

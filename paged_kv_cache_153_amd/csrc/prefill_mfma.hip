@@ -28,18 +28,21 @@
 //                weight part: the C layout of the two S tiles gives each lane
 //                keys 4q..4q+3 of both tiles, which is the B layout of a
 //                32-deep contraction once the contraction index is relabelled
-//                (k = 8q + j  ->  key 4q + j of tile j / 4); V is read with
-//                the same relabelling, and the weights go in as fp16 hi + lo
-//                parts, which keeps ~21 bits of each weight;
+//                (k = 8q + j  ->  key 4q + j of tile j / 4); the V^T operand
+//                (8 keys of one output row per lane) comes from the V rows in
+//                LDS by transposing reads with the same relabelling, and the
+//                weights go in as fp16 hi + lo parts, which keeps ~21 bits of
+//                each weight;
 //   the weight sums as one more block whose V rows are all ones.
-// q.K of step st + 1 is issued between the max and the exponentials of step
-// st, so the matrix cores have work while the vector ALUs do the softmax;
-// the softmax runs at raised wave priority (s_setprio) so that it overlaps
-// the other wave's matrix products.
-// LDS rows are 2D bytes.  K rows have their 16-byte chunks XOR-swizzled by
-// the row, so that the 16 lanes that read one chunk of 16 different K rows
-// hit distinct banks; V rows are plain, since the lanes of a quad read one V
-// row whole (measured: an XOR swizzle by row there costs a two-way conflict).
+// The step loop is software-pipelined by one step: q.K and the max of step
+// st + 1 come before P.V of step st, and the exponentials and the weight
+// split of step st + 1 are interleaved with those P.V products, so each
+// wave feeds its SIMD's matrix core and vector ALU at the same time.
+// LDS rows are 2D bytes, their 16-byte chunks XOR-swizzled by the row: in K
+// so that the 16 lanes that read one chunk of 16 different K rows hit
+// distinct banks, in V (by an even amount, keeping 32-byte pairs together)
+// so that the 8 rows one half-wave's transposing read touches, 32 bytes of
+// each, hit distinct banks.
 #include "prefill_common.h"
 
 #include <type_traits>
@@ -52,8 +55,10 @@ using prefill::kBufs;
 using prefill::kKeys;
 using prefill::kPLog;
 using prefill::kSlack;
-using prefill::kWaves;
 using prefill::tile_off;
+
+constexpr int kWaves = 4;                            // waves per workgroup
+constexpr int kColsWG = kWaves * 16 * prefill::kCB;  // columns per workgroup
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArgs a) {
@@ -61,7 +66,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KS = D / 32;                 // 16x16x32 steps of q.K
   constexpr int NE = D / 16;                 // P.V blocks of 16 output rows
-  constexpr int VH = D / 16;                 // output row d = VH * r + e
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RPW = 64 / CPR;              // rows one wave loads per round
   constexpr int ROUNDS = kKeys / (kWaves * RPW);
@@ -69,7 +73,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   constexpr int TILE = kKeys * 2 * D;        // bytes of one K or V step tile
   constexpr int COLS_W = 16 * CB;            // columns per wave
   constexpr int TOK_W = COLS_W / G;          // query tokens per wave
-  using vrow_t = typename prefill::VRow<D>::type;
 
   // [buffer][K|V]: step st lives in buffer st % kBufs; its rows arrive by
   // direct global->LDS loads issued kAhead steps before it is used
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
 
   // ---- workgroup -> (sequence, KV head, query block) and its keys ----------
   prefill::Work wk;
-  if (!prefill::workgroup_work<G>(a, wk)) return;  // the whole workgroup
+  if (!prefill::workgroup_work<G, kColsWG>(a, wk)) return;  // the whole workgroup
   const int s = wk.s, g = wk.g, q0 = wk.q0, T = wk.T, n = wk.n;
   const int wg_tok0 = wk.wg_tok0, wg_lo = wk.wg_lo, st0 = wk.st0, nsteps = wk.nsteps;
   const int win = a.window;
@@ -123,6 +126,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
   const int lrow = lane / CPR;
   const int lch = lane % CPR;
+  // V chunk swizzle of row r: rows r and r' of one half-wave's transposing
+  // read (r mod 8, or r / 2 mod 4 for D = 64, distinct) get distinct 32-byte
+  // pairs of one 256-byte bank row
+  auto vswz = [](int r) { return 2 * ((D == 64 ? r >> 1 : r) & (CPR / 2 - 1)); };
 
   // Step sl goes to buffer (sl - st0) % kBufs.  Wave w's round j fills rows
   // (4 j + w) * RPW .. + RPW - 1 of the K and the V tile: lane l lands at
@@ -145,18 +152,34 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
     }
   };
+  // Lane offsets inside a piece whose rows are not clamped (most steps): the
+  // piece's first row address is wave-uniform (scalar registers) and each
+  // lane adds a fixed offset, so issuing a step takes no vector arithmetic.
+  uint32_t koff[ROUNDS], voff[ROUNDS];
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) {
+    const int r = (j * kWaves + w) * RPW + lrow;
+    koff[j] = (uint32_t)(lrow * (2 * D) + ((lch ^ (r & (CPR - 1))) << 4));
+    voff[j] = (uint32_t)(lrow * (2 * D) + ((lch ^ vswz(r)) << 4)) + (uint32_t)v_bytes;
+  }
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
       const int piece = j * kWaves + w;
-      const int r = piece * RPW + lrow;
-      const int key = min(max(sd * kKeys + r, wg_lo), n - 1);
-      const int c = lch ^ (r & (CPR - 1));
-      const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D);
-      load_lds16(src + c * 16, &lds[b][0][piece * 1024]);            // K: swizzled
-      load_lds16(src + v_bytes + lch * 16, &lds[b][1][piece * 1024]);  // V: plain rows
+      const int kb = sd * kKeys + piece * RPW;  // the piece's first key
+      if (kb >= wg_lo && kb + RPW <= n) {
+        const char* base = kvg + (size_t)ids[j] * block_bytes + (kb % BS) * (2 * D);
+        load_lds16(base + koff[j], &lds[b][0][piece * 1024]);  // K: swizzled
+        load_lds16(base + voff[j], &lds[b][1][piece * 1024]);  // V: swizzled
+      } else {
+        const int r = piece * RPW + lrow;
+        const int key = min(max(sd * kKeys + r, wg_lo), n - 1);
+        const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D);
+        load_lds16(src + ((lch ^ (r & (CPR - 1))) << 4), &lds[b][0][piece * 1024]);
+        load_lds16(src + v_bytes + ((lch ^ vswz(r)) << 4), &lds[b][1][piece * 1024]);
+      }
     }
   };
 
@@ -199,33 +222,34 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
               __builtin_bit_cast(half8_t, kr[kk][j]), qop[cb][j], sc[cb][kk], 0, 0, 0);
   };
 
-  // softmax and P.V of step st; q.K of the next step (buffer Bn) is issued
-  // between the max and the exponentials, so its matrix-core work overlaps
-  // the vector work of this step
-  auto softmax_pv = [&](int st, auto B, const float4_t (&sc)[CB][2], auto Bn,
-                        float4_t (&sn)[CB][2]) {
+  // V^T operand of output block e for the step in buffer B: lane (quad, col)
+  // gets V[key][16 e + col] for the keys 4 quad + r of tile h (elements
+  // 4 h + r); for that, lane (quad, 4 r + u) addresses V row 16 h + 4 quad + r
+  // at d = 16 e + 4 u
+  auto read_v = [&](auto B, half8_t (&av)[NE]) {
     constexpr int b = decltype(B)::value;
     const unsigned char* vt = lds[b][1];
-    // The wave takes issue priority for its vector work (V reads, max,
-    // exponentials, weight split) and drops it before its P.V products: the
-    // other wave of the SIMD is then usually in its matrix phase, whose
-    // issued MFMAs keep running, so the two phases overlap more (measured
-    // +3.5-5% on every head shape).  A wave's in-kernel priority, not a
-    // queue priority.
-    __builtin_amdgcn_s_setprio(1);
-    // V rows 4 quad + i of both tiles, this lane's D/16 values of each
-    vrow_t vr[8];
+    const int u = col & 3;
 #pragma unroll
-    for (int jv = 0; jv < 8; ++jv) {
-      const int r = (jv >> 2) * 16 + 4 * quad + (jv & 3);
-      if constexpr (D == 128)
-        vr[jv] = *reinterpret_cast<const u32x4_t*>(vt + r * (2 * D) + col * 16);
-      else
-        vr[jv] = *reinterpret_cast<const u32x2_t*>(vt + r * (2 * D) + col * 8);
+    for (int h = 0; h < 2; ++h) {
+      const int r = 16 * h + 4 * quad + (col >> 2);
+      const unsigned char* vrow = vt + r * (2 * D) + (u & 1) * 8;
+      const int sw = vswz(r);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const half4_t t = lds_read_tr16(vrow + (((2 * e + (u >> 1)) ^ sw) << 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[e][4 * h + i] = t[i];
+      }
     }
+  };
+
+  // Raw scores of step st (in log2 units they are cs * y), masked on the
+  // steps that cross the diagonal, the end of the context or a window
+  // start, and each lane's max in log2 units.
+  auto scores = [&](int st, const float4_t (&sc)[CB][2], float (&y)[CB][8], float (&lm)[CB]) {
     const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n ||
                       st * kKeys < w_lomax;
-    float y[CB][8];  // raw scores; in log2 units they are cs * y
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -239,20 +263,40 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
           if (t > p_col[cb] || t < lo_col[cb]) y[cb][k] = -INFINITY;
         }
       }
-      const float lm = cs * fmaxf(fmaxf(fmaxf(y[cb][0], y[cb][1]), fmaxf(y[cb][2], y[cb][3])),
-                                  fmaxf(fmaxf(y[cb][4], y[cb][5]), fmaxf(y[cb][6], y[cb][7])));
-      if (wave_any(lm > m[cb] + kSlack)) {
-        // some column's reference must move: to the column's max, exactly
-        const float m_new = fmaxf(m[cb], rows4_max(lm));
-        const float alpha = fast_exp2(m[cb] - m_new);
+      // scores are finite or -inf here (the mask replaces what no column sees)
+      const float t = max3_nonan(max3_nonan(y[cb][0], y[cb][1], y[cb][2]),
+                                 max3_nonan(y[cb][3], y[cb][4], y[cb][5]), y[cb][6]);
+      lm[cb] = cs * max3_nonan(t, y[cb][7], y[cb][7]);
+    }
+  };
+
+  // Moves the reference of a column block when some column's score passes
+  // it by more than kSlack: to the columns' max rounded up to an integer, so
+  // that the factor alpha = 2^(m_old - m_new) is a power of two.  Everything
+  // summed so far is rescaled by alpha, and so are the weights P of the step
+  // whose P.V products are still to come (exactly: a power of two, down to
+  // fp16's subnormals).
+  auto rescale = [&](const float (&lm)[CB], half8_t (*P)[CB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      if (wave_any(lm[cb] > m[cb] + kSlack)) {
+        const float m_new = ceilf(fmaxf(m[cb], rows4_max(lm[cb])));
+        const float alpha = ldexpf(1.f, (int)fmaxf(m[cb] - m_new, -200.f));
         acl[cb] *= alpha;
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[cb][e] *= alpha;
+        if (P) {
+          const half_t ah = (half_t)alpha;
+          P[0][cb] *= ah;
+          P[1][cb] *= ah;
+        }
         m[cb] = m_new;
       }
     }
-    qk(Bn, sn);
-    half8_t phi[CB], plo[CB];
+  };
+
+  // Weights exp2(cs y - m + kPLog) as fp16 hi + lo parts: P[0] hi, P[1] lo.
+  auto weights = [&](const float (&y)[CB][8], half8_t (&P)[2][CB]) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const float off = kPLog - m[cb];
@@ -261,67 +305,42 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       for (int k = 0; k < 8; ++k) pw[k] = fast_exp2(fmaf(y[cb][k], cs, off));
       uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const auto h = __builtin_amdgcn_cvt_pkrtz(pw[2 * k], pw[2 * k + 1]);
-        const auto r = __builtin_amdgcn_cvt_pkrtz(fmaf((float)h[0], -1.f, pw[2 * k]),
-                                                  fmaf((float)h[1], -1.f, pw[2 * k + 1]));
-        hw[k] = __builtin_bit_cast(uint32_t, h);
-        lw[k] = __builtin_bit_cast(uint32_t, r);
-      }
-      phi[cb] = __builtin_bit_cast(half8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
-      plo[cb] = __builtin_bit_cast(half8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // P.V in pairs of output blocks: each accumulator's hi and lo products
-    // are 2 * CB instructions apart
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, phi[cb], acl[cb], 0, 0, 0);
-#pragma unroll
-    for (int e0 = 0; e0 < NE; e0 += 2) {
-      half8_t av[2];
-#pragma unroll
-      for (int ee = 0; ee < 2; ++ee) {
-        const int e = e0 + ee;
-        const int wd = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        av[ee] = __builtin_bit_cast(
-            half8_t, u32x4_t{__builtin_amdgcn_perm(vr[1][wd], vr[0][wd], sel),
-                             __builtin_amdgcn_perm(vr[3][wd], vr[2][wd], sel),
-                             __builtin_amdgcn_perm(vr[5][wd], vr[4][wd], sel),
-                             __builtin_amdgcn_perm(vr[7][wd], vr[6][wd], sel)});
-      }
-#pragma unroll
-      for (int ee = 0; ee < 2; ++ee)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ee], phi[cb],
-                                                                    acc[cb][e0 + ee], 0, 0, 0);
-#pragma unroll
-      for (int ee = 0; ee < 2; ++ee)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ee], plo[cb],
-                                                                    acc[cb][e0 + ee], 0, 0, 0);
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, plo[cb], acl[cb], 0, 0, 0);
-    {  // K reads first, then each q.K product followed by vector work
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * KS * CB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
+      for (int k = 0; k < 4; ++k) split_f16(pw[2 * k], pw[2 * k + 1], hw[k], lw[k]);
+      P[0][cb] = __builtin_bit_cast(half8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
+      P[1][cb] = __builtin_bit_cast(half8_t, u32x4_t{lw[0], lw[1], lw[2], lw[3]});
     }
   };
 
+  // P.V of one step: each accumulator's hi and lo products are 2 * CB
+  // instructions apart; the weight sums on the all-ones block.
+  auto pv = [&](const half8_t (&av)[NE], const half8_t (&P)[2][CB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[0][cb], acl[cb], 0, 0, 0);
+#pragma unroll
+    for (int e0 = 0; e0 < NE; e0 += 2) {
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int ee = 0; ee < 2; ++ee)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[cb][e0 + ee] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                av[e0 + ee], P[part][cb], acc[cb][e0 + ee], 0, 0, 0);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      acl[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, P[1][cb], acl[cb], 0, 0, 0);
+  };
+
   // ---- steps st0 .. nsteps - 1 --------------------------------------------
-  // Iteration st: wait until step st + 1 has landed (own loads, then the
-  // barrier for everyone's), issue step st + kAhead into the buffer step
-  // st - 1 used, then run q.K of step st + 1 on the matrix cores while the
-  // softmax of step st runs on the vector ALUs, and P.V of step st.
+  // Software-pipelined by one step: iteration st waits until step st + 1
+  // has landed (own loads, then the barrier for everyone's), issues step
+  // st + kAhead into the buffer step st - 1 used, runs q.K of step st + 1
+  // and its max (and, rarely, the rescale), and then P.V of step st on the
+  // matrix cores interleaved with the exponentials and the weight split of
+  // step st + 1 on the vector ALUs.  A wave's last step computes the scores
+  // of the step after it too (all masked: weights 0, never used).
   auto vm_wait = [](auto N) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(N)::value) : "memory");
   };
@@ -339,33 +358,48 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   fetch_ids(st0 + 3);
   vm_wait(std::integral_constant<int, 2 * LPS>{});
   barrier();
-  float4_t sc[CB][2];
-  if (w_pmax >= 0) qk(I0{}, sc);
-  auto step = [&](int st, auto B) {
+  // weights of even steps of a trip in pe, of odd ones in po
+  half8_t pe[2][CB], po[2][CB];
+  if (w_pmax >= 0) {
+    float4_t s0[CB][2];
+    float y[CB][8], lm[CB];
+    qk(I0{}, s0);
+    scores(st0, s0, y, lm);
+    rescale(lm, nullptr);
+    weights(y, pe);
+  }
+  auto step = [&](int st, auto B, half8_t (&pc)[2][CB], half8_t (&pn)[2][CB]) {
     constexpr int b = decltype(B)::value;
     vm_wait(std::integral_constant<int, LPS>{});
     barrier();
     issue(st + kAhead, std::integral_constant<int, (b + kAhead) % kBufs>{});
     fetch_ids(st + kAhead + 1);
-    if (st * kKeys <= w_pmax) {
-      float4_t sn[CB][2];
-      softmax_pv(st, B, sc, std::integral_constant<int, (b + 1) % kBufs>{}, sn);
+    if (st * kKeys > w_pmax) return;  // the wave's columns end before this step
+    float4_t sn[CB][2];
+    float y[CB][8], lm[CB];
+    qk(std::integral_constant<int, (b + 1) % kBufs>{}, sn);
+    half8_t av[NE];
+    read_v(B, av);  // after q.K: the V operand takes the K operand's registers
+    scores(st + 1, sn, y, lm);
+    rescale(lm, pc);
+    pv(av, pc);
+    weights(y, pn);
+    // each P.V product followed by vector work of the next step
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        sc[cb][0] = sn[cb][0];
-        sc[cb][1] = sn[cb][1];
-      }
+    for (int i = 0; i < 2 * CB + 2 * NE * CB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
   };
   for (int st = st0; st < nsteps; st += kBufs) {  // fixed buffers in each trip
-    step(st, I0{});
-    if (st + 1 < nsteps) step(st + 1, I1{});
-    if (st + 2 < nsteps) step(st + 2, I2{});
-    if (st + 3 < nsteps) step(st + 3, I3{});
+    step(st, I0{}, pe, po);
+    if (st + 1 < nsteps) step(st + 1, I1{}, po, pe);
+    if (st + 2 < nsteps) step(st + 2, I2{}, pe, po);
+    if (st + 3 < nsteps) step(st + 3, I3{}, po, pe);
   }
   vm_wait(std::integral_constant<int, 0>{});  // no load may land after the exit
 
-  // ---- normalise and store: lane (quad, col) holds d = VH * (4 quad + i) + e
+  // ---- normalise and store: lane (quad, col) holds d = 16 e + 4 quad + i
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const float lt = acl[cb][0];
@@ -373,13 +407,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       const float inv = 1.f / lt;
       float* o = a.out + ((size_t)(q0 + tok[cb]) * a.num_q_heads + g * G + hh) * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int e4 = 0; e4 < NE / 4; ++e4)
-          *reinterpret_cast<float4_t*>(o + VH * (4 * quad + i) + 4 * e4) =
-              float4_t{acc[cb][4 * e4][i], acc[cb][4 * e4 + 1][i], acc[cb][4 * e4 + 2][i],
-                       acc[cb][4 * e4 + 3][i]} * inv;
-      }
+      for (int e = 0; e < NE; ++e)
+        *reinterpret_cast<float4_t*>(o + 16 * e + 4 * quad) = acc[cb][e] * inv;
     }
   }
 }
@@ -416,7 +445,7 @@ int by_block(const PrefillArgs& a, int block_size, int group, hipStream_t stream
 
 }  // namespace
 
-int prefill_columns_per_workgroup() { return prefill::kColsWG; }
+int prefill_columns_per_workgroup() { return kColsWG; }
 
 int launch_prefill_mfma(const PrefillArgs& a, int head_dim, int block_size, int group,
                         hipStream_t stream) {

@@ -35,12 +35,14 @@
 namespace pa {
 namespace {
 
+constexpr int kWaves = 4;                           // waves per workgroup
+constexpr int kColsWG = kWaves * 16 * prefill::kCB;  // columns per workgroup
+
 using prefill::kAhead;
 using prefill::kBufs;
 using prefill::kKeys;
 using prefill::kPLog;
 using prefill::kSlack;
-using prefill::kWaves;
 using prefill::tile_off;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
 
   // ---- workgroup -> (sequence, KV head, query block) and its keys ----------
   prefill::Work wk;
-  if (!prefill::workgroup_work<G>(a, wk)) return;  // the whole workgroup
+  if (!prefill::workgroup_work<G, kColsWG>(a, wk)) return;  // the whole workgroup
   const int s = wk.s, g = wk.g, q0 = wk.q0, T = wk.T, n = wk.n;
   const int wg_tok0 = wk.wg_tok0, wg_lo = wk.wg_lo, st0 = wk.st0, nsteps = wk.nsteps;
   const int win = a.window;
@@ -460,6 +462,8 @@ int by_block(const PrefillArgs& a, int block_size, int group, hipStream_t stream
 }
 
 }  // namespace
+
+int prefill_i8_columns_per_workgroup() { return kColsWG; }
 
 int launch_prefill_mfma_i8(const PrefillArgs& a, int head_dim, int block_size, int group,
                            hipStream_t stream) {

@@ -6,15 +6,19 @@
 //  * single:    one workgroup per (sequence, KV head), whole context;
 //  * partition: one workgroup per (sequence, KV head, P-token partition);
 //  * balanced:  W workgroups, each given an equal, contiguous slice of the
-//               global tile list ordered (sequence, KV head, tile).  A
-//               workgroup walks the (sequence, KV head) segments its slice
-//               covers; a segment it covers completely is finished in place,
-//               a segment cut by a slice boundary leaves a partial (at most
-//               two per workgroup: its first and its last segment) that the
-//               balanced merge kernel combines.  Every workgroup does the
-//               same number of tiles whatever the length distribution, which
-//               removes the tail that ragged batches leave with the other
-//               schedules.
+//               global work list ordered (sequence, KV head, tile), where a
+//               (sequence, KV head) segment of nt > 0 tiles counts as
+//               seg_cost + nt units: seg_cost units for what starting and
+//               finishing a segment costs (loading q and the first tiles,
+//               the cross-wave merge), then one unit per tile.  A workgroup
+//               walks the segments its slice covers and computes the tiles
+//               among its units; a segment it covers completely is finished
+//               in place, a segment whose tiles a slice boundary cuts leaves
+//               a partial (at most two per workgroup: the one whose first
+//               tile lies in its slice, and its last) that the balanced
+//               merge kernel combines.  Every workgroup does the same amount
+//               of work whatever the length distribution, which removes the
+//               tail that ragged batches leave with the other schedules.
 //
 // A sequence's work is the tile span that holds its keys: tiles
 // [t0, t0 + nt) with t0 = floor(lo / 16) and t0 + nt = ceil(n / 16), where
@@ -59,7 +63,12 @@ __device__ __forceinline__ Span seq_span(const DecodeArgs& a, int s) {
   return sp;
 }
 
-// Fills prefix[s] = sum_{s' <= s} nt(s') for s < S (per KV head) with the
+// Work units of one (sequence, KV head) segment in the balanced schedule.
+__device__ __forceinline__ int seg_units(const DecodeArgs& a, int nt) {
+  return nt > 0 ? nt + a.seg_cost : 0;
+}
+
+// Fills prefix[s] = sum_{s' <= s} units(s') for s < S (per KV head) with the
 // whole workgroup; every thread sees the result after the final barrier.
 // Scans in chunks of blockDim.x with a running carry.
 __device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
@@ -67,7 +76,7 @@ __device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += nt) {
     const int s = base + (int)threadIdx.x;
-    if (s < a.num_seqs) prefix[s] = seq_span(a, s).nt;
+    if (s < a.num_seqs) prefix[s] = seg_units(a, seq_span(a, s).nt);
     __syncthreads();
     for (int off = 1; off < nt; off <<= 1) {  // inclusive Hillis-Steele scan
       int v = 0;
@@ -84,7 +93,7 @@ __device__ inline void build_tile_prefix(const DecodeArgs& a, int* prefix) {
   }
 }
 
-// Smallest s with hkv * prefix[s] > t (the sequence holding global tile t).
+// Smallest s with hkv * prefix[s] > t (the sequence holding global unit t).
 __device__ __forceinline__ int owner_of(const int* prefix, int num_seqs, int hkv, int64_t t) {
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
@@ -113,33 +122,36 @@ template <int G, int D, int NW, typename RangeFn>
 __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) {
   if (a.schedule == kScheduleBalanced) {
     build_tile_prefix(a, prefix);
-    const int S = a.num_seqs, hkv = a.num_kv_heads;
+    const int S = a.num_seqs, hkv = a.num_kv_heads, c = a.seg_cost;
     const int64_t total = (int64_t)hkv * prefix[S - 1];
     const int64_t chunk = balanced_chunk(total, a.num_workgroups);
-    int64_t t = (int64_t)blockIdx.x * chunk;
-    const int64_t t1 = min(t + chunk, total);
-    bool first = true;
+    const int64_t t_start = (int64_t)blockIdx.x * chunk;
+    const int64_t t1 = min(t_start + chunk, total);
+    int64_t t = t_start;
     while (t < t1) {
       const int s = owner_of(prefix, S, hkv, t);
-      const int before_tiles = s ? prefix[s - 1] : 0;
-      const int nt = prefix[s] - before_tiles;  // > 0: s owns tile t
-      const int64_t before = (int64_t)hkv * before_tiles;
-      const int g = (int)((t - before) / nt);
-      const int64_t seg0 = before + (int64_t)g * nt;
-      const int ta = (int)(t - seg0);
-      const int tb = (int)min((int64_t)nt, t1 - seg0);
-      Sink sink;
-      if (ta == 0 && tb == nt) {
-        sink = output_sink<G, D>(a, s, g);
-      } else {  // slot 2w: the workgroup's first segment, 2w + 1: its last
-        const size_t slot = 2 * (size_t)blockIdx.x + (first ? 0 : 1);
-        sink = Sink{a.ws_o + slot * G * D, a.ws_m + slot * G, a.ws_l + slot * G, D, 1};
+      const int before_units = s ? prefix[s - 1] : 0;
+      const int nu = prefix[s] - before_units;  // > 0: s owns unit t
+      const int nt = nu - c;
+      const int64_t before = (int64_t)hkv * before_units;
+      const int g = (int)((t - before) / nu);
+      const int64_t seg0 = before + (int64_t)g * nu;
+      const int64_t off = seg0 + c;  // the segment's first tile unit
+      const int ta = (int)(max(t, off) - off);
+      const int tb = (int)(min(seg0 + nu, t1) - off);
+      if (tb > ta) {
+        Sink sink;
+        if (ta == 0 && tb == nt) {
+          sink = output_sink<G, D>(a, s, g);
+        } else {  // slot 2w: the segment's tiles start in the slice, 2w + 1: before it
+          const size_t slot = 2 * (size_t)blockIdx.x + (t_start >= off ? 0 : 1);
+          sink = Sink{a.ws_o + slot * G * D, a.ws_m + slot * G, a.ws_l + slot * G, D, 1};
+        }
+        const Span sp = seq_span(a, s);
+        range(s, g, sp.lo, sp.n, sp.t0 + ta, sp.t0 + tb, sink);
+        __syncthreads();
       }
-      const Span sp = seq_span(a, s);
-      range(s, g, sp.lo, sp.n, sp.t0 + ta, sp.t0 + tb, sink);
-      __syncthreads();
-      t = seg0 + tb;
-      first = false;
+      t = seg0 + nu;
     }
     return;
   }

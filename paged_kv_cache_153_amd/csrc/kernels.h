@@ -46,6 +46,7 @@ struct DecodeArgs {
   int variant;              // MFMA: 1 = one tile in flight per wave, 0 = two
   int cached_kv;            // 1: plain K/V loads; 0: non-temporal (streaming) loads
   int window;               // > 0: attend to the last `window` tokens only; 0: all
+  int seg_cost;             // balanced: tile-equivalents charged per (sequence, KV head)
 };
 
 // Causal multi-token queries (a prefill chunk per sequence).

@@ -112,10 +112,10 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
 
 // Balanced schedule: one workgroup per (sequence, query head) row merges the
 // partials that the workgroups whose slices cut the row's segment left in
-// their slots (slot 2w if the segment was workgroup w's first, 2w + 1 if its
-// last).  It locates the segment from two sums over the context lengths —
-// the tiles of the sequences before s and of all sequences — computed with
-// the decode's own arithmetic.  A segment inside one slice was finished by
+// their slots (slot 2w if the segment's tiles start in workgroup w's slice,
+// 2w + 1 if before it).  It locates the segment from two sums over the
+// context lengths — the work units of the sequences before s and of all
+// sequences — computed with the decode's own arithmetic.  A segment inside one slice was finished by
 // the decode; an empty sequence gets zeros here.  Thread groups of D/4 take
 // the slots round robin as in the partition merge.
 template <int D>
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
   const int g = h / G;
   int before = 0, all = 0;
   for (int j = threadIdx.x; j < S; j += kMergeThreads) {
-    const int t = seq_span(a, j).nt;
+    const int t = seg_units(a, seq_span(a, j).nt);
     all += t;
     before += j < s ? t : 0;
   }
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArg
   }
   const int64_t total = (int64_t)hkv * all;
   const int64_t chunk = balanced_chunk(total, a.num_workgroups);
-  const int64_t off = (int64_t)hkv * before + (int64_t)g * nt;
+  const int64_t off = (int64_t)hkv * before + (int64_t)g * (nt + a.seg_cost) + a.seg_cost;
   const int64_t w_lo = off / chunk;
   const int64_t w_hi = (off + nt - 1) / chunk;
   if (w_lo == w_hi) return;

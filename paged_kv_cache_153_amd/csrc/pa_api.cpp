@@ -105,6 +105,14 @@ int device_cus() {
 // kernel variant is picked.
 constexpr int kMaxWorkgroupsPerCU = 8;
 
+// Balanced-schedule charge per (sequence, KV head) segment, in tiles: the
+// fixed cost of starting and finishing a range (q and first-tile latency,
+// the cross-wave merge).  Swept on the ragged GQA batch (64 seqs, lengths
+// U[128, 8192]): f16 0 / 3 / 6 / 10 / 16 -> 190.0 / 184.1 / 182.9 / 181.8 /
+// 183.4 us, INT8 0 / 6 / 10 / 16 -> 114.1 / 108.2 / 108.2 / 108.5 us.
+constexpr int kSegCostF16 = 10;
+constexpr int kSegCostI8 = 8;
+
 Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_tokens,
                int partition, int cus) {
   Plan p;
@@ -541,6 +549,16 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   }
   a.cached_kv = cached_kv;
   a.window = sliding_window;
+  // Balanced schedule: what one (sequence, KV head) segment costs beyond its
+  // tiles, in tiles of the kernel that runs (measured on ragged batches).
+  a.seg_cost = dtype == PA_I8 ? pa::kSegCostI8 : pa::kSegCostF16;
+  {  // PA_TUNE_SEGCOST overrides it (tuning experiments only)
+    static const int forced = [] {
+      const char* e = std::getenv("PA_TUNE_SEGCOST");
+      return e ? std::atoi(e) : -1;
+    }();
+    if (forced >= 0 && forced <= 64) a.seg_cost = forced;
+  }
 
   int use = kernel;
   if (use == PA_KERNEL_AUTO) use = pa::choose_kernel(dtype, group);

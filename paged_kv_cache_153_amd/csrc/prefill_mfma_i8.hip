@@ -147,6 +147,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
       ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
     }
   };
+  // A piece of RRPW rows lies in one block when RRPW <= BS (both powers of
+  // two, pieces aligned).  When none of its rows is clamped either (most
+  // steps), its first row address is wave-uniform and each lane adds a fixed
+  // offset; otherwise every lane finds its own row's block and clamped key.
+  constexpr bool kPieceInBlock = RRPW <= BS;
+  const uint32_t loff = (uint32_t)((lane / RCPR) * D + (lane % RCPR) * 16);
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);
@@ -154,12 +160,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
     for (int j = 0; j < ROUNDS; ++j) {
       const int piece = j * kWaves + w;
       const bool is_v = piece >= PIECES / 2;
-      const int r = (piece % (PIECES / 2)) * RRPW + lane / RCPR;  // row in the step
-      const int key = clamp_key(sd * kKeys + r);
-      const int id = id_of_row(r);
-      const char* src = kvg + (size_t)id * block_bytes + (is_v ? v_bytes : 0) +
-                        (size_t)(key % BS) * D + (lane % RCPR) * 16;
-      load_lds16(src, &raw[b].kv[piece * 1024]);
+      const int r0 = (piece % (PIECES / 2)) * RRPW;  // the piece's first row in the step
+      const int kb = sd * kKeys + r0;
+      const size_t kv_off = is_v ? v_bytes : 0;
+      if (kPieceInBlock && kb >= wg_lo && kb + RRPW <= n) {
+        const char* base = kvg + (size_t)id_of_row(r0) * block_bytes + kv_off +
+                           (size_t)(kb % BS) * D;
+        load_lds16(base + loff, &raw[b].kv[piece * 1024]);
+      } else {
+        const int r = r0 + lane / RCPR;  // row in the step
+        const int key = clamp_key(sd * kKeys + r);
+        const char* src = kvg + (size_t)id_of_row(r) * block_bytes + kv_off +
+                          (size_t)(key % BS) * D + (lane % RCPR) * 16;
+        load_lds16(src, &raw[b].kv[piece * 1024]);
+      }
     }
     // scales: wave w loads entries 16 w + (lane % 16)
     const int e = 16 * w + (lane & 15);
@@ -288,8 +302,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
           if (t > p_col[cb] || t < lo_col[cb]) y[cb][k] = -INFINITY;
         }
       }
-      const float lm = cs * fmaxf(fmaxf(fmaxf(y[cb][0], y[cb][1]), fmaxf(y[cb][2], y[cb][3])),
-                                  fmaxf(fmaxf(y[cb][4], y[cb][5]), fmaxf(y[cb][6], y[cb][7])));
+      // scores are finite or -inf here (codes and scales are finite)
+      const float t = max3_nonan(max3_nonan(y[cb][0], y[cb][1], y[cb][2]),
+                                 max3_nonan(y[cb][3], y[cb][4], y[cb][5]), y[cb][6]);
+      const float lm = cs * max3_nonan(t, y[cb][7], y[cb][7]);
       if (wave_any(lm > m[cb] + kSlack)) {
         // some column's reference must move: to the column's max, exactly
         const float m_new = fmaxf(m[cb], rows4_max(lm));

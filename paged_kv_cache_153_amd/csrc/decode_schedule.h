@@ -16,9 +16,12 @@
 //               in place, a segment whose tiles a slice boundary cuts leaves
 //               a partial (at most two per workgroup: the one whose first
 //               tile lies in its slice, and its last) that the balanced
-//               merge kernel combines.  Every workgroup does the same amount
-//               of work whatever the length distribution, which removes the
-//               tail that ragged batches leave with the other schedules.
+//               merge kernel combines; the workgroup whose slice start is
+//               the first boundary inside a cut segment's tiles records it
+//               for the merge, which then visits only the cut segments.
+//               Every workgroup does the same amount of work whatever the
+//               length distribution, which removes the tail that ragged
+//               batches leave with the other schedules.
 //
 // A sequence's work is the tile span that holds its keys: tiles
 // [t0, t0 + nt) with t0 = floor(lo / 16) and t0 + nt = ceil(n / 16), where
@@ -127,6 +130,38 @@ __device__ void run_schedule(const DecodeArgs& a, int* prefix, RangeFn&& range) 
     const int64_t chunk = balanced_chunk(total, a.num_workgroups);
     const int64_t t_start = (int64_t)blockIdx.x * chunk;
     const int64_t t1 = min(t_start + chunk, total);
+    // Empty sequences own no units: workgroup w writes the zero outputs of
+    // the empty sequences w, w + W, ...
+    for (int s = blockIdx.x; s < S; s += gridDim.x)
+      if (prefix[s] == (s ? prefix[s - 1] : 0))
+        for (int g = 0; g < hkv; ++g) write_zero_output<G, D, NW>(a, s, g);
+    // The segment whose tiles the boundary at t_start cuts, recorded for the
+    // merge by the first boundary inside them (the workgroups [w_lo, w_hi]
+    // that hold its tiles each left a partial; w_lo's slot is 2 w_lo when
+    // the tiles start exactly at its slice, else 2 w_lo + 1)
+    if (threadIdx.x == 0) {
+      int rec[kCutInts] = {-1, 0, 0, 0, 0, 0, 0, 0};
+      if (t_start > 0 && t_start < total) {
+        const int s = owner_of(prefix, S, hkv, t_start);
+        const int before_units = s ? prefix[s - 1] : 0;
+        const int nu = prefix[s] - before_units;
+        const int64_t before = (int64_t)hkv * before_units;
+        const int g = (int)((t_start - before) / nu);
+        const int64_t off = before + (int64_t)g * nu + c;
+        const int nt = nu - c;
+        const int64_t w_lo = off / chunk;
+        if (off < t_start && t_start < off + nt && w_lo == (int64_t)blockIdx.x - 1) {
+          rec[0] = s;
+          rec[1] = g;
+          rec[2] = (int)w_lo;
+          rec[3] = (int)((off + nt - 1) / chunk);
+          rec[4] = (int)(2 * w_lo + (w_lo * chunk >= off ? 0 : 1));
+        }
+      }
+      int* dst = a.ws_cut + (size_t)blockIdx.x * kCutInts;
+#pragma unroll
+      for (int i = 0; i < kCutInts; ++i) dst[i] = rec[i];
+    }
     int64_t t = t_start;
     while (t < t1) {
       const int s = owner_of(prefix, S, hkv, t);

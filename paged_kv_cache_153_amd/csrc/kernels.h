@@ -27,6 +27,9 @@ struct DecodeArgs {
   float* ws_o;              // [S, Hq, NP, D] partition outputs (normalised)
   float* ws_m;              // [S, Hq, NP] partition max, log2 units
   float* ws_l;              // [S, Hq, NP] partition sum of exp2(y - m)
+  int* ws_cut;              // balanced: per workgroup w, the segment whose tiles the
+                            // boundary at the start of w's slice cuts first (kCutInts
+                            // ints; s < 0: none)
   const void* q;            // [S, Hq, D]
   const void* kv;           // [NB, 2, Hkv, BS, D]
   const float* kv_scales;   // INT8 pool: [NB, Hkv, 2, BS] row scales; else null
@@ -48,6 +51,10 @@ struct DecodeArgs {
   int window;               // > 0: attend to the last `window` tokens only; 0: all
   int seg_cost;             // balanced: tile-equivalents charged per (sequence, KV head)
 };
+
+// Balanced schedule: ints per workgroup in ws_cut: sequence, KV head, first
+// and last contributing workgroup, slot of the first one (then padding).
+constexpr int kCutInts = 8;
 
 // Causal multi-token queries (a prefill chunk per sequence).
 struct PrefillArgs {

@@ -97,66 +97,32 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a) {
   combine_groups<D>(st, grp, c4, a.out + (size_t)row * D);
 }
 
-// Sum of v over the workgroup, returned to every thread.
-__device__ __forceinline__ int block_sum(int v, int* red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int k = 0; k < kMergeThreads / 64; ++k) t += red[k];
-  return t;
-}
-
-// Balanced schedule: one workgroup per (sequence, query head) row merges the
-// partials that the workgroups whose slices cut the row's segment left in
-// their slots (slot 2w if the segment's tiles start in workgroup w's slice,
-// 2w + 1 if before it).  It locates the segment from two sums over the
-// context lengths — the work units of the sequences before s and of all
-// sequences — computed with the decode's own arithmetic.  A segment inside one slice was finished by
-// the decode; an empty sequence gets zeros here.  Thread groups of D/4 take
-// the slots round robin as in the partition merge.
+// Balanced schedule: one workgroup per decode workgroup w merges the
+// segment that w recorded in its cut-list entry, if any: the segment's tiles
+// were cut by slice boundaries, and the workgroups [w_lo, w_hi] left its
+// partials (all G heads) in slot s_lo of w_lo and slot 2w of the others.
+// Threads are grouped D/4 to a head row; each keeps the running
+// log-sum-exp of its float4 over the contributors.  Empty sequences and
+// segments inside one slice were finished by the decode kernel.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(DecodeArgs a) {
   constexpr int TPR = D / 4;
-  constexpr int NG = kMergeThreads / TPR;
-  __shared__ int red[2][kMergeThreads / 64];
-  const int S = a.num_seqs, hkv = a.num_kv_heads, G = a.num_q_heads / hkv;
-  const int row = blockIdx.x;
-  const int s = row / a.num_q_heads;
-  const int h = row % a.num_q_heads;
-  const int g = h / G;
-  int before = 0, all = 0;
-  for (int j = threadIdx.x; j < S; j += kMergeThreads) {
-    const int t = seg_units(a, seq_span(a, j).nt);
-    all += t;
-    before += j < s ? t : 0;
-  }
-  before = block_sum(before, red[0]);
-  all = block_sum(all, red[1]);
-  const int nt = seq_span(a, s).nt;
-  float* out = a.out + (size_t)row * D;
-  if (nt == 0) {
-    for (int d = threadIdx.x; d < D; d += kMergeThreads) out[d] = 0.f;
-    return;
-  }
-  const int64_t total = (int64_t)hkv * all;
-  const int64_t chunk = balanced_chunk(total, a.num_workgroups);
-  const int64_t off = (int64_t)hkv * before + (int64_t)g * (nt + a.seg_cost) + a.seg_cost;
-  const int64_t w_lo = off / chunk;
-  const int64_t w_hi = (off + nt - 1) / chunk;
-  if (w_lo == w_hi) return;
-  const int grp = threadIdx.x / TPR;
+  const int* rec = a.ws_cut + (size_t)blockIdx.x * kCutInts;
+  const int s = rec[0];
+  if (s < 0) return;
+  const int g = rec[1], w_lo = rec[2], w_hi = rec[3], slot_lo = rec[4];
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int hh = threadIdx.x / TPR;
+  if (hh >= G) return;
   const int c4 = (threadIdx.x % TPR) * 4;
-  const int hh = h % G;
   Lse4 st;
-  for (int64_t w = w_lo + grp; w <= w_hi; w += NG) {
-    const size_t idx = (2 * (size_t)w + (w * chunk >= off ? 0 : 1)) * G + hh;
+  for (int w = w_lo; w <= w_hi; ++w) {
+    const size_t idx = (size_t)(w == w_lo ? slot_lo : 2 * w) * G + hh;
     st.push(a.ws_m[idx], a.ws_l[idx], *reinterpret_cast<const float4_t*>(a.ws_o + idx * D + c4));
   }
-  combine_groups<D>(st, grp, c4, out);
+  float* out = a.out + ((size_t)s * a.num_q_heads + g * G + hh) * D + c4;
+  const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+  *reinterpret_cast<float4_t*>(out) = st.o * inv;
 }
 
 }  // namespace
@@ -174,7 +140,7 @@ int launch_merge(const DecodeArgs& a, int head_dim, hipStream_t stream) {
 }
 
 int launch_merge_balanced(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-  const unsigned grid = (unsigned)a.num_seqs * a.num_q_heads;
+  const unsigned grid = (unsigned)a.num_workgroups;
   if (grid == 0) return 0;
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_balanced_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);

@@ -80,7 +80,7 @@ struct Plan {
   int num_parts = 1;
   int workgroups = 0;  // balanced: grid size upper bound used for the workspace
   size_t ws_bytes = 0;
-  size_t off_m = 0, off_l = 0;
+  size_t off_m = 0, off_l = 0, off_cut = 0;
 };
 
 constexpr size_t kAlign = 256;
@@ -133,7 +133,8 @@ Plan make_plan(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, in
     const size_t bytes_ml = round_up(slots * sizeof(float));
     p.off_m = bytes_o;
     p.off_l = bytes_o + bytes_ml;
-    p.ws_bytes = bytes_o + 2 * bytes_ml;
+    p.off_cut = bytes_o + 2 * bytes_ml;
+    p.ws_bytes = p.off_cut + round_up((size_t)p.workgroups * kCutInts * sizeof(int));
     return p;
   }
   p.schedule = kSchedulePartition;
@@ -521,6 +522,7 @@ int pa_decode(float* out, const void* query, const void* kv_cache, const float* 
   a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
   a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.ws_cut = plan.off_cut ? reinterpret_cast<int*>(ws + plan.off_cut) : nullptr;
   a.q = query;
   a.kv = kv_cache;
   a.kv_scales = kv_scales;

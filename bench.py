@@ -320,7 +320,7 @@ class Step:
         ws = pa.decode_workspace_size(S, Hq, Hkv, D, bs, self.mb, self.mb * bs, partition,
                                       pa.I8 if self.int8 else
                                       pa.F32 if w["dtype"] == "f32" else pa.F16, kernel,
-                                      sliding_window=window)
+                                      sliding_window=window, cached_kv=self.cached_kv)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         # one packed host->device transfer per step: slots | pairs | lens | tables
         self.upload = upload

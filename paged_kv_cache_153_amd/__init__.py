@@ -261,12 +261,14 @@ def stage_and_write(stage_dst, stage_src, key, value, kv_cache, slot_mapping, co
 
 def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                           max_blocks_per_seq, max_context_len, partition_size=0,
-                          dtype=F16, kernel="auto", sliding_window=0):
-    """Bytes of split-context workspace ``decode`` needs for this shape."""
+                          dtype=F16, kernel="auto", sliding_window=0, cached_kv=False):
+    """Bytes of split-context workspace ``decode`` needs for this shape (the
+    load policy ``cached_kv`` can change the schedule, hence the size)."""
     need = ctypes.c_size_t(0)
     _check(lib().pa_decode(None, None, None, None, None, None, num_seqs, num_q_heads,
                            num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len, 1, 1.0,
-                           int(sliding_window), partition_size, KERNELS[kernel], None, 0,
+                           int(sliding_window), partition_size,
+                           KERNELS[kernel] | (KV_CACHED if cached_kv else 0), None, 0,
                            ctypes.byref(need), dtype, None))
     return need.value
 
@@ -307,7 +309,7 @@ def decode(query, kv_cache, block_tables, context_lens, scale=None, max_context_
         scale = d ** -0.5
     dt = _dtype_code(kv_cache)
     need = decode_workspace_size(s, hq, hkv, d, bs, mb, int(max_context_len), partition_size,
-                                 dt, kernel, sliding_window)
+                                 dt, kernel, sliding_window, cached_kv)
     if out is None:
         out = torch.empty((s, hq, d), dtype=torch.float32, device=query.device)
     elif out.dtype != torch.float32 or out.shape != (s, hq, d):

@@ -267,6 +267,23 @@ def test_cached_and_streaming_loads_agree(device):
     assert np.array_equal(run_decode(y, device), run_decode(y, device, cached_kv=True))
 
 
+def test_cached_auto_schedule_sizes_its_workspace(device):
+    """Cached loads with the automatic schedule take fixed partitions; at 64
+    sequences x 32 heads under a 16K bound their workspace is larger than the
+    balanced schedule's that streaming loads would pick, and the binding must
+    size it for the policy it passes."""
+    rng = np.random.default_rng(15)
+    lens = [16384] + rng.integers(1, 200, 63).tolist()
+    x = synth.make_decode_inputs(lens, 32, 8, 128, 16, dtype="f16", seed=15)
+    stream = pa.decode_workspace_size(64, 32, 8, 128, 16, x.block_tables.shape[1], 16384)
+    cached = pa.decode_workspace_size(64, 32, 8, 128, 16, x.block_tables.shape[1], 16384,
+                                      cached_kv=True)
+    assert cached > stream
+    want = ref_decode(x)
+    got = run_decode(x, device, kernel="mfma", cached_kv=True)
+    assert np.isfinite(got).all() and np.abs(got - want).max() <= TOL
+
+
 @pytest.mark.parametrize("kern", ["valu", "mfma"])
 def test_balanced_schedule_many_short_and_long(device, kern):
     """Balanced slices cut sequences at arbitrary tiles: many slices per long

@@ -618,6 +618,9 @@ int pa_prefill(float* out, const void* query, const void* kv_cache, const float*
     return fail(PA_ERR_INVALID_ARG, "prefill scale must be positive and finite");
   const long long max_tokens_ll = (long long)max_blocks_per_seq * block_size;
   if (max_tokens_ll > (1LL << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  // the kernels address a block in 32-bit byte offsets
+  if ((long long)num_kv_heads * block_size * head_dim * 4 >= (1LL << 32))
+    return fail(PA_ERR_UNSUPPORTED, "num_kv_heads too large for prefill");
   if (num_seqs == 0 || total_queries == 0 || max_query_len == 0) return PA_OK;
   if (!out || !query || !kv_cache || !block_tables || !context_lens || !query_start)
     return fail(PA_ERR_INVALID_ARG, "null device pointer");

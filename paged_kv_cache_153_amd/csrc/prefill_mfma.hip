@@ -142,17 +142,23 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   // first key load row wg_lo (finite; their weights are 0): a piece's RPW
   // rows, clamped into [wg_lo, n - 1], still lie in one block, and rows no
   // column sees are never read.  Steps past the last re-read it, so every
-  // step issues the same loads and the wait counts stay fixed.
+  // step issues the same loads and the wait counts stay fixed.  Most steps
+  // lie wholly inside [wg_lo, n): their pieces need no clamping, and they
+  // take one wave-uniform test instead of one per piece.  Keys are below
+  // n <= max_blocks * BS, so a block index never passes the table's row.
   constexpr int LPS = 2 * ROUNDS;  // loads per lane per step
-  int ids[ROUNDS];
+  auto inside = [&](int sd) { return sd * kKeys >= wg_lo && (sd + 1) * kKeys <= n; };
+  uint32_t ids[ROUNDS];
   auto fetch_ids = [&](int sl) {
     const int sd = min(sl, nsteps - 1);
+    const bool in = inside(sd);
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
-      const int k0 = min(max(sd * kKeys + (j * kWaves + w) * RPW, wg_lo), n - 1);
-      const int lb = k0 / BS;  // wave-uniform: the piece's rows share a block
-      const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
-      ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
+      const int k = sd * kKeys + (j * kWaves + w) * RPW;
+      const int k0 = in ? k : min(max(k, wg_lo), n - 1);
+      // wave-uniform: the piece's rows share a block
+      const int v = load_uniform(bt_row + (uint32_t)k0 / BS);
+      ids[j] = (uint32_t)v < (uint64_t)a.num_blocks ? (uint32_t)v : 0u;
     }
   };
   // Lane offsets inside a piece whose rows are not clamped (most steps): the
@@ -165,21 +171,34 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     koff[j] = (uint32_t)(lrow * (2 * D) + ((lch ^ (r & (CPR - 1))) << 4));
     voff[j] = (uint32_t)(lrow * (2 * D) + ((lch ^ vswz(r)) << 4)) + (uint32_t)v_bytes;
   }
+  const uint32_t blk_bytes = (uint32_t)block_bytes;  // < 2^32 for every supported shape
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);
+    auto piece_base = [&](int j, int key) {
+      return kvg + (uint64_t)ids[j] * blk_bytes + ((uint32_t)key % BS) * (2 * D);
+    };
+    if (inside(sd)) {
+#pragma unroll
+      for (int j = 0; j < ROUNDS; ++j) {
+        const int piece = j * kWaves + w;
+        const char* base = piece_base(j, sd * kKeys + piece * RPW);
+        load_lds16(base + koff[j], &lds[b][0][piece * 1024]);  // K: swizzled
+        load_lds16(base + voff[j], &lds[b][1][piece * 1024]);  // V: swizzled
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
       const int piece = j * kWaves + w;
       const int kb = sd * kKeys + piece * RPW;  // the piece's first key
       if (kb >= wg_lo && kb + RPW <= n) {
-        const char* base = kvg + (size_t)ids[j] * block_bytes + (kb % BS) * (2 * D);
-        load_lds16(base + koff[j], &lds[b][0][piece * 1024]);  // K: swizzled
-        load_lds16(base + voff[j], &lds[b][1][piece * 1024]);  // V: swizzled
+        const char* base = piece_base(j, kb);
+        load_lds16(base + koff[j], &lds[b][0][piece * 1024]);
+        load_lds16(base + voff[j], &lds[b][1][piece * 1024]);
       } else {
         const int r = piece * RPW + lrow;
-        const int key = min(max(sd * kKeys + r, wg_lo), n - 1);
-        const char* src = kvg + (size_t)ids[j] * block_bytes + (key % BS) * (2 * D);
+        const char* src = piece_base(j, min(max(sd * kKeys + r, wg_lo), n - 1));
         load_lds16(src + ((lch ^ (r & (CPR - 1))) << 4), &lds[b][0][piece * 1024]);
         load_lds16(src + v_bytes + ((lch ^ vswz(r)) << 4), &lds[b][1][piece * 1024]);
       }

@@ -130,9 +130,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   const float* scg = a.kv_scales + (size_t)g * 2 * BS;   // scales [NB, Hkv, 2, BS]
   const size_t sblock = 2 * (size_t)a.num_kv_heads * BS;  // floats per block
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks;
+  // Most steps lie wholly inside [wg_lo, n): they need no clamping, and
+  // take one wave-uniform test instead of one per piece.  Keys are below
+  // n <= max_blocks * BS, so a block index never passes the table's row.
   constexpr int LPS = ROUNDS + 1;  // loads per lane per step: pieces + scales
-  int ids[kKeys / 8];
+  uint32_t ids[kKeys / 8];
   auto clamp_key = [&](int k) { return min(max(k, wg_lo), n - 1); };
+  auto inside = [&](int sd) { return sd * kKeys >= wg_lo && (sd + 1) * kKeys <= n; };
   // the block id of step row r (a select chain, not a dynamic register index)
   auto id_of_row = [&](int r) {
     const int q = r >> 3;
@@ -140,11 +144,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   };
   auto fetch_ids = [&](int sl) {
     const int sd = min(sl, nsteps - 1);
+    const bool in = inside(sd);
 #pragma unroll
     for (int j = 0; j < kKeys / 8; ++j) {
-      const int lb = clamp_key(sd * kKeys + 8 * j) / BS;
-      const int v = lb < a.max_blocks ? load_uniform(bt_row + lb) : 0;
-      ids[j] = (v < 0 || v >= a.num_blocks) ? 0 : v;
+      const int k = sd * kKeys + 8 * j;
+      const int v = load_uniform(bt_row + (uint32_t)(in ? k : clamp_key(k)) / BS);
+      ids[j] = (uint32_t)v < (uint64_t)a.num_blocks ? (uint32_t)v : 0u;
     }
   };
   // A piece of RRPW rows lies in one block when RRPW <= BS (both powers of
@@ -153,33 +158,45 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   // offset; otherwise every lane finds its own row's block and clamped key.
   constexpr bool kPieceInBlock = RRPW <= BS;
   const uint32_t loff = (uint32_t)((lane / RCPR) * D + (lane % RCPR) * 16);
+  const uint32_t blk_bytes = (uint32_t)block_bytes;  // < 2^32 for every supported shape
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);
+    const bool in = inside(sd);
+    auto piece_src = [&](uint32_t id, bool is_v, int key) {
+      return kvg + (uint64_t)id * blk_bytes + (is_v ? v_bytes : 0) + ((uint32_t)key % BS) * D;
+    };
+    if (kPieceInBlock && in) {
 #pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) {
-      const int piece = j * kWaves + w;
-      const bool is_v = piece >= PIECES / 2;
-      const int r0 = (piece % (PIECES / 2)) * RRPW;  // the piece's first row in the step
-      const int kb = sd * kKeys + r0;
-      const size_t kv_off = is_v ? v_bytes : 0;
-      if (kPieceInBlock && kb >= wg_lo && kb + RRPW <= n) {
-        const char* base = kvg + (size_t)id_of_row(r0) * block_bytes + kv_off +
-                           (size_t)(kb % BS) * D;
-        load_lds16(base + loff, &raw[b].kv[piece * 1024]);
-      } else {
-        const int r = r0 + lane / RCPR;  // row in the step
-        const int key = clamp_key(sd * kKeys + r);
-        const char* src = kvg + (size_t)id_of_row(r) * block_bytes + kv_off +
-                          (size_t)(key % BS) * D + (lane % RCPR) * 16;
-        load_lds16(src, &raw[b].kv[piece * 1024]);
+      for (int j = 0; j < ROUNDS; ++j) {
+        const int piece = j * kWaves + w;
+        const int r0 = (piece % (PIECES / 2)) * RRPW;
+        load_lds16(piece_src(id_of_row(r0), piece >= PIECES / 2, sd * kKeys + r0) + loff,
+                   &raw[b].kv[piece * 1024]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < ROUNDS; ++j) {
+        const int piece = j * kWaves + w;
+        const bool is_v = piece >= PIECES / 2;
+        const int r0 = (piece % (PIECES / 2)) * RRPW;  // the piece's first row in the step
+        const int kb = sd * kKeys + r0;
+        if (kPieceInBlock && kb >= wg_lo && kb + RRPW <= n) {
+          load_lds16(piece_src(id_of_row(r0), is_v, kb) + loff, &raw[b].kv[piece * 1024]);
+        } else {
+          const int r = r0 + lane / RCPR;  // row in the step
+          load_lds16(piece_src(id_of_row(r), is_v, clamp_key(sd * kKeys + r)) +
+                         (lane % RCPR) * 16,
+                     &raw[b].kv[piece * 1024]);
+        }
       }
     }
     // scales: wave w loads entries 16 w + (lane % 16)
     const int e = 16 * w + (lane & 15);
     const int r = e % kKeys;
-    const int key = clamp_key(sd * kKeys + r);
-    const float* src = scg + (size_t)id_of_row(r) * sblock + (e >= kKeys ? BS : 0) + key % BS;
+    const int key = in ? sd * kKeys + r : clamp_key(sd * kKeys + r);
+    const float* src =
+        scg + (uint64_t)id_of_row(r) * sblock + (e >= kKeys ? BS : 0) + (uint32_t)key % BS;
     load_lds4(src, &raw[b].sc[64 * w]);
   };
 

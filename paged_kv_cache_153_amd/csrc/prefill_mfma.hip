@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
       const int k0 = in ? k : min(max(k, wg_lo), n - 1);
       // wave-uniform: the piece's rows share a block
       const int v = load_uniform(bt_row + (uint32_t)k0 / BS);
-      ids[j] = (uint32_t)v < (uint64_t)a.num_blocks ? (uint32_t)v : 0u;
+      ids[j] = (uint32_t)v;  // checked against the pool where it is used
     }
   };
   // Lane offsets inside a piece whose rows are not clamped (most steps): the
@@ -172,11 +172,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
     voff[j] = (uint32_t)(lrow * (2 * D) + ((lch ^ vswz(r)) << 4)) + (uint32_t)v_bytes;
   }
   const uint32_t blk_bytes = (uint32_t)block_bytes;  // < 2^32 for every supported shape
+  // ids outside the pool read block 0 (32-bit scalar compare, at the use so
+  // that the block-id loads are not waited for when they are issued)
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)UINT32_MAX);
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);
     auto piece_base = [&](int j, int key) {
-      return kvg + (uint64_t)ids[j] * blk_bytes + ((uint32_t)key % BS) * (2 * D);
+      const uint32_t id = ids[j] < nb32 ? ids[j] : 0u;
+      return kvg + (uint64_t)id * blk_bytes + ((uint32_t)key % BS) * (2 * D);
     };
     if (inside(sd)) {
 #pragma unroll

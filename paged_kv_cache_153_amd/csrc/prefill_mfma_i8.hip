@@ -137,10 +137,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   uint32_t ids[kKeys / 8];
   auto clamp_key = [&](int k) { return min(max(k, wg_lo), n - 1); };
   auto inside = [&](int sd) { return sd * kKeys >= wg_lo && (sd + 1) * kKeys <= n; };
-  // the block id of step row r (a select chain, not a dynamic register index)
+  // the block id of step row r (a select chain, not a dynamic register
+  // index); ids outside the pool read block 0 (checked at the use, so that
+  // the block-id loads are not waited for when they are issued)
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)UINT32_MAX);
   auto id_of_row = [&](int r) {
     const int q = r >> 3;
-    return q == 0 ? ids[0] : q == 1 ? ids[1] : q == 2 ? ids[2] : ids[3];
+    const uint32_t id = q == 0 ? ids[0] : q == 1 ? ids[1] : q == 2 ? ids[2] : ids[3];
+    return id < nb32 ? id : 0u;
   };
   auto fetch_ids = [&](int sl) {
     const int sd = min(sl, nsteps - 1);
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
     for (int j = 0; j < kKeys / 8; ++j) {
       const int k = sd * kKeys + 8 * j;
       const int v = load_uniform(bt_row + (uint32_t)(in ? k : clamp_key(k)) / BS);
-      ids[j] = (uint32_t)v < (uint64_t)a.num_blocks ? (uint32_t)v : 0u;
+      ids[j] = (uint32_t)v;  // checked against the pool where it is used
     }
   };
   // A piece of RRPW rows lies in one block when RRPW <= BS (both powers of

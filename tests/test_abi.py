@@ -397,6 +397,8 @@ def _prefill_status(**kw):
     (dict(bs=24), -2), (dict(Hq=6), -2), (dict(Hq=7), -1), (dict(kernel=0x200), -1),
     (dict(NB=0), -1), (dict(S=-1), -1), (dict(scale=0.0), -1), (dict(scale=-0.1), -1),
     (dict(scale=float("inf")), -1), (dict(scale=float("nan")), -1), (dict(window=-1), -1),
+    # a block of 2 * Hkv * bs * D * 2 bytes must fit 32-bit offsets
+    (dict(Hq=1 << 18, Hkv=1 << 18, bs=32), -2),
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert _prefill_status(**kw) == status

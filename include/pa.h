@@ -278,7 +278,9 @@ size_t pa_decode_static_capacity(void);
  * PA_F16 or PA_I8; head_dim 64 or 128; block_size 8, 16 or 32; G in
  * {1, 2, 4, 8}.
  * num_seqs * num_kv_heads * ceil(max_query_len * G / 128) workgroups above
- * 2^24 - 1 return PA_ERR_INVALID_ARG.
+ * 2^24 - 1 return PA_ERR_INVALID_ARG; a pool whose blocks exceed 32-bit
+ * byte offsets (num_kv_heads * block_size * head_dim * 4 >= 2^32) returns
+ * PA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */
 int pa_prefill(float* out, const void* query, const void* kv_cache,
                const float* kv_scales, const int32_t* block_tables,

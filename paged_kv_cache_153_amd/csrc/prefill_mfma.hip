@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_kernel(PrefillArg
   const uint32_t blk_bytes = (uint32_t)block_bytes;  // < 2^32 for every supported shape
   // ids outside the pool read block 0 (32-bit scalar compare, at the use so
   // that the block-id loads are not waited for when they are issued)
-  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)UINT32_MAX);
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)1 << 31);  // negative ids fail it
   auto issue = [&](int sl, auto B) {
     constexpr int b = decltype(B)::value;
     const int sd = min(sl, nsteps - 1);

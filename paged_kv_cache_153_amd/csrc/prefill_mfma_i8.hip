@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   // the block id of step row r (a select chain, not a dynamic register
   // index); ids outside the pool read block 0 (checked at the use, so that
   // the block-id loads are not waited for when they are issued)
-  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)UINT32_MAX);
+  const uint32_t nb32 = (uint32_t)min(a.num_blocks, (int64_t)1 << 31);  // negative ids fail it
   auto id_of_row = [&](int r) {
     const int q = r >> 3;
     const uint32_t id = q == 0 ? ids[0] : q == 1 ? ids[1] : q == 2 ? ids[2] : ids[3];

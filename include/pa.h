@@ -30,7 +30,8 @@
  *   - Sizes and shapes are host integers.  Contents of device arrays (block
  *     ids, slots, lengths) are the caller's contract; the kernels clamp every
  *     index they read so a bad entry cannot address memory outside the
- *     buffers, but the result is then unspecified.  With the environment
+ *     buffers: a block-table id outside [0, num_blocks) is read as block 0;
+ *     for other bad entries the result is unspecified.  With the environment
  *     variable PA_CHECK=1 the library copies those arrays to the host,
  *     validates them and returns PA_ERR_INVALID_ARG instead (slow; for
  *     debugging).  PA_CHECK is read on every call.

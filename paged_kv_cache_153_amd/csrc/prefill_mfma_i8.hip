@@ -13,20 +13,21 @@
 // Work decomposition, step shape and softmax as in prefill_mfma.hip; what
 // changes is how a step's K/V reach the matrix cores:
 //  * raw step tiles: each step's K and V codes (32 rows x D bytes each) and
-//    their 64 row scales arrive by direct global->LDS loads, issued three
+//    their 64 row scales arrive by direct global->LDS loads, issued five
 //    steps ahead into four raw buffers (each wave loads 16 of the scales);
 //  * conversion: once per workgroup, not per wave, the 256 threads widen the
-//    codes of the next step exactly — K to fp16 in the swizzled layout of
-//    the f16 kernel's K tile, V to bf16 — into one of two converted buffers,
-//    so the four waves share the work;
+//    codes of the step two ahead exactly — K to fp16 in the swizzled layout
+//    of the f16 kernel's K tile, V to bf16 — into two K and three V buffers
+//    (the V buffer also takes the step's scales), so the four waves share
+//    the work;
 //  * q.K^T: v_mfma_f32_16x16x32_f16 on the converted K, the K scale then
 //    multiplies each score;
 //  * P.V: the weights times the V scales, split into bf16 hi + lo parts
 //    (~16 significant bits; bf16's exponent takes any weight * scale), with
 //    v_mfma_f32_16x16x32_bf16 on the converted V codes;
 //  * the weight sums stay in fp32 without the V scales.
-// Per step: wait for the next raw tile, a barrier, convert it, a barrier,
-// then the softmax and P.V of this step with q.K of the next interleaved.
+// Per step: wait for the raw tile two ahead, one barrier, convert it, then
+// the softmax and P.V of this step with q.K of the next interleaved.
 #include "i8_codes.h"
 #include "prefill_common.h"
 
@@ -38,8 +39,6 @@ namespace {
 constexpr int kWaves = 4;                           // waves per workgroup
 constexpr int kColsWG = kWaves * 16 * prefill::kCB;  // columns per workgroup
 
-using prefill::kAhead;
-using prefill::kBufs;
 using prefill::kKeys;
 using prefill::kPLog;
 using prefill::kSlack;
@@ -55,6 +54,14 @@ struct RawTile {
   // rest of each slot is filled by the slot's other lanes and never read
   float sc[kWaves * 64];
 };
+
+template <int D>
+struct ConvertedV {
+  unsigned char v[kKeys * 2 * D];  // bf16 rows
+  float sc[2 * kKeys];             // K scales of the step's rows, then V scales
+};
+
+constexpr int kRawBufs = 4;  // raw buffers; steps are issued five ahead
 
 template <int D, int BS, int G>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(PrefillArgs a) {
@@ -75,9 +82,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   constexpr int TOK_W = COLS_W / G;     // query tokens per wave
   using vrow_t = typename prefill::VRow<D>::type;
 
-  __shared__ __attribute__((aligned(16))) RawTile<D> raw[kBufs];
-  // [buffer][K fp16 (swizzled) | V bf16 (plain rows)]
-  __shared__ __attribute__((aligned(16))) unsigned char cvt[2][2][CTILE];
+  // raw step tiles; converted K (fp16, swizzled) of two steps; converted V
+  // (bf16, plain rows) of three steps, each with its step's 64 row scales
+  __shared__ __attribute__((aligned(16))) RawTile<D> raw[kRawBufs];
+  __shared__ __attribute__((aligned(16))) unsigned char cvk[2][CTILE];
+  __shared__ __attribute__((aligned(16))) ConvertedV<D> cvv[3];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -163,8 +172,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   constexpr bool kPieceInBlock = RRPW <= BS;
   const uint32_t loff = (uint32_t)((lane / RCPR) * D + (lane % RCPR) * 16);
   const uint32_t blk_bytes = (uint32_t)block_bytes;  // < 2^32 for every supported shape
-  auto issue = [&](int sl, auto B) {
-    constexpr int b = decltype(B)::value;
+  auto issue = [&](int sl, int b) {
     const int sd = min(sl, nsteps - 1);
     const bool in = inside(sd);
     auto piece_src = [&](uint32_t id, bool is_v, int key) {
@@ -206,15 +214,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
 
   // ---- conversion of a raw step tile: thread t widens CPT codes of row
   // t / 8 of K and of V
-  auto convert = [&](auto RB, auto CBUF) {
-    constexpr int rb = decltype(RB)::value;
-    constexpr int cbf = decltype(CBUF)::value;
+  auto convert = [&](int rb, int kbuf, int vbuf) {
     const int t = threadIdx.x;
     const int row = t >> 3, sub = t & 7;
     const unsigned char* kr = &raw[rb].kv[row * D + sub * CPT];
     const unsigned char* vr = kr + kKeys * D;
-    unsigned char* kc = cvt[cbf][0];
-    unsigned char* vc = cvt[cbf][1];
+    unsigned char* kc = cvk[kbuf];
+    unsigned char* vc = cvv[vbuf].v;
+    // the step's scales travel with its V: entry e (K rows, then V rows)
+    // sits in wave e / 16's slot of the raw tile
+    if (t < 2 * kKeys) cvv[vbuf].sc[t] = raw[rb].sc[64 * (t >> 4) + (t & 15)];
     if constexpr (CPT == 16) {
       const u32x4_t k4 = *reinterpret_cast<const u32x4_t*>(kr);
       const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(vr);
@@ -258,9 +267,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   }
   const float cs = a.scale_log2;  // > 0: the max is taken on the raw scores
 
-  auto qk = [&](auto CBUF, float4_t (&sc)[CB][2]) {
-    constexpr int cbf = decltype(CBUF)::value;
-    const unsigned char* kt = cvt[cbf][0];
+  auto qk = [&](int kbuf, float4_t (&sc)[CB][2]) {
+    const unsigned char* kt = cvk[kbuf];
     u32x4_t kr[2][KS];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -283,14 +291,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   // softmax and P.V of step st (raw buffer RB for its scales, converted
   // buffer CV for its V); q.K of the next step (converted buffer CN) is
   // issued between the max and the exponentials
-  auto softmax_pv = [&](int st, auto RB, auto CV, const float4_t (&sc)[CB][2], auto CN,
+  auto softmax_pv = [&](int st, int vbuf, const float4_t (&sc)[CB][2], int knext,
                         float4_t (&sn)[CB][2]) {
-    constexpr int rb = decltype(RB)::value;
-    constexpr int cv = decltype(CV)::value;
     // vector work at raised issue priority, dropped before the P.V products
     // (a wave's in-kernel priority, as in the f16 kernel)
     __builtin_amdgcn_s_setprio(1);
-    const unsigned char* vt = cvt[cv][1];
+    const unsigned char* vt = cvv[vbuf].v;
     vrow_t vr[8];
 #pragma unroll
     for (int jv = 0; jv < 8; ++jv) {
@@ -304,8 +310,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
     float4_t sk[2], sv[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      sk[kk] = *reinterpret_cast<const float4_t*>(&raw[rb].sc[64 * kk + 4 * quad]);
-      sv[kk] = *reinterpret_cast<const float4_t*>(&raw[rb].sc[64 * (2 + kk) + 4 * quad]);
+      sk[kk] = *reinterpret_cast<const float4_t*>(&cvv[vbuf].sc[16 * kk + 4 * quad]);
+      sv[kk] = *reinterpret_cast<const float4_t*>(&cvv[vbuf].sc[kKeys + 16 * kk + 4 * quad]);
     }
     const bool edge = (st + 1) * kKeys - 1 > w_pmin || (st + 1) * kKeys > n ||
                       st * kKeys < w_lomax;
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
         m[cb] = m_new;
       }
     }
-    qk(CN, sn);
+    qk(knext, sn);
     bf16x8_t phi[CB], plo[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -394,58 +400,53 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_mfma_i8_kernel(Prefill
   };
 
   // ---- steps st0 .. nsteps - 1 --------------------------------------------
-  // Iteration st: wait until raw step st + 1 has landed (own loads, then the
-  // barrier for everyone's; every wave has also finished iteration st - 1),
-  // issue raw step st + kAhead into the buffer raw step st - 1 used, convert
-  // raw step st + 1 into the converted buffer step st - 1 used, a barrier,
-  // then run q.K of step st + 1 on the matrix cores while the softmax of
-  // step st runs on the vector ALUs, and P.V of step st.
+  // Raw step tiles are issued five steps ahead into four buffers and
+  // converted two steps ahead: iteration i (step st = st0 + i) waits until
+  // raw step st + 2 has landed (own loads, then one barrier for everyone's;
+  // the barrier also publishes step st + 1's conversion and ends everyone's
+  // reads of iteration i - 1), issues raw step st + 5 into the buffer raw
+  // step st + 1 left, converts raw step st + 2 (K into the buffer step st's
+  // q.K used, V and scales into the one step st - 1's P.V used), and runs
+  // the softmax and P.V of step st with q.K of step st + 1 interleaved.  K
+  // conversions live two steps, V conversions three: one barrier per step.
   auto vm_wait = [](auto N) {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(decltype(N)::value) : "memory");
   };
   auto barrier = []() { asm volatile("s_barrier" ::: "memory"); };
   auto lds_barrier = []() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  fetch_ids(st0);
-  issue(st0, I0{});
-  fetch_ids(st0 + 1);
-  issue(st0 + 1, I1{});
-  fetch_ids(st0 + 2);
-  issue(st0 + 2, I2{});
-  fetch_ids(st0 + 3);
-  vm_wait(std::integral_constant<int, 2 * LPS>{});
+  for (int j = 0; j < kRawBufs; ++j) {
+    fetch_ids(st0 + j);
+    issue(st0 + j, j);
+  }
+  fetch_ids(st0 + kRawBufs);
+  vm_wait(std::integral_constant<int, 2 * LPS>{});  // raw steps st0, st0 + 1
   barrier();
-  convert(I0{}, I0{});
-  lds_barrier();
+  convert(0, 0, 0);
+  convert(1, 1, 1);
+  lds_barrier();  // both converted; raw buffers 0 and 1 free
+  issue(st0 + kRawBufs, 0);
+  fetch_ids(st0 + kRawBufs + 1);
   float4_t sc[CB][2];
-  if (w_pmax >= 0) qk(I0{}, sc);
-  auto step = [&](int st, auto RB, auto CV) {
-    constexpr int rb = decltype(RB)::value;
-    constexpr int cv = decltype(CV)::value;
-    vm_wait(std::integral_constant<int, LPS>{});
+  if (w_pmax >= 0) qk(0, sc);
+  int v_cur = 0;  // (st - st0) % 3
+  for (int st = st0; st < nsteps; ++st) {
+    const int i = st - st0;
+    const int v_conv = v_cur == 0 ? 2 : v_cur - 1;  // (i + 2) % 3
+    vm_wait(std::integral_constant<int, 2 * LPS>{});  // raw step st + 2
     barrier();
-    issue(st + kAhead, std::integral_constant<int, (rb + kAhead) % kBufs>{});
-    fetch_ids(st + kAhead + 1);
-    convert(std::integral_constant<int, (rb + 1) % kBufs>{}, std::integral_constant<int, 1 - cv>{});
-    lds_barrier();
+    issue(st + kRawBufs + 1, (i + 1) & (kRawBufs - 1));
+    fetch_ids(st + kRawBufs + 2);
+    convert((i + 2) & (kRawBufs - 1), i & 1, v_conv);
     if (st * kKeys <= w_pmax) {
       float4_t sn[CB][2];
-      softmax_pv(st, RB, CV, sc, std::integral_constant<int, 1 - cv>{}, sn);
+      softmax_pv(st, v_cur, sc, (i + 1) & 1, sn);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         sc[cb][0] = sn[cb][0];
         sc[cb][1] = sn[cb][1];
       }
     }
-  };
-  for (int st = st0; st < nsteps; st += kBufs) {  // fixed buffers in each trip
-    step(st, I0{}, I0{});
-    if (st + 1 < nsteps) step(st + 1, I1{}, I1{});
-    if (st + 2 < nsteps) step(st + 2, I2{}, I0{});
-    if (st + 3 < nsteps) step(st + 3, I3{}, I1{});
+    v_cur = v_cur == 2 ? 0 : v_cur + 1;
   }
   vm_wait(std::integral_constant<int, 0>{});  // no load may land after the exit
 

@@ -23,8 +23,8 @@ the same step on this host; ``cache_write_us`` is the upload + cache write
 (+ copy-on-write) launch timed on its own in further steps.  The default
 run (the 7B layer) adds ``workloads``: one compact record for each other
 workload of the benchmark set (GQA, 70B with automatic and 512-token
-partitions, shared prefix at block 8/16/32, tiny), the INT8 pools and a
-GQA prefill chunk.
+partitions, shared prefix at block 8/16/32, tiny), the INT8 pools and the
+GQA prefill chunk over an f16 and an INT8 pool.
 """
 
 from __future__ import annotations
@@ -658,7 +658,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, AMD specificati
 
 
 def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parity=True,
-                  cpu=True):
+                  cpu=True, kv_dtype=None):
     """Chunked-prefill attention: each step writes a chunk of new K/V rows per
     sequence (pa_cache_write) and runs causal multi-token attention over the
     paged cache (pa_prefill).  Flops counted: 4 * D per (query, head, key
@@ -678,7 +678,7 @@ def prefill_bench(args, dev, workload=None, steps=None, warmup=None, check_parit
         raise SystemExit("prefill needs a float16 workload and chunk <= context")
     x = synth.make_decode_inputs([n] * S, Hq, Hkv, D, bs, dtype="f16", seed=args.seed,
                                  device=dev, std=w["std"])
-    int8 = args.kv_dtype == "i8"
+    int8 = (kv_dtype or args.kv_dtype) == "i8"
     if int8:
         x = synth.int8_pool(x)
     g = synth._gen(args.seed + 7, dev)
@@ -794,7 +794,11 @@ EXTRA_DECODE = [
     ("gqa7b_i8", "gqa7b", {"kv_dtype": "i8"}),
     ("llama70b_i8", "llama70b", {"kv_dtype": "i8"}),
 ]
-EXTRA_PREFILL = ["gqa7b"]
+EXTRA_PREFILL = [
+    # (key, workload, pool)
+    ("prefill_gqa7b", "gqa7b", "f16"),
+    ("prefill_gqa7b_i8", "gqa7b", "i8"),
+]
 
 
 def measure_decode(args, dev, name, block_size=None, partition=0, kv_dtype="f16", window=0,
@@ -1046,11 +1050,12 @@ def main():
         extra = {}
         for k, name, kw in EXTRA_DECODE:
             extra[k] = extra_line(args, dev, k, name, kw)
-        for name in EXTRA_PREFILL:
+        for k, name, pool in EXTRA_PREFILL:
             r = prefill_bench(args, dev, workload=name, steps=args.steps, warmup=args.warmup,
-                              check_parity=not args.no_parity, cpu=False)
-            extra[f"prefill_{name}"] = {
-                "workload": r["config"]["workload"], "kernel": "prefill_mfma",
+                              check_parity=not args.no_parity, cpu=False, kv_dtype=pool)
+            extra[k] = {
+                "workload": r["config"]["workload"],
+                "kernel": "prefill_mfma_i8" if pool == "i8" else "prefill_mfma",
                 "attention_us": r["attention_us"], "tflops": r["roofline"]["achieved"],
                 "mfma_frac": r["roofline"]["frac"], "parity_max_abs_err": r["parity_max_abs_err"],
                 "traffic": r["roofline"]["traffic"], "traffic_profile": r["traffic_profile"]}
